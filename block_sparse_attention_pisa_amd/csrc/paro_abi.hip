@@ -1,0 +1,106 @@
+// C ABI of libparo: host-side argument validation, then the kernel launchers.
+// Validation touches no HIP API, so every error path runs without a device
+// and nothing is launched when an argument is rejected.
+#include <cmath>
+#include <cstdint>
+#include <initializer_list>
+
+#include "paro_common.h"
+
+namespace {
+
+int check_problem(const paro_problem* p) {
+  if (!p) return PARO_ERR_NULL;
+  if (p->dtype != PARO_DTYPE_BF16 && p->dtype != PARO_DTYPE_FP32) return PARO_ERR_DTYPE;
+  if (p->B < 1 || p->H < 1 || p->L < 1) return PARO_ERR_SHAPE;
+  if (p->block != paro::kBlock) return PARO_ERR_SHAPE;
+  if (p->d != 64 && p->d != 128) return PARO_ERR_SHAPE;
+  if (static_cast<int64_t>(p->B) * p->H > 65535) return PARO_ERR_SHAPE;
+  const int64_t T = (static_cast<int64_t>(p->L) + p->block - 1) / p->block;
+  if (T > PARO_MAX_BLOCKS) return PARO_ERR_SHAPE;
+  if (T * p->B * p->H > INT32_MAX) return PARO_ERR_SHAPE;
+  if (!std::isfinite(p->scale) || !(p->scale > 0.0)) return PARO_ERR_ARG;
+  return PARO_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int check_ptrs(std::initializer_list<const void*> ptrs) {
+  for (const void* q : ptrs)
+    if (!q) return PARO_ERR_NULL;
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return PARO_ERR_ALIGN;
+  return PARO_OK;
+}
+
+int num_blocks(const paro_problem* p) { return (p->L + p->block - 1) / p->block; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? PARO_OK : PARO_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t paro_num_blocks(int32_t L, int32_t block) {
+  if (L < 1 || block < 1) return -1;
+  return static_cast<int32_t>((static_cast<int64_t>(L) + block - 1) / block);
+}
+
+int paro_version(void) { return PARO_VERSION; }
+
+const char* paro_status_string(int status) {
+  switch (status) {
+    case PARO_OK: return "ok";
+    case PARO_ERR_NULL: return "a required pointer is NULL";
+    case PARO_ERR_SHAPE: return "unsupported shape (B, H, L, d, block, keep_k or number of blocks)";
+    case PARO_ERR_DTYPE: return "unknown dtype code";
+    case PARO_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case PARO_ERR_WORKSPACE: return "workspace smaller than paro_precompute_workspace_bytes()";
+    case PARO_ERR_HIP: return "a kernel launch reported a HIP error";
+    case PARO_ERR_ARG: return "scale must be finite and > 0, lambda finite";
+    default: return "unknown status";
+  }
+}
+
+size_t paro_precompute_workspace_bytes(const paro_problem* p) {
+  if (check_problem(p) != PARO_OK) return 0;
+  return paro::precompute_workspace_bytes(*p);
+}
+
+int paro_precompute(const paro_problem* p, const void* K, const void* V, float* kbar, float* vsum, float* Hbar,
+                    double* M, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc != PARO_OK) return rc;
+  if ((rc = check_ptrs({K, V, kbar, vsum, Hbar, M, workspace})) != PARO_OK) return rc;
+  if (workspace_bytes < paro::precompute_workspace_bytes(*p)) return PARO_ERR_WORKSPACE;
+  return from_hip(paro::launch_precompute(*p, K, V, kbar, vsum, Hbar, M, workspace,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int paro_route(const paro_problem* p, const void* Q, const float* kbar, const double* M, int32_t keep_k,
+               double lambda, int32_t* idx, void* stream) {
+  int rc = check_problem(p);
+  if (rc != PARO_OK) return rc;
+  const int T = num_blocks(p);
+  if (keep_k < 0 || keep_k > T) return PARO_ERR_SHAPE;
+  if (paro::route_rows_per_group(T, p->d) < 1) return PARO_ERR_SHAPE;
+  if (!std::isfinite(lambda)) return PARO_ERR_ARG;
+  if ((rc = check_ptrs({Q, kbar, M})) != PARO_OK) return rc;
+  if (keep_k > 0 && (rc = check_ptrs({idx})) != PARO_OK) return rc;
+  return from_hip(paro::launch_route(*p, Q, kbar, M, keep_k, lambda, idx, static_cast<hipStream_t>(stream)));
+}
+
+int paro_attention(const paro_problem* p, const void* Q, const void* K, const void* V, const float* kbar,
+                   const float* vsum, const float* Hbar, const int32_t* idx, int32_t keep_k, void* O,
+                   void* stream) {
+  int rc = check_problem(p);
+  if (rc != PARO_OK) return rc;
+  const int T = num_blocks(p);
+  if (keep_k < 0 || keep_k > T) return PARO_ERR_SHAPE;
+  if ((rc = check_ptrs({Q, K, V, kbar, vsum, Hbar, O})) != PARO_OK) return rc;
+  if (keep_k > 0 && (rc = check_ptrs({idx})) != PARO_OK) return rc;
+  return from_hip(paro::launch_attention(*p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

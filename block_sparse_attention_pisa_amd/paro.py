@@ -1,0 +1,192 @@
+"""Thin ctypes binding of libparo (include/paro.h).
+
+Argument marshalling only: every step of the PISA path runs in the HIP
+kernels of libparo.so. PyTorch supplies device memory and the current
+stream. There is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libparo.so")
+
+PARO_OK = 0
+PARO_DTYPE_BF16 = 0
+PARO_DTYPE_FP32 = 1
+BLOCK = 64
+
+STATUS = {
+    0: "PARO_OK", -1: "PARO_ERR_NULL", -2: "PARO_ERR_SHAPE", -3: "PARO_ERR_DTYPE",
+    -4: "PARO_ERR_ALIGN", -5: "PARO_ERR_WORKSPACE", -6: "PARO_ERR_HIP", -7: "PARO_ERR_ARG",
+}
+
+EXPORTED = (
+    "paro_precompute", "paro_precompute_workspace_bytes", "paro_route", "paro_attention",
+    "paro_num_blocks", "paro_status_string", "paro_version",
+)
+
+
+class ParoProblem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
+        ("d", ctypes.c_int32), ("block", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_double),
+    ]
+
+
+class ParoError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = lib().paro_status_string(code).decode() if _LIB is not None else ""
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({msg})")
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libparo.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m block_sparse_attention_pisa_amd.build` "
+                "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_double
+        pp = ctypes.POINTER(ParoProblem)
+        L.paro_precompute.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.paro_precompute.restype = ctypes.c_int
+        L.paro_precompute_workspace_bytes.argtypes = [pp]
+        L.paro_precompute_workspace_bytes.restype = sz
+        L.paro_route.argtypes = [pp, vp, vp, vp, i32, dbl, vp, vp]
+        L.paro_route.restype = ctypes.c_int
+        L.paro_attention.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+        L.paro_attention.restype = ctypes.c_int
+        L.paro_num_blocks.argtypes = [i32, i32]
+        L.paro_num_blocks.restype = i32
+        L.paro_status_string.argtypes = [ctypes.c_int]
+        L.paro_status_string.restype = ctypes.c_char_p
+        L.paro_version.argtypes = []
+        L.paro_version.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def _check(rc: int, where: str):
+    if rc != PARO_OK:
+        raise ParoError(rc, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PARO_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return PARO_DTYPE_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def problem(q: torch.Tensor, scale: float | None = None, block: int = BLOCK) -> ParoProblem:
+    """Problem descriptor for a [B, H, L, d] tensor."""
+    if q.dim() != 4:
+        raise ValueError("expected a [B, H, L, d] tensor")
+    B, H, L, d = q.shape
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    return ParoProblem(B, H, L, d, block, _dtype_code(q), s)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def num_blocks(L: int, block: int = BLOCK) -> int:
+    return int(lib().paro_num_blocks(L, block))
+
+
+def workspace_bytes(p: ParoProblem) -> int:
+    return int(lib().paro_precompute_workspace_bytes(ctypes.byref(p)))
+
+
+def alloc_stats(k: torch.Tensor, block: int = BLOCK):
+    """Allocate (kbar, vsum, Hbar, M, workspace) for a [B, H, L, d] key tensor."""
+    B, H, L, d = k.shape
+    T = -(-L // block)
+    dev = k.device
+    p = problem(k, block=block)
+    ws = torch.empty(max(16, workspace_bytes(p)), dtype=torch.uint8, device=dev)
+    return (torch.empty(B, H, T, d, dtype=torch.float32, device=dev),
+            torch.empty(B, H, T, d, dtype=torch.float32, device=dev),
+            torch.empty(B, H, d, d, dtype=torch.float32, device=dev),
+            torch.empty(B, H, T, dtype=torch.float64, device=dev),
+            ws)
+
+
+def precompute(k: torch.Tensor, v: torch.Tensor, out=None, scale: float | None = None):
+    """Block statistics (kbar, vsum, Hbar, M) of [B, H, L, d] keys and values."""
+    p = problem(k, scale)
+    kbar, vsum, Hbar, M, ws = alloc_stats(k) if out is None else out
+    _check(lib().paro_precompute(
+        ctypes.byref(p), _dev(k, "k"), _dev(v, "v", k.dtype), _dev(kbar, "kbar", torch.float32),
+        _dev(vsum, "vsum", torch.float32), _dev(Hbar, "Hbar", torch.float32),
+        _dev(M, "M", torch.float64), _dev(ws, "workspace"), ws.numel() * ws.element_size(),
+        _stream()), "paro_precompute")
+    return kbar, vsum, Hbar, M
+
+
+def route(q: torch.Tensor, kbar: torch.Tensor, M: torch.Tensor, keep_k: int, lam: float,
+          scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Top-keep_k kv-block indices [B, H, T, keep_k] (int32, ascending per row)."""
+    p = problem(q, scale)
+    B, H, L, d = q.shape
+    T = -(-L // BLOCK)
+    idx = torch.empty(B, H, T, keep_k, dtype=torch.int32, device=q.device) if out is None else out
+    ptr = _dev(idx, "idx", torch.int32) if keep_k > 0 else None
+    _check(lib().paro_route(ctypes.byref(p), _dev(q, "q"), _dev(kbar, "kbar", torch.float32),
+                            _dev(M, "M", torch.float64), int(keep_k), float(lam), ptr, _stream()),
+           "paro_route")
+    return idx
+
+
+def attention(q, k, v, kbar, vsum, Hbar, idx, keep_k: int, scale: float | None = None,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """Piecewise attention output [B, H, L, d] in the dtype of q."""
+    p = problem(q, scale)
+    o = torch.empty_like(q) if out is None else out
+    ptr = _dev(idx, "idx", torch.int32) if keep_k > 0 else None
+    _check(lib().paro_attention(
+        ctypes.byref(p), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+        _dev(kbar, "kbar", torch.float32), _dev(vsum, "vsum", torch.float32),
+        _dev(Hbar, "Hbar", torch.float32), ptr, int(keep_k), _dev(o, "o", q.dtype), _stream()),
+        "paro_attention")
+    return o
+
+
+def keep_to_k(keep: float, T: int) -> int:
+    """Kept fraction -> block count, k = ceil(keep * T) (integer-exact for permille fractions)."""
+    return min(T, max(0, -(-round(keep * 1000) * T // 1000)))
+
+
+def pisa_attention(q, k, v, keep_k: int | None = None, keep: float | None = None, lam: float = 0.1,
+                   scale: float | None = None) -> torch.Tensor:
+    """Whole path: precompute, route and fused attention on the current stream."""
+    T = -(-q.shape[2] // BLOCK)
+    if keep_k is None:
+        keep_k = keep_to_k(0.125 if keep is None else keep, T)
+    kbar, vsum, Hbar, M = precompute(k, v, scale=scale)
+    idx = route(q, kbar, M, keep_k, lam, scale=scale)
+    return attention(q, k, v, kbar, vsum, Hbar, idx, keep_k, scale=scale)

@@ -1,0 +1,150 @@
+/*
+ * paro.h - C ABI of the PISA block-sparse attention hot path on AMD CDNA4
+ * (gfx950 / MI355X).
+ *
+ * Method: "PISA: Piecewise Sparse Attention Is Wiser for Efficient Diffusion
+ * Transformers" (technical summary), section 2. For every query block i the
+ * key/value blocks are split into an exact set S_i (the top-k blocks of a
+ * covariance-aware score) and a tail U_i (all other blocks). The output is
+ * o_t = N_t / D_t where
+ *   N_t = sum_{j in S_i} sum_n exp(q'_t k_{j,n}) v_{j,n}
+ *       + sum_{j in U_i} alpha_{t,j} vsum_j
+ *       + (q'_t Hbar) sum_{j in U_i} alpha_{t,j},
+ *   D_t = sum_{j in S_i} sum_n exp(q'_t k_{j,n}) + sum_{j in U_i} alpha_{t,j} n_j,
+ *   alpha_{t,j} = exp(q'_t kbar_j), q'_t = scale * q_t,
+ *   kbar_j = mean of the keys of block j, vsum_j = sum of its values,
+ *   H_j = sum_n (k_{j,n} - kbar_j)^T v_{j,n}, Hbar = mean of H_j over all blocks,
+ *   M_j = ||H_j - Hbar||_2 (largest singular value).
+ * The denominator and the exact definition of H_j are not printed on the page;
+ * the forms above are the ones under which the correction is the first-order
+ * Taylor term of the exact block sums (its first-order part of the
+ * denominator is zero).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Q, K, V, O: contiguous [B, H, L, d] tensors, d fastest, in device
+ *   memory, element type given by paro_problem.dtype (bf16 bits or fp32).
+ * - Blocks: T = ceil(L / block) blocks of `block` consecutive tokens; the last
+ *   block may be partial (n_{T-1} = L - block*(T-1) valid tokens). Padded
+ *   positions never contribute to any statistic, score or output.
+ * - Every pointer is a device pointer aligned to 16 bytes. The caller owns
+ *   every buffer; the library never allocates, frees, keeps or frees a pointer
+ *   after return. Outputs are fully overwritten; inputs are never written;
+ *   outputs must not alias inputs.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   All work is enqueued on it asynchronously; the library never
+ *   synchronizes. Device faults surface at the caller's next synchronization.
+ * - Return value: PARO_OK (0) or a negative PARO_ERR_* code. Arguments are
+ *   validated on the host before anything is launched; on an error nothing
+ *   is launched and no output is touched. The library never prints or aborts.
+ *   NaN/Inf inputs are not detected.
+ * - Supported: block == 64; d in {64, 128}; 1 <= B, H; 1 <= L; B*H*L*d < 2^31;
+ *   T <= PARO_MAX_BLOCKS.
+ */
+#ifndef PARO_H_
+#define PARO_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PARO_VERSION 100
+
+#define PARO_OK 0
+#define PARO_ERR_NULL (-1)      /* a required pointer is NULL */
+#define PARO_ERR_SHAPE (-2)     /* unsupported B, H, L, d, block, keep_k or T */
+#define PARO_ERR_DTYPE (-3)     /* unknown dtype code */
+#define PARO_ERR_ALIGN (-4)     /* a pointer is not 16-byte aligned */
+#define PARO_ERR_WORKSPACE (-5) /* workspace smaller than paro_precompute_workspace_bytes() */
+#define PARO_ERR_HIP (-6)       /* a kernel launch reported a HIP error */
+#define PARO_ERR_ARG (-7)       /* scale not finite and > 0, or lambda not finite */
+
+#define PARO_DTYPE_BF16 0
+#define PARO_DTYPE_FP32 1
+
+#define PARO_MAX_BLOCKS 16384
+
+typedef struct paro_problem {
+  int32_t B;      /* batch */
+  int32_t H;      /* heads */
+  int32_t L;      /* tokens per sequence */
+  int32_t d;      /* head dimension (64 or 128) */
+  int32_t block;  /* tokens per block (64) */
+  int32_t dtype;  /* PARO_DTYPE_BF16 or PARO_DTYPE_FP32: Q, K, V and O */
+  double scale;   /* softmax scale (q' = scale * q), finite and > 0; usually 1/sqrt(d) */
+} paro_problem;
+
+/*
+ * paro_precompute - block statistics (section 2, "hardware implementation",
+ * pre-computation step, and "covariance-aware routing" for M_j).
+ *
+ * in : K, V [B, H, L, d] (dtype)
+ * out: kbar [B, H, T, d] fp32   mean of the valid keys of block j
+ *      vsum [B, H, T, d] fp32   sum of the valid values of block j
+ *      Hbar [B, H, d, d] fp32   mean over all T blocks of H_j; row = key dim,
+ *                               column = value dim
+ *      M    [B, H, T]    fp64   largest singular value of H_j - Hbar
+ *                               (fp32 power iteration, final norm in fp64)
+ * workspace: device scratch of at least paro_precompute_workspace_bytes(p)
+ *            bytes (per-chunk partial sums of H_j); contents on entry are
+ *            ignored and undefined on return.
+ * H_j itself is never written to memory.
+ */
+int paro_precompute(const paro_problem* p, const void* K, const void* V, float* kbar,
+                    float* vsum, float* Hbar, double* M, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace paro_precompute needs for this problem (0 on bad shape). */
+size_t paro_precompute_workspace_bytes(const paro_problem* p);
+
+/*
+ * paro_route - covariance-aware top-k routing (section 2, "covariance-aware
+ * routing"): score_ij = scale * qbar_i . kbar_j + lambda * M_j with qbar_i the
+ * mean of the valid queries of block i. S_i = the keep_k highest scores of
+ * row i, exact ties resolved toward the lower j, written in ascending j.
+ *
+ * in : Q [B, H, L, d] (dtype); kbar, M from paro_precompute; 0 <= keep_k <= T;
+ *      lambda finite.
+ * out: idx [B, H, T, keep_k] int32 (nothing is written when keep_k == 0).
+ * Scores are formed in fp64 from fp32 kbar and fp64 qbar and M.
+ */
+int paro_route(const paro_problem* p, const void* Q, const float* kbar, const double* M,
+               int32_t keep_k, double lambda, int32_t* idx, void* stream);
+
+/*
+ * paro_attention - the fused piecewise attention (section 2, "core
+ * algorithm" and the stage 1 / stage 2 / stage 3 pipeline): stage 1 exact
+ * online softmax over the blocks listed in idx; stage 2 zeroth-order terms of
+ * every other block from kbar and vsum, sharing the same running maximum;
+ * stage 3 the global first-order correction (q' Hbar) * sum alpha; then N / D.
+ *
+ * in : Q, K, V [B, H, L, d] (dtype); kbar, vsum, Hbar from paro_precompute;
+ *      idx [B, H, T, keep_k] int32: for every row, keep_k distinct block
+ *      indices in [0, T) in ascending order (as paro_route writes them);
+ *      0 <= keep_k <= T.
+ * out: O [B, H, L, d] (dtype; rows >= L of the last block are not written).
+ * bf16 problems use bf16 MFMA products with fp32 accumulation (tail
+ * centroids, value sums and Hbar rounded to bf16 for the matrix cores);
+ * fp32 problems use fp32 arithmetic throughout. An idx row that breaks the
+ * stated contract gives undefined output values (never an out-of-bounds access).
+ */
+int paro_attention(const paro_problem* p, const void* Q, const void* K, const void* V,
+                   const float* kbar, const float* vsum, const float* Hbar,
+                   const int32_t* idx, int32_t keep_k, void* O, void* stream);
+
+/* T = ceil(L / block), or -1 when L < 1 or block < 1. */
+int32_t paro_num_blocks(int32_t L, int32_t block);
+
+/* Static description of a status code (never NULL). */
+const char* paro_status_string(int status);
+
+/* PARO_VERSION of the loaded library. */
+int paro_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PARO_H_ */

@@ -1,0 +1,103 @@
+"""C ABI checks that need no GPU: exported symbols, helpers and host-side validation.
+
+Validation runs before any HIP call, so rejected arguments return their error
+code here (a launch attempted without a device would give PARO_ERR_HIP instead).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_attention_pisa_amd import paro
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paro.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(paro.LIB_PATH), reason="libparo.so not built")
+
+FAKE = 0x10000  # an aligned non-null address that validation never dereferences
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(paro_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert set(names) == set(paro.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", paro.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (paro_\w+)", out))
+    for n in names:
+        assert n in exported, n
+    L = paro.lib()
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_helpers():
+    L = paro.lib()
+    assert L.paro_version() == 100
+    assert L.paro_num_blocks(75600, 64) == 1182
+    assert L.paro_num_blocks(64, 64) == 1 and L.paro_num_blocks(65, 64) == 2
+    assert L.paro_num_blocks(0, 64) == -1
+    for c in range(-7, 1):
+        assert len(L.paro_status_string(c)) > 0
+    assert L.paro_status_string(-99) == b"unknown status"
+
+
+def _p(**kw):
+    d = dict(B=1, H=2, L=1000, d=128, block=64, dtype=0, scale=0.088)
+    d.update(kw)
+    return paro.ParoProblem(**d)
+
+
+def test_workspace_bytes():
+    L = paro.lib()
+    p = _p()
+    n = L.paro_precompute_workspace_bytes(ctypes.byref(p))
+    assert n > 0 and n % (128 * 128 * 4) == 0
+    assert L.paro_precompute_workspace_bytes(ctypes.byref(_p(d=96))) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), -2), (dict(block=32), -2), (dict(L=0), -2), (dict(B=0), -2), (dict(H=-1), -2),
+    (dict(dtype=7), -3), (dict(scale=0.0), -7), (dict(scale=float("nan")), -7),
+    (dict(L=64 * 16384 + 1), -2), (dict(B=300, H=300), -2),
+])
+def test_problem_validation(kw, code):
+    L = paro.lib()
+    p = _p(**kw)
+    ws = 1 << 30
+    assert L.paro_precompute(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == code
+    assert L.paro_route(ctypes.byref(p), FAKE, FAKE, FAKE, 2, 0.1, FAKE, None) == code
+    assert L.paro_attention(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, None) == code
+
+
+def test_pointer_and_argument_validation():
+    L = paro.lib()
+    p = _p()
+    pp = ctypes.byref(p)
+    ws = L.paro_precompute_workspace_bytes(pp)
+    assert L.paro_precompute(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == -1
+    assert L.paro_precompute(pp, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == -1
+    assert L.paro_precompute(pp, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == -4
+    assert L.paro_precompute(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == -5
+    T = L.paro_num_blocks(1000, 64)
+    assert L.paro_route(pp, FAKE, FAKE, FAKE, T + 1, 0.1, FAKE, None) == -2
+    assert L.paro_route(pp, FAKE, FAKE, FAKE, -1, 0.1, FAKE, None) == -2
+    assert L.paro_route(pp, FAKE, FAKE, FAKE, 2, float("inf"), FAKE, None) == -7
+    assert L.paro_route(pp, FAKE, FAKE, FAKE, 2, 0.1, None, None) == -1
+    assert L.paro_route(pp, FAKE, FAKE + 4, FAKE, 2, 0.1, FAKE, None) == -4
+    assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, FAKE, None) == -1
+    assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T + 1, FAKE, None) == -2
+    assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE + 2, None) == -4
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 64, 64)
+    with pytest.raises(ValueError):
+        paro.precompute(q, q)

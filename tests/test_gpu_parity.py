@@ -1,0 +1,125 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small cases run whole; the DiT-sized workloads run the GPU over every head
+and every query block (the launch configuration the benchmark times) and the
+oracle checks sampled heads and query blocks.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_pisa_amd import paro
+from oracle import pisa
+from workloads import WORKLOADS, Workload, make_inputs, random_uniform_inputs
+
+from parity_util import (check_attention, check_route, check_stats, full_parity, log, run_gpu,
+                         sample_qblocks)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_fp32_whole_pipeline():
+    s = full_parity(WORKLOADS["tiny_fp32"])
+    assert s["max_err"] <= 1e-5
+
+
+def test_image_4608_all_heads():
+    w = WORKLOADS["image_4608"]
+    s = full_parity(w, qblocks=lambda T: list(range(T)))
+    log("[parity] image summary", s)
+
+
+def test_video480p_sampled():
+    w = WORKLOADS["video480p_32760"]
+    s = full_parity(w, heads=[(0, 0), (0, 11)], qblocks=lambda T: sample_qblocks(T, 24))
+    log("[parity] 480p summary", s)
+
+
+def test_video720p_sampled():
+    w = WORKLOADS["video720p_75600"]
+    s = full_parity(w, heads=[(0, 0), (0, 39)], qblocks=lambda T: sample_qblocks(T, 12), diag=False)
+    log("[parity] 720p summary", s)
+
+
+def test_video_long_sampled():
+    w = WORKLOADS["video_long_118800"]
+    s = full_parity(w, heads=[(0, 23)], qblocks=lambda T: sample_qblocks(T, 8), diag=False)
+    log("[parity] long summary", s)
+
+
+def test_long_dense_control_equals_softmax_attention():
+    """keep = 100%: the path must reduce to plain softmax attention."""
+    w = WORKLOADS["video_long_118800_dense"]
+    q, k, v = make_inputs(w, heads=[3])   # one head at full length
+    (qd, kd, vd), stats, idx = run_gpu(q, k, v, w.k, w.lam)
+    assert (idx.cpu() == torch.arange(w.T, dtype=torch.int32)).all()
+    o = paro.attention(qd, kd, vd, *stats[:3], idx, w.k).float().cpu().numpy()[0, 0]
+    qn, kn, vn = (x[0, 0].double().numpy() for x in (q, k, v))
+    rows = np.concatenate([np.arange(0, 64), np.arange(60000, 60064), np.arange(w.L - 16, w.L)])
+    dense = pisa.dense_attention(qn, kn, vn, w.scale, rows=rows)
+    mx, mean = check_attention(o[rows], dense, "bf16")
+    log(f"[parity] dense control max {mx:.3g} mean {mean:.3g}")
+
+
+@pytest.mark.parametrize("case", [
+    dict(L=37, d=128, keep=1, H=1, B=1),            # one partial block
+    dict(L=64, d=128, keep=0, H=2, B=1),            # keep 0: everything in the tail
+    dict(L=64 * 7 + 5, d=128, keep=8, H=1, B=2),    # keep = T: dense
+    dict(L=64 * 9 - 17, d=64, keep=3, H=3, B=1),    # d = 64, ragged tail
+    dict(L=64 * 40 + 1, d=128, keep=5, H=2, B=2),   # last block of one token
+])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_edge_shapes(case, dtype):
+    B, H, L, d, keep = case["B"], case["H"], case["L"], case["d"], case["keep"]
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v = random_uniform_inputs(B, H, L, d, dtype=tdt, seed=L + d, scale=0.8)
+    lam, scale = 0.1, 1 / np.sqrt(d)
+    (qd, kd, vd), stats, idx = run_gpu(q, k, v, keep, lam)
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    idx_h = idx.cpu().numpy()
+    idx_or = torch.empty_like(idx.cpu())
+    refs = {}
+    for b in range(B):
+        for h in range(H):
+            st = pisa.block_stats(kn[b, h], vn[b, h], 64)
+            ir, sc = pisa.route(qn[b, h], st["kbar"], st["M"], keep, lam, scale, 64)
+            check_stats(stats, st, b, h)
+            if keep:
+                check_route(idx_h[b, h], ir, sc)
+            idx_or[b, h] = torch.from_numpy(ir.astype(np.int32))
+            refs[(b, h)] = (st, ir)
+    o = paro.attention(qd, kd, vd, *stats[:3], idx_or.cuda(), keep).float().cpu().numpy()
+    for (b, h), (st, ir) in refs.items():
+        oref = pisa.attention(qn[b, h], kn[b, h], vn[b, h], st, ir, scale, 64)
+        check_attention(o[b, h], oref, dtype)
+
+
+def test_rows_past_L_are_not_written():
+    """The output is written only for the L valid rows (bytes after it stay untouched)."""
+    B, H, L, d = 1, 1, 64 * 3 - 10, 128
+    q, k, v = random_uniform_inputs(B, H, L, d, dtype=torch.bfloat16, seed=5)
+    qd, kd, vd = (x.cuda() for x in (q, k, v))
+    stats = paro.precompute(kd, vd)
+    idx = paro.route(qd, stats[0], stats[3], 1, 0.1)
+    o = paro.attention(qd, kd, vd, *stats[:3], idx, 1)
+    n = B * H * L * d
+    buf = torch.full((n + 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+    ov = buf[:n].view(B, H, L, d)
+    paro.attention(qd, kd, vd, *stats[:3], idx, 1, out=ov)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
+    assert (buf[n:] == 7.0).all()
+    assert torch.equal(ov, o)
+
+
+def test_deterministic_bitwise():
+    w = WORKLOADS["image_4608"]
+    q, k, v = make_inputs(w, heads=[0, 1, 2, 3])
+    outs = []
+    for _ in range(2):
+        (qd, kd, vd), stats, idx = run_gpu(q, k, v, w.k, w.lam)
+        o = paro.attention(qd, kd, vd, *stats[:3], idx, w.k)
+        torch.cuda.synchronize()
+        outs.append([x.cpu() for x in (*stats, idx, o)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
