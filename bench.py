@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of the PISA hot path on one MI355X.
+
+One step = paro_precompute + paro_route + paro_attention over one batch of
+synthetic DiT-shaped input already resident in HBM. The default workload is
+the 720p video shape (B=1, 40 heads, 75,600 tokens, d=128, bf16, 12.5% of
+the kv-blocks exact). Prints one JSON line:
+  value      dense-equivalent TFLOP/s = 4 B H L^2 d / step time
+  roofline   the attention kernel against the bf16 MFMA peak, from its
+             algorithmic FLOPs (exact blocks + zeroth-order terms of U_i +
+             correction) over its mean launch time measured with HIP events
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic_video720p_75600.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_pisa_amd", "csrc", "paro_attention.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="video720p_75600")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-qblocks", type=int, default=48, help="query blocks per head in the oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=1)
+    return ap.parse_args()
+
+
+def attention_flops(w, idx_cpu) -> float:
+    """Algorithmic FLOPs of one attention launch.
+
+    Exact part 4 d sum_i n_i sum_{j in S_i} n_j (QK^T and PV), zeroth-order
+    part 4 d sum_i n_i |U_i| (one centroid logit and one value-sum product
+    per tail block), correction 2 d^2 L per head (q' Hbar).
+    """
+    import numpy as np
+    T, L, d, blk = w.T, w.L, w.d, w.block
+    n = np.full(T, blk, dtype=np.int64)
+    n[-1] = L - blk * (T - 1)
+    per_head = 0.0
+    idx = idx_cpu.reshape(-1, T, w.k) if w.k else None
+    heads = w.B * w.H
+    total = 0.0
+    for h in range(heads):
+        if w.k:
+            sel_tokens = n[idx[h]].sum(axis=1)           # sum_{j in S_i} n_j per row i
+        else:
+            sel_tokens = np.zeros(T, dtype=np.int64)
+        exact = 4.0 * d * float((n * sel_tokens).sum())
+        tail = 4.0 * d * float((n * (T - w.k)).sum())
+        corr = 2.0 * d * d * L if w.k < T else 0.0
+        total += exact + tail + corr
+    return total
+
+
+def traffic_entry():
+    """HBM bytes per attention launch from committed counter runs, if the kernel is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != sha:
+            return None
+        return rec["hbm_bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def cpu_baseline(w, q, k, v, nq: int, nheads: int):
+    """Time the fp64 oracle on host cores on a bounded sample of the workload.
+
+    Per sampled head: block statistics and routing in full, attention on nq
+    evenly spaced query blocks (plus the last); the head time is extrapolated
+    to all T query blocks, and the rate is the dense-equivalent FLOPs of a
+    head over that time.
+    """
+    import numpy as np
+    from oracle import pisa
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    T = w.T
+    qbs = sorted(set(np.linspace(0, T - 1, nq).round().astype(int).tolist()) | {T - 1})
+    total_s = 0.0
+    for h in range(nheads):
+        qh, kh, vh = (x[0, h].double().numpy() for x in (q, k, v))
+        t0 = time.perf_counter()
+        st = pisa.block_stats(kh, vh, w.block)
+        idx, _ = pisa.route(qh, st["kbar"], st["M"], w.k, w.lam, w.scale, w.block)
+        t1 = time.perf_counter()
+        pisa.attention(qh, kh, vh, st, idx, w.scale, w.block, qblocks=qbs)
+        t2 = time.perf_counter()
+        total_s += (t1 - t0) + (t2 - t1) * T / len(qbs)
+    per_head_s = total_s / nheads
+    flops_head = 4.0 * w.L * w.L * w.d
+    return {
+        "value": flops_head / per_head_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"{nheads} head(s) of {w.name}: precompute + routing in full, attention on "
+                   f"{len(qbs)} of {T} query blocks, extrapolated to the whole head "
+                   f"({per_head_s:.1f} s per head, {per_head_s * w.B * w.H:.0f} s for the whole step)"),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the kernels shard by "
+              "(batch, head) with no communication, so multi-GPU runs are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from block_sparse_attention_pisa_amd import paro
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[a.workload]
+    t_gen = time.perf_counter()
+    q, k, v = make_inputs(w)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    stats = paro.alloc_stats(kd)
+    idx = torch.empty(w.B, w.H, w.T, w.k, dtype=torch.int32, device=dev)
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        paro.precompute(kd, vd, out=stats)
+        if ev:
+            ev[1].record(stream)
+        paro.route(qd, stats[0], stats[3], w.k, w.lam, out=idx)
+        if ev:
+            ev[2].record(stream)
+        paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, w.k, out=out)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre = [e[0].elapsed_time(e[1]) for e in evs]
+    rou = [e[1].elapsed_time(e[2]) for e in evs]
+    att = [e[2].elapsed_time(e[3]) for e in evs]
+    ms_step = wall * 1e3 / a.steps
+    dense_flops = 4.0 * w.B * w.H * w.L * w.L * w.d
+    value = dense_flops / (ms_step * 1e-3) / 1e12
+
+    idx_cpu = idx.cpu().numpy()
+    attn_flops = attention_flops(w, idx_cpu)
+    attn_ms = sum(att) / len(att)
+    achieved = attn_flops / (attn_ms * 1e-3) / 1e12
+    traffic = traffic_entry()
+    kv_bytes = 2.0 * w.B * w.H * w.L * w.d * (2 if w.dtype == "bf16" else 4)
+    pre_ms = sum(pre) / len(pre)
+
+    res = {
+        "metric": "dense-equiv TFLOP/s + ms/call, 32k-119k-token DiT attention, 12.5% density",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Fourier-feature Q/K, N(0,1) V; no trained weights)",
+        "config": {**w.describe(), "parallelism": "none (1 GPU)"},
+        "phases_ms": {"precompute": round(pre_ms, 4), "route": round(sum(rou) / len(rou), 4),
+                      "attention": round(attn_ms, 4)},
+        "precompute_hbm": {"algorithmic_GBs": round(kv_bytes / (pre_ms * 1e-3) / 1e9, 1),
+                           "frac_of_peak": round(kv_bytes / (pre_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "roofline": {
+            "kernel": "k_attn_bf16 (paro_attention)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": attn_flops,
+        },
+        "input_generation_s": round(t_gen, 1),
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, a.cpu_qblocks, a.cpu_heads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

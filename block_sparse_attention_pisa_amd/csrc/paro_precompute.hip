@@ -15,10 +15,10 @@
 //                        tokens are contiguous.
 //   2. k_hbar_reduce   : fixed-order fp64 sum of the chunk partials -> Hbar.
 //   3. k_block_spectral: re-reads K and V, rebuilds H_j in registers, forms
-//                        A = H_j - Hbar and runs fp32 power iteration on A^T A
-//                        until the Rayleigh estimate has converged far below
-//                        the fp32 rounding of A; the final ||A x|| / ||x|| is
-//                        accumulated in fp64. H_j never reaches memory.
+//                        A = H_j - Hbar and finds its largest singular value
+//                        by restarted Lanczos on A^T A (fp32 vectors, fp64
+//                        scalars); the final ||A x|| / ||x|| is accumulated in
+//                        fp64. H_j never reaches memory.
 // No float atomics anywhere: results are bitwise reproducible.
 #include "paro_common.h"
 
@@ -37,13 +37,6 @@ struct TileLds {
   float vsum[D];
 };
 
-template <int D>
-struct SpectralLds {
-  float xpart[16][D];  // column partials of A^T y (one row per 16-lane group)
-  float xs[D];         // current iterate (unnormalised)
-  double red[4][3];    // per-wave partial sums
-  double red2[16];
-};
 
 // H accumulator: entry (mi, nt, r) holds
 //   H[16 * (MTW * wave + mi) + 4 * (lane / 16) + r][16 * nt + lane % 16],
@@ -156,11 +149,15 @@ __device__ __forceinline__ void accumulate_ktv(const TileLds<uint16_t, D>& s, HA
 template <int D>
 __device__ __forceinline__ void accumulate_ktv(const TileLds<float, D>& s, HAcc<D>& acc) {
   constexpr int MTW = HAcc<D>::MTW, NTT = HAcc<D>::NTT;
+#pragma unroll
   for (int mi = 0; mi < MTW; ++mi)
+#pragma unroll
     for (int nt = 0; nt < NTT; ++nt)
+#pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = acc_row<D>(mi, r), col = acc_col(nt);
         float sum = 0.f;
+#pragma unroll 4
         for (int t = 0; t < kBlock; ++t) sum += s.kt[row][t] * s.vt[col][t];
         acc.v[mi][nt][r] += sum;
       }
@@ -228,15 +225,41 @@ __global__ __launch_bounds__(256) void k_hbar_reduce(const float* __restrict__ w
 }
 
 // ------------------------------------------------------------ kernel 3
+// M_j by restarted Lanczos on B = A^T A (A = H_j - Hbar). Each cycle runs
+// kLanczosK steps w = B v_k with classical Gram-Schmidt against the whole
+// basis (fp32 vectors, fp64 dot products), finds the top eigenpair of the
+// small tridiagonal matrix (64-point Sturm multisection across the lanes of
+// one wave, then inverse iteration), restarts from the Ritz vector, and
+// stops when the Ritz residual bound res^2 / (gap * theta) is negligible.
+// Power iteration alone needs thousands of steps when sigma_2 / sigma_1 is
+// close to 1 (blocks of i.i.d. keys); this reaches the fp32 floor in one
+// cycle for almost every block. M_j = ||A x|| / ||x|| is then evaluated in
+// fp64 from the fp32 Ritz vector, so its error is quadratic in the angle.
+constexpr int kLanczosK = 8;
+constexpr int kLanczosCycles = 16;
+constexpr double kLanczosTol = 1e-10;
+
 __device__ __forceinline__ float start_sign(int row) {
   return ((static_cast<uint32_t>(row + 1) * 2654435761u) >> 16) & 1u ? -1.f : 1.f;
 }
+
+template <int D>
+struct SpectralLds {
+  float xpart[16][D];           // column partials of A^T y (one row per 16-lane group)
+  float vk[kLanczosK + 1][D];   // Lanczos basis
+  float xs[D];                  // Ritz vector of the last cycle
+  double alpha[kLanczosK];
+  double beta[kLanczosK];
+  double red2[16];
+  double x2;
+  int flag;                     // 0 running, 1 converged, 2 A == 0
+};
 
 // xpart[group][col] = sum over this lane's rows of A[row][col] * y[row].
 template <int D>
 __device__ __forceinline__ void write_col_partials(const HAcc<D>& A, const float (&y)[D / 64][4],
                                                    SpectralLds<D>& sp) {
-  const int grp = threadIdx.x / 16;  // 16 groups of 16 lanes
+  const int grp = threadIdx.x / 16;
 #pragma unroll
   for (int nt = 0; nt < HAcc<D>::NTT; ++nt) {
     float p = 0.f;
@@ -248,18 +271,167 @@ __device__ __forceinline__ void write_col_partials(const HAcc<D>& A, const float
   }
 }
 
-// Sums over the waves that hold the D entries of the iterate.
+// xpart <- column partials of A^T (A x) for x = vk[k] (all threads).
 template <int D>
-__device__ __forceinline__ double red_total(const SpectralLds<D>& sp, int k) {
-  double t = sp.red[0][k];
-  if (D > 64) t += sp.red[1][k];
-  return t;
+__device__ __forceinline__ void apply_ata(const HAcc<D>& A, SpectralLds<D>& sp, int k) {
+  constexpr int MTW = HAcc<D>::MTW, NTT = HAcc<D>::NTT;
+  float xc[NTT];
+#pragma unroll
+  for (int nt = 0; nt < NTT; ++nt) xc[nt] = sp.vk[k][acc_col(nt)];
+  float y[MTW][4];
+#pragma unroll
+  for (int mi = 0; mi < MTW; ++mi)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float p = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NTT; ++nt) p += A.v[mi][nt][r] * xc[nt];
+      y[mi][r] = row_sum16(p);
+    }
+  write_col_partials<D>(A, y, sp);
 }
 
-constexpr int kMaxPowerIters = 500;
-// Stop when the estimated remaining relative error of the Rayleigh value
-// ||A x|| / ||x|| falls below this (far below the fp32 rounding of A).
-constexpr double kPowerTol = 1e-10;
+// One Lanczos step on wave 0 (lane l holds entries l + 64 e).
+template <int D>
+__device__ __forceinline__ void lanczos_step(SpectralLds<D>& sp, int k, int l) {
+  constexpr int E = D / 64;
+  float w0[E], w[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) s += sp.xpart[q][l + 64 * e];
+    w0[e] = s;
+    w[e] = s;
+  }
+  double alpha = 0.0;
+#pragma unroll
+  for (int kk = 0; kk < kLanczosK; ++kk) {
+    if (kk <= k) {
+      double part = 0.0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) part += static_cast<double>(w0[e]) * sp.vk[kk][l + 64 * e];
+      const double c = wave_sum_f64(part);
+      if (kk == k) alpha = c;
+      const float cf = static_cast<float>(c);
+#pragma unroll
+      for (int e = 0; e < E; ++e) w[e] -= cf * sp.vk[kk][l + 64 * e];
+    }
+  }
+  double n = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) n += static_cast<double>(w[e]) * w[e];
+  const double beta = sqrt(wave_sum_f64(n));
+  const float inv = beta > 0.0 ? static_cast<float>(1.0 / beta) : 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) sp.vk[k + 1][l + 64 * e] = w[e] * inv;
+  if (l == 0) {
+    sp.alpha[k] = alpha;
+    sp.beta[k] = beta;
+  }
+}
+
+// Number of eigenvalues below x of the tridiagonal (al, be): sign changes of
+// the Sturm sequence p_i = det(T_i - x I), evaluated without division.
+__device__ __forceinline__ int sturm_below(const double (&al)[kLanczosK], const double (&be)[kLanczosK], double x) {
+  double p0 = 1.0, p1 = al[0] - x;
+  int changes = p1 < 0.0 ? 1 : 0;
+#pragma unroll
+  for (int i = 1; i < kLanczosK; ++i) {
+    const double p2 = (al[i] - x) * p1 - be[i - 1] * be[i - 1] * p0;
+    changes += ((p2 < 0.0) != (p1 < 0.0)) ? 1 : 0;
+    p0 = p1;
+    p1 = p2;
+  }
+  return changes;
+}
+
+// Bracket the m-th largest eigenvalue inside [lo, hi] by 64-point multisection.
+__device__ __forceinline__ void multisect(const double (&al)[kLanczosK], const double (&be)[kLanczosK], int m,
+                                          int rounds, double& lo, double& hi, int l) {
+  for (int r = 0; r < rounds; ++r) {
+    const double step = (hi - lo) / 65.0;
+    const double x = lo + step * (l + 1);
+    const bool above = kLanczosK - sturm_below(al, be, x) >= m;  // x still below theta_m
+    const int c = __builtin_popcountll(__ballot(above));
+    const double nlo = c > 0 ? lo + step * c : lo;
+    const double nhi = c < 64 ? lo + step * (c + 1) : hi;
+    lo = nlo;
+    hi = nhi;
+  }
+}
+
+// End of a cycle on wave 0: Ritz pair, convergence test, restart vector.
+template <int D>
+__device__ __forceinline__ void lanczos_restart(SpectralLds<D>& sp, int l, bool last) {
+  constexpr int K = kLanczosK, E = D / 64;
+  double al[K], be[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    al[i] = sp.alpha[i];
+    be[i] = sp.beta[i];
+  }
+  double lo = al[0], hi = al[0];
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const double r = (i > 0 ? fabs(be[i - 1]) : 0.0) + (i < K - 1 ? fabs(be[i]) : 0.0);
+    lo = fmin(lo, al[i] - r);
+    hi = fmax(hi, al[i] + r);
+  }
+  double lo1 = lo, hi1 = hi, lo2 = lo, hi2 = hi;
+  multisect(al, be, 1, 9, lo1, hi1, l);
+  multisect(al, be, 2, 5, lo2, hi2, l);
+  const double theta = 0.5 * (lo1 + hi1);
+  // inverse iteration with (mu I - T), mu just above theta: positive definite
+  const double mu = theta + fmax(fabs(theta) * 1e-13, 1e-300);
+  double s[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) s[i] = 1.0;
+  for (int pass = 0; pass < 2; ++pass) {
+    double cp[K], bp[K];
+    double den = mu - al[0];
+    den = fmax(den, 1e-300);
+    cp[0] = -be[0] / den;
+    bp[0] = s[0] / den;
+#pragma unroll
+    for (int i = 1; i < K; ++i) {
+      den = (mu - al[i]) + be[i - 1] * cp[i - 1];
+      den = fmax(den, 1e-300);
+      cp[i] = -be[i] / den;
+      bp[i] = (s[i] + be[i - 1] * bp[i - 1]) / den;
+    }
+    s[K - 1] = bp[K - 1];
+#pragma unroll
+    for (int i = K - 2; i >= 0; --i) s[i] = bp[i] - cp[i] * s[i + 1];
+    double n = 0.0;
+#pragma unroll
+    for (int i = 0; i < K; ++i) n += s[i] * s[i];
+    const double inv = 1.0 / sqrt(n);
+#pragma unroll
+    for (int i = 0; i < K; ++i) s[i] *= inv;
+  }
+  const double res = fabs(be[K - 1] * s[K - 1]);
+  const double gap = theta - hi2;
+  const bool conv = res == 0.0 || (gap > 0.0 && theta > 0.0 && res * res < kLanczosTol * gap * theta);
+  float x[E];
+  double n = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < K; ++i) acc += static_cast<float>(s[i]) * sp.vk[i][l + 64 * e];
+    x[e] = acc;
+    n += static_cast<double>(acc) * acc;
+  }
+  n = wave_sum_f64(n);
+  const float inv = n > 0.0 ? static_cast<float>(1.0 / sqrt(n)) : 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    sp.xs[l + 64 * e] = x[e];
+    sp.vk[0][l + 64 * e] = x[e] * inv;
+  }
+  if (l == 0) sp.flag = (conv || last) ? 1 : 0;
+}
 
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void k_block_spectral(const E* __restrict__ K, const E* __restrict__ V,
@@ -270,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void k_block_spectral(const E* __restrict
   extern __shared__ __align__(16) unsigned char smem[];
   TileLds<E, D>& s = *reinterpret_cast<TileLds<E, D>*>(smem);
   SpectralLds<D>& sp = *reinterpret_cast<SpectralLds<D>*>(smem + sizeof(TileLds<E, D>));
-  constexpr int MTW = HAcc<D>::MTW, NTT = HAcc<D>::NTT;
+  constexpr int MTW = HAcc<D>::MTW, NTT = HAcc<D>::NTT, NE = D / 64;
   const int bh = blockIdx.y;
   const int t = threadIdx.x, w = t / 64, l = t % 64;
   const E* Kh = K + static_cast<size_t>(bh) * L * D;
@@ -309,84 +481,58 @@ __global__ __launch_bounds__(kThreads) void k_block_spectral(const E* __restrict
 #pragma unroll
       for (int nt = 0; nt < NTT; ++nt) A.v[mi][nt] -= hb.v[mi][nt];
 
-    // x0 = A^T r with a fixed +-1 pattern r over the rows.
-    float y[MTW][4];
-#pragma unroll
-    for (int mi = 0; mi < MTW; ++mi)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) y[mi][r] = start_sign(acc_row<D>(mi, r));
-    write_col_partials<D>(A, y, sp);
-    __syncthreads();
-    if (t < D) {
-      float xp = 0.f;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) xp += sp.xpart[q][t];
-      sp.xs[t] = xp;
-      const double n2 = wave_sum_f64(static_cast<double>(xp) * xp);
-      if (l == 0) sp.red[w][0] = n2;
-    }
-    __syncthreads();
-    double n2 = red_total<D>(sp, 0);
-    bool zero = !(n2 > 0.0);
-    float inv = zero ? 0.f : static_cast<float>(1.0 / sqrt(n2));
-    double delta_prev = 0.0;
-    for (int it = 1; it <= kMaxPowerIters && !zero; ++it) {
-      // y = A x (x = xs * inv), all-reduced over the 16 lanes sharing rows.
-      float xc[NTT];
-#pragma unroll
-      for (int nt = 0; nt < NTT; ++nt) xc[nt] = sp.xs[acc_col(nt)] * inv;
+    // start vector A^T r with a fixed +-1 pattern r over the rows
+    {
+      float y[MTW][4];
 #pragma unroll
       for (int mi = 0; mi < MTW; ++mi)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float p = 0.f;
-#pragma unroll
-          for (int nt = 0; nt < NTT; ++nt) p += A.v[mi][nt][r] * xc[nt];
-          y[mi][r] = row_sum16(p);
-        }
+        for (int r = 0; r < 4; ++r) y[mi][r] = start_sign(acc_row<D>(mi, r));
       write_col_partials<D>(A, y, sp);
-      __syncthreads();
-      if (t < D) {
-        const float xo = sp.xs[t] * inv;
-        float xp = 0.f;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) xp += sp.xpart[q][t];
-        sp.xs[t] = xp;
-        const double a = wave_sum_f64(static_cast<double>(xp) * xp);
-        const double b = wave_sum_f64(static_cast<double>(xp) * xo);
-        const double c = wave_sum_f64(static_cast<double>(xo) * xo);
-        if (l == 0) {
-          sp.red[w][0] = a;
-          sp.red[w][1] = b;
-          sp.red[w][2] = c;
-        }
-      }
-      __syncthreads();
-      n2 = red_total<D>(sp, 0);
-      const double dp = red_total<D>(sp, 1), o2 = red_total<D>(sp, 2);
-      if (!(n2 > 0.0)) {
-        zero = true;
-        break;
-      }
-      inv = static_cast<float>(1.0 / sqrt(n2));
-      const double cosang = dp / sqrt(n2 * o2);
-      const double delta2 = fmax(0.0, 2.0 - 2.0 * cosang);
-      const double delta = sqrt(delta2);
-      if (it >= 2) {
-        if (delta == 0.0) break;
-        double rho = delta_prev > 0.0 ? delta / delta_prev : 0.999;
-        rho = fmin(rho, 0.999);
-        if (delta2 * rho * rho / (2.0 * (1.0 - rho)) < kPowerTol) break;
-      }
-      delta_prev = delta;
     }
-    // M_j = ||A x|| / ||x|| evaluated in fp64 from the fp32 iterate.
+    __syncthreads();
+    if (w == 0) {
+      float x[NE];
+      double n = 0.0;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) sum += sp.xpart[q][l + 64 * e];
+        x[e] = sum;
+        n += static_cast<double>(sum) * sum;
+      }
+      n = wave_sum_f64(n);
+      const float inv = n > 0.0 ? static_cast<float>(1.0 / sqrt(n)) : 0.f;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        sp.vk[0][l + 64 * e] = x[e] * inv;
+        sp.xs[l + 64 * e] = x[e];
+      }
+      if (l == 0) sp.flag = n > 0.0 ? 0 : 2;
+    }
+    __syncthreads();
+    const bool zero = sp.flag == 2;
+    if (!zero) {
+      for (int cyc = 0; cyc < kLanczosCycles; ++cyc) {
+        for (int k = 0; k < kLanczosK; ++k) {
+          apply_ata<D>(A, sp, k);
+          __syncthreads();
+          if (w == 0) lanczos_step<D>(sp, k, l);
+          __syncthreads();
+        }
+        if (w == 0) lanczos_restart<D>(sp, l, cyc == kLanczosCycles - 1);
+        __syncthreads();
+        if (sp.flag == 1) break;
+      }
+    }
+    // M_j = ||A x|| / ||x|| in fp64 from the fp32 Ritz vector.
     double mval = 0.0;
     if (!zero) {
-      double ysq = 0.0;
       float xc[NTT];
 #pragma unroll
       for (int nt = 0; nt < NTT; ++nt) xc[nt] = sp.xs[acc_col(nt)];
+      double ysq = 0.0;
 #pragma unroll
       for (int mi = 0; mi < MTW; ++mi)
 #pragma unroll
@@ -398,15 +544,18 @@ __global__ __launch_bounds__(kThreads) void k_block_spectral(const E* __restrict
           ysq += p * p;
         }
       if (l % 16 == 0) sp.red2[t / 16] = ysq;
-      if (t < D) {
-        const double x2 = wave_sum_f64(static_cast<double>(sp.xs[t]) * sp.xs[t]);
-        if (l == 0) sp.red[w][0] = x2;
+      if (w == 0) {
+        double x2 = 0.0;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) x2 += static_cast<double>(sp.xs[l + 64 * e]) * sp.xs[l + 64 * e];
+        x2 = wave_sum_f64(x2);
+        if (l == 0) sp.x2 = x2;
       }
       __syncthreads();
       if (t == 0) {
         double ys = 0.0;
         for (int q = 0; q < 16; ++q) ys += sp.red2[q];
-        mval = sqrt(ys / red_total<D>(sp, 0));
+        mval = sqrt(ys / sp.x2);
       }
     }
     if (t == 0) M[static_cast<size_t>(bh) * T + j] = mval;
