@@ -3,25 +3,33 @@
 // "hardware implementation": stage 1 exact, stage 2 zeroth-order scan,
 // stage 3 global first-order correction, then o = N / D).
 //
-// bf16 kernel (k_attn_bf16): one workgroup of 2 waves per query block of 64
-// rows; each wave owns 32 query rows. Per kv tile of 64 keys:
-//   S^T = K Q^T  (v_mfma_f32_32x32x16_bf16, A = K rows from LDS, B = Q^T held
-//                 in registers for the whole kernel). In the C layout of S^T
-//                 every lane holds one query and 32 of the tile's keys, so
-//                 the online-softmax state (running max m, denominator D,
-//                 tail weight c) is per lane and the row max needs one
-//                 cross-half exchange.
-//   O^T += V^T P^T (A = V^T from an LDS tile stored transposed, B = P in
-//                 registers straight from the S^T accumulators: the K rows
-//                 are read in a permuted order so that each lane's 8
-//                 consecutive P values match 8 consecutive keys of V^T).
-// Stage 1 walks the exact blocks of idx in ascending order with the next
-// tile's global loads in flight during the current tile's MFMAs. Stage 2
-// scans all T centroids in chunks of 64 through the same code path (kbar as
-// keys, vsum as values, both rounded to bf16), with blocks of S_i and j >= T
-// masked, adding n_j * p to D and p to c. Stage 3 forms r^T = Hbar^T q^T on
-// MFMA (Hbar rounded to bf16, transposed into LDS) and adds
-// (scale * c) * r before the final division.
+// bf16 kernel (k_attn_bf16): a workgroup of 4 waves serves 4 consecutive
+// query blocks of one (batch, head), one wave per block of 64 rows.
+//  * The exact lists of the 4 blocks are merged into their sorted union; each
+//    union tile (64 keys x d) is staged once into LDS for the 4 waves (the
+//    global loads of the next tile sit in registers while the current one is
+//    consumed; two LDS buffers; one barrier per tile). K is stored row-major
+//    and V transposed (V^T[dim][key]), both with XOR-swizzled 16-byte chunks,
+//    so every MFMA operand is one conflict-free ds_read_b128.
+//  * A wave computes S^T = K Q^T for its 64 queries as two 32-row halves on
+//    v_mfma_f32_32x32x16_bf16, both halves fed by the same K operand read; Q^T
+//    stays in registers. In the C layout of S^T each lane owns one query per
+//    half and 32 keys, so the softmax state is per lane.
+//  * O^T += V^T P^T with P straight from the S^T accumulators (K rows are read
+//    in a permuted order so each lane's 8 consecutive P values are 8
+//    consecutive keys of a V^T row). The O^T accumulators are only ever
+//    written by MFMAs inside the tile loops.
+//  * The softmax reference m is fixed by the first tile a wave sees and never
+//    moves, so O needs no rescaling: N and D share the factor exp(-m), which
+//    cancels in N / D. A tile whose maximum exceeds m by more than 2^64 (far
+//    beyond real attention logits) marks the wave, and after the pass the
+//    marked waves recompute their block with m set to the exact maximum
+//    recorded during the first pass.
+//  * Stage 2 runs the same tile code over all T centroids in chunks of 32
+//    (kbar as keys, vsum as values, converted to bf16 while staging), with the
+//    blocks of S_i and j >= T masked; the weights add n_j p to D and p to c.
+//  * Stage 3 forms r^T = Hbar^T q^T on MFMA (Hbar transposed into LDS in
+//    bf16) and adds (scale c) r before the division.
 //
 // fp32 kernel (k_attn_f32): the same three stages in plain fp32 arithmetic,
 // one key at a time; used for fp32 problems.
@@ -33,200 +41,213 @@ namespace paro {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-
-// ------------------------------------------------------------------ bf16
-constexpr int kAttnThreads = 128;
+constexpr int kWaves = 4;                 // query blocks per workgroup
+constexpr int kAttnThreads = 64 * kWaves;
+constexpr float kOverflowSlack = 64.f;    // log2 units above the reference max that trigger a rerun
 
 template <int D>
-struct AttnLds {
-  static constexpr int KS = D + 8;   // row stride of the key tile
-  static constexpr int VS = 64 + 8;  // row stride of the transposed value tile
-  uint16_t ks[64][KS];
-  uint16_t vt[D][VS];
-};
-// Hbar^T staged in bf16 reuses the tile region after both loops.
-template <int D>
-struct HtLds {
-  uint16_t ht[D][D + 8];
+struct Geo {
+  static constexpr int CG = D / 8;                         // 16-byte chunks in a K row
+  static constexpr int TILE = 64 * D;                      // bf16 elements of a K or V tile
+  static constexpr int NK = D / 16;                        // k-steps of S^T = K Q^T
+  static constexpr int NU = D / 32;                        // 32-dim output tiles
+  static constexpr int KPT = 64 * CG / kAttnThreads;       // K chunks staged per thread
 };
 
-// Key (row of the K tile) that MFMA row m of S^T sub-tile t reads, chosen so
-// that accumulator register i of a lane in half g holds key
-// 32 t + 16 (i / 8) + 8 g + (i % 8).
+// K tile: row-major [64 keys][D], chunk c of row r stored at c ^ kswz(r).
+template <int D>
+__device__ __forceinline__ int k_off(int row, int c) {
+  const int f = (((row & 7) << 1) | ((row >> 3) & 1)) & (Geo<D>::CG - 1);
+  return row * D + 8 * (c ^ f);
+}
+// Transposed tile with rows of `rlen` elements: chunk c of row r at c ^ (r & 7).
+__device__ __forceinline__ int t_off(int row, int c, int rlen) { return row * rlen + 8 * (c ^ (row & 7)); }
+
+// Key (tile row) that MFMA row m of S^T sub-tile t reads, chosen so that
+// accumulator register i of a lane in half g holds key 32 t + 16 (i/8) + 8 g + i%8.
 __device__ __forceinline__ int perm_key(int t, int m) {
   const int a = m >> 3, g = (m >> 2) & 1, b = m & 3;
   return 32 * t + 16 * (a >> 1) + 8 * g + 4 * (a & 1) + b;
 }
-
-template <int D>
-struct TileRegs {
-  uint4 k[D / 16];     // 64 rows x D/8 chunks of 16 B = 8D chunks / 128 threads
-  uint4 v[D / 64][4];  // 16 token groups x D/8 dim groups = 2D items / 128 threads
-};
-
-// Global -> registers for one exact kv tile (rows >= nvalid zero-filled).
-template <int D>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ Kh, const uint16_t* __restrict__ Vh,
-                                          int row0, int nvalid, TileRegs<D>& r) {
-  constexpr int CG = D / 8;
-#pragma unroll
-  for (int i = 0; i < D / 16; ++i) {
-    const int c = threadIdx.x + kAttnThreads * i;
-    const int row = c / CG, cg = c % CG;
-    r.k[i] = row < nvalid ? *reinterpret_cast<const uint4*>(Kh + static_cast<size_t>(row0 + row) * D + 8 * cg)
-                          : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) {
-    const int item = threadIdx.x + kAttnThreads * i;
-    const int tg = item / CG, dg = item % CG;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int tok = 4 * tg + q;
-      r.v[i][q] = tok < nvalid
-                      ? *reinterpret_cast<const uint4*>(Vh + static_cast<size_t>(row0 + tok) * D + 8 * dg)
-                      : make_uint4(0, 0, 0, 0);
-    }
-  }
-}
+__device__ __forceinline__ int reg_key(int t, int i, int g) { return 32 * t + 16 * (i >> 3) + 8 * g + (i & 7); }
 
 __device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
   const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
   return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
-
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, AttnLds<D>& s) {
-  constexpr int CG = D / 8;
-#pragma unroll
-  for (int i = 0; i < D / 16; ++i) {
-    const int c = threadIdx.x + kAttnThreads * i;
-    *reinterpret_cast<uint4*>(&s.ks[c / CG][8 * (c % CG)]) = r.k[i];
-  }
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) {
-    const int item = threadIdx.x + kAttnThreads * i;
-    const int tg = item / CG, dg = item % CG;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t w0 = half16(r.v[i][0], e) | (half16(r.v[i][1], e) << 16);
-      const uint32_t w1 = half16(r.v[i][2], e) | (half16(r.v[i][3], e) << 16);
-      *reinterpret_cast<uint2*>(&s.vt[8 * dg + e][4 * tg]) = make_uint2(w0, w1);
-    }
-  }
+__device__ __forceinline__ uint4 to_bf16x8(const float4& a, const float4& b) {
+  return make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
 }
 
-// Tail chunk: centroids [64 c, 64 c + 64) of kbar / vsum (fp32 -> bf16) into LDS.
+// ------------------------------------------------------------ staging
+// One step's data in flight, KPT + 4 registers of 16 bytes per thread:
+//  exact tile (bf16): r[0..KPT) = K chunks (row-major), r[KPT..KPT+4) = 4 keys x 8 dims of V;
+//  centroid chunk (fp32, 32 centroids): r[0..KPT) = kbar chunks as float4 pairs,
+//  r[KPT..KPT+4) = 2 centroids x 8 dims of vsum.
 template <int D>
-__device__ __forceinline__ void stage_centroids(const float* __restrict__ kb, const float* __restrict__ vs,
-                                                int j0, int T, AttnLds<D>& s) {
-  constexpr int CG = D / 8;
-#pragma unroll
-  for (int i = 0; i < D / 16; ++i) {
-    const int c = threadIdx.x + kAttnThreads * i;
-    const int row = c / CG, cg = c % CG;
-    uint4 o = make_uint4(0, 0, 0, 0);
-    if (j0 + row < T) {
-      const float4* src = reinterpret_cast<const float4*>(kb + static_cast<size_t>(j0 + row) * D + 8 * cg);
-      const float4 x = src[0], y = src[1];
-      o = make_uint4(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w), pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
-    }
-    *reinterpret_cast<uint4*>(&s.ks[row][8 * cg]) = o;
-  }
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) {
-    const int item = threadIdx.x + kAttnThreads * i;
-    const int tg = item / CG, dg = item % CG;
-    float f[4][8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int jj = j0 + 4 * tg + q;
-      if (jj < T) {
-        const float4* src = reinterpret_cast<const float4*>(vs + static_cast<size_t>(jj) * D + 8 * dg);
-        const float4 x = src[0], y = src[1];
-        f[q][0] = x.x; f[q][1] = x.y; f[q][2] = x.z; f[q][3] = x.w;
-        f[q][4] = y.x; f[q][5] = y.y; f[q][6] = y.z; f[q][7] = y.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[q][e] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<uint2*>(&s.vt[8 * dg + e][4 * tg]) =
-          make_uint2(pack_bf16x2(f[0][e], f[1][e]), pack_bf16x2(f[2][e], f[3][e]));
-  }
-}
-
-template <int D>
-struct AttnState {
-  bf16x8 qb[D / 16];    // B operand Q^T: query (lane % 32), dims 16 s + 8 g .. + 8
-  f32x16 o[D / 32];     // O^T accumulators, dims 32 u + 8 (i / 4) + 4 g + i % 4
-  float m;              // running max (log2 domain), equal in both halves
-  float dsum;           // this lane's part of D
-  float csum;           // this lane's part of c = sum of tail weights
+struct Stage {
+  uint4 r[Geo<D>::KPT + 4];
 };
 
-// One 64-key tile from LDS. Keys whose mask bit is set get weight 0.
-// kTail adds n_j * p to D (instead of p) and p to c.
-template <int D, bool kTail>
-__device__ __forceinline__ void tile_step(const AttnLds<D>& s, AttnState<D>& st, float cl2, uint64_t keymask,
-                                          int nlast_key, float nlast) {
-  const int l = threadIdx.x % 64, g = l / 32, ql = l % 32;
-  f32x16 sacc[2];
+template <int D>
+__device__ __forceinline__ void load_exact(const uint16_t* __restrict__ Kh, const uint16_t* __restrict__ Vh,
+                                           int row0, int nvalid, Stage<D>& st) {
+  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    sacc[t] = f32x16{};
-    const uint16_t* krow = &s.ks[perm_key(t, ql)][8 * g];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      sacc[t] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(krow + 16 * ks), st.qb[ks], sacc[t]);
+  for (int i = 0; i < KPT; ++i) {
+    const int q = threadIdx.x + kAttnThreads * i;
+    const int row = q / CG, c = q % CG;
+    st.r[i] = row < nvalid ? *reinterpret_cast<const uint4*>(Kh + static_cast<size_t>(row0 + row) * D + 8 * c)
+                           : make_uint4(0, 0, 0, 0);
   }
-  // logits in log2 units, masked keys -> -inf
-  float mx = -INFINITY;
+  const int item = threadIdx.x;  // 16 key groups x CG dim groups
+  const int kg = item / CG, dg = item % CG;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int e = 0; e < 4; ++e) {
+    const int row = 4 * kg + e;
+    st.r[KPT + e] = (item < 16 * CG && row < nvalid)
+                        ? *reinterpret_cast<const uint4*>(Vh + static_cast<size_t>(row0 + row) * D + 8 * dg)
+                        : make_uint4(0, 0, 0, 0);
+  }
+}
+template <int D>
+__device__ __forceinline__ void store_exact(const Stage<D>& st, uint16_t* kt, uint16_t* vt) {
+  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int q = threadIdx.x + kAttnThreads * i;
+    *reinterpret_cast<uint4*>(kt + k_off<D>(q / CG, q % CG)) = st.r[i];
+  }
+  const int item = threadIdx.x;
+  if (item < 16 * CG) {
+    const int kg = item / CG, dg = item % CG;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w0 = half16(st.r[KPT], e) | (half16(st.r[KPT + 1], e) << 16);
+      const uint32_t w1 = half16(st.r[KPT + 2], e) | (half16(st.r[KPT + 3], e) << 16);
+      *reinterpret_cast<uint2*>(vt + t_off(8 * dg + e, kg >> 1, 64) + 4 * (kg & 1)) = make_uint2(w0, w1);
+    }
+  }
+}
+// Tail chunk of 32 centroids [j0, j0 + 32): kbar rows -> K tile rows 0..31,
+// vsum rows -> keys 0..31 of the V^T tile (fp32 converted to bf16 on store).
+template <int D>
+__device__ __forceinline__ void load_centroids(const float* __restrict__ kb, const float* __restrict__ vs, int j0,
+                                               int T, Stage<D>& st) {
+  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT;
+  const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < KPT / 2; ++i) {
+    const int q = threadIdx.x + kAttnThreads * i;
+    const int row = q / CG, c = q % CG;
+    const bool ok = j0 + row < T;
+    const uint4* src = reinterpret_cast<const uint4*>(kb + static_cast<size_t>(j0 + row) * D + 8 * c);
+    st.r[2 * i] = ok ? src[0] : z;
+    st.r[2 * i + 1] = ok ? src[1] : z;
+  }
+  const int item = threadIdx.x;  // 16 centroid pairs x CG dim groups
+  const int kp = item / CG, dg = item % CG;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int row = 2 * kp + e;
+    const bool ok = item < 16 * CG && j0 + row < T;
+    const uint4* src = reinterpret_cast<const uint4*>(vs + static_cast<size_t>(j0 + row) * D + 8 * dg);
+    st.r[KPT + 2 * e] = ok ? src[0] : z;
+    st.r[KPT + 2 * e + 1] = ok ? src[1] : z;
+  }
+}
+__device__ __forceinline__ float4 as_f4(const uint4& u) { return __builtin_bit_cast(float4, u); }
+template <int D>
+__device__ __forceinline__ void store_centroids(const Stage<D>& st, uint16_t* kt, uint16_t* vt) {
+  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT;
+#pragma unroll
+  for (int i = 0; i < KPT / 2; ++i) {
+    const int q = threadIdx.x + kAttnThreads * i;
+    *reinterpret_cast<uint4*>(kt + k_off<D>(q / CG, q % CG)) = to_bf16x8(as_f4(st.r[2 * i]), as_f4(st.r[2 * i + 1]));
+  }
+  const int item = threadIdx.x;
+  if (item < 16 * CG) {
+    const int kp = item / CG, dg = item % CG;
+    const float4 x0 = as_f4(st.r[KPT]), y0 = as_f4(st.r[KPT + 1]), x1 = as_f4(st.r[KPT + 2]), y1 = as_f4(st.r[KPT + 3]);
+    const float a0[8] = {x0.x, x0.y, x0.z, x0.w, y0.x, y0.y, y0.z, y0.w};
+    const float a1[8] = {x1.x, x1.y, x1.z, x1.w, y1.x, y1.y, y1.z, y1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      *reinterpret_cast<uint32_t*>(vt + t_off(8 * dg + e, kp >> 2, 64) + 2 * (kp & 3)) = pack_bf16x2(a0[e], a1[e]);
+  }
+}
+
+// ------------------------------------------------------------ compute
+template <int D>
+struct Acc {
+  bf16x8 qb[2][Geo<D>::NK];   // B operand Q^T of half h: query 32 h + lane % 32, dims 16 s + 8 g .. + 8
+  f32x16 o[Geo<D>::NU][2];    // O^T: dims 32 u + 8 (i / 4) + 4 g + i % 4, query 32 h + lane % 32
+  float m[2];                 // reference max (log2 units), -inf until the first tile
+  float mtrue[2];             // exact running max, for a rerun
+  float dsum[2];              // this lane's part of D
+  float csum[2];              // this lane's part of c
+  bool over;                  // some logit exceeded m + kOverflowSlack
+};
+
+template <int D>
+__device__ __forceinline__ void qk_half(const uint16_t* kt, const Acc<D>& a, int t, f32x16 (&s)[2]) {
+  const int l = threadIdx.x & 63, g = l >> 5, ql = l & 31;
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+  const int row = perm_key(t, ql);
+#pragma unroll
+  for (int ks = 0; ks < Geo<D>::NK; ++ks) {
+    const bf16x8 av = *reinterpret_cast<const bf16x8*>(kt + k_off<D>(row, g + 2 * ks));
+    s[0] = mfma32x32x16(av, a.qb[0][ks], s[0]);
+    s[1] = mfma32x32x16(av, a.qb[1][ks], s[1]);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void pv_half(const uint16_t* vt, int t, const bf16x8 (&pb)[2][2], Acc<D>& a) {
+  const int l = threadIdx.x & 63, g = l >> 5, ql = l & 31;
+#pragma unroll
+  for (int u = 0; u < Geo<D>::NU; ++u)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt + t_off(32 * u + ql, 4 * t + 2 * s + g, 64));
+      a.o[u][0] = mfma32x32x16(av, pb[0][s], a.o[u][0]);
+      a.o[u][1] = mfma32x32x16(av, pb[1][s], a.o[u][1]);
+    }
+}
+
+// Softmax weights of one 32-key sub-tile against the fixed reference max.
+template <int D, bool kMask, bool kTail>
+__device__ __forceinline__ void softmax_half(f32x16 (&s)[2], Acc<D>& a, int t, float cl2, uint64_t keymask,
+                                             int nlast_key, float nlast, bf16x8 (&pb)[2][2]) {
+  const int g = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float v = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = 32 * t + 16 * (i / 8) + 8 * g + (i % 8);
-      const float x = ((keymask >> key) & 1ull) ? -INFINITY : sacc[t][i] * cl2;
-      sacc[t][i] = x;
-      mx = fmaxf(mx, x);
+      if (kMask && ((keymask >> reg_key(t, i, g)) & 1ull)) s[h][i] = -INFINITY;
+      v = fmaxf(v, s[h][i]);
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  // While every key seen so far is masked the max stays -inf; subtracting 0
-  // instead keeps every weight (and alpha) exactly 0 without a branch.
-  const float mnew = fmaxf(st.m, mx);
-  const float mref = mnew == -INFINITY ? 0.f : mnew;
-  const float alpha = __builtin_amdgcn_exp2f(st.m - mref);
-  st.m = mnew;
-  float psum = 0.f, pw = 0.f;
-  bf16x8 pb[4];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
+    v = fmaxf(v, __shfl_xor(v, 32)) * cl2;
+    a.mtrue[h] = fmaxf(a.mtrue[h], v);
+    if (a.m[h] == -INFINITY) a.m[h] = v;
+    a.over = a.over || v > a.m[h] + kOverflowSlack;
+    const float mref = a.m[h] == -INFINITY ? 0.f : a.m[h];
+    float ps = 0.f, pw = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(sacc[t][i] - mref);
-      psum += p;
-      if (kTail) {
-        const int key = 32 * t + 16 * (i / 8) + 8 * g + (i % 8);
-        pw += key == nlast_key ? p * nlast : p * 64.f;
-      }
-      pb[2 * t + i / 8][i % 8] = static_cast<__bf16>(p);
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][i], cl2, -mref));
+      ps += p;
+      if (kTail) pw += reg_key(t, i, g) == nlast_key ? p * nlast : p * 64.f;
+      pb[h][i >> 3][i & 7] = static_cast<__bf16>(p);
     }
-  if (kTail) {
-    st.dsum = st.dsum * alpha + pw;
-    st.csum = st.csum * alpha + psum;
-  } else {
-    st.dsum = st.dsum * alpha + psum;
-  }
-#pragma unroll
-  for (int u = 0; u < D / 32; ++u) {
-    st.o[u] *= alpha;
-    const uint16_t* vrow = &s.vt[32 * u + ql][8 * g];
-#pragma unroll
-    for (int sp = 0; sp < 4; ++sp)
-      st.o[u] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(vrow + 16 * sp), pb[sp], st.o[u]);
+    if (kTail) {
+      a.dsum[h] += pw;
+      a.csum[h] += ps;
+    } else {
+      a.dsum[h] += ps;
+    }
   }
 }
 
@@ -234,122 +255,232 @@ template <int D>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const float* __restrict__ kbar, const float* __restrict__ vsum, const float* __restrict__ Hbar,
-    const int32_t* __restrict__ idx, uint16_t* __restrict__ O, int L, int T, int keep_k, float scale,
-    int nwg) {
+    const int32_t* __restrict__ idx, uint16_t* __restrict__ O, int L, int T, int keep_k, float scale, int nwg) {
+  constexpr int TILE = Geo<D>::TILE;
   extern __shared__ __align__(16) unsigned char smem[];
-  AttnLds<D>& s = *reinterpret_cast<AttnLds<D>*>(smem);
-  uint32_t* selmask = reinterpret_cast<uint32_t*>(smem + sizeof(AttnLds<D>));
+  uint16_t* buf = reinterpret_cast<uint16_t*>(smem);  // 2 x (K tile, V^T tile)
   const int nw = ceil_div(T, 32);
+  uint32_t* masks = reinterpret_cast<uint32_t*>(smem + sizeof(uint16_t) * 4 * TILE);  // [kWaves][nw]
+  int* sh = reinterpret_cast<int*>(masks + kWaves * nw);                             // nu, rerun flags
+  uint16_t* ulist = reinterpret_cast<uint16_t*>(sh + 8);                             // [T]
 
-  // XCD-aware order: consecutive workgroup ids land on different XCDs, so
-  // give each XCD a contiguous run of (head, query block) work items.
+  // XCD-aware order: consecutive workgroup ids go to different XCDs, so hand
+  // each XCD a contiguous run of (head, query-block group) items.
   int wg = blockIdx.x;
   const int n8 = (nwg / 8) * 8;
   if (wg < n8) wg = (wg % 8) * (nwg / 8) + wg / 8;
-  const int qblk = wg % T, bh = wg / T;
+  const int ngrp = ceil_div(T, kWaves);
+  const int grp = wg % ngrp, bh = wg / ngrp;
 
-  const int tid = threadIdx.x, w = tid / 64, l = tid % 64, g = l / 32, ql = l % 32;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, ql = l & 31;
+  const int qblk = grp * kWaves + w;
+  const bool qvalid = qblk < T;
   const size_t head = static_cast<size_t>(bh) * L * D;
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
-  const int32_t* irow = idx + (static_cast<size_t>(bh) * T + qblk) * keep_k;
   const float cl2 = scale * kLog2e;
+  const int nlast = L - 64 * (T - 1);
 
-  AttnState<D> st;
-  const int qrow = qblk * 64 + 32 * w + ql;
-  {
-    const uint16_t* qp = Q + head + static_cast<size_t>(qrow) * D + 8 * g;
+  Acc<D> a;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      uint4 v = qrow < L ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
-      st.qb[ks] = __builtin_bit_cast(bf16x8, v);
+  for (int h = 0; h < 2; ++h) {
+    const int row = qblk * 64 + 32 * h + ql;
+    const uint16_t* qp = Q + head + static_cast<size_t>(row) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < Geo<D>::NK; ++ks) {
+      const uint4 v = (qvalid && row < L) ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
+      a.qb[h][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+    a.m[h] = -INFINITY;
+    a.mtrue[h] = -INFINITY;
+  }
+
+  // ---- membership masks of the 4 exact lists and their sorted union
+  for (int e = tid; e < kWaves * nw; e += kAttnThreads) masks[e] = 0u;
+  __syncthreads();
+  if (qvalid) {
+    const int32_t* irow = idx + (static_cast<size_t>(bh) * T + qblk) * keep_k;
+    for (int e = l; e < keep_k; e += 64) {
+      const int j = min(max(irow[e], 0), T - 1);
+      atomicOr(&masks[w * nw + (j >> 5)], 1u << (j & 31));
     }
   }
-#pragma unroll
-  for (int u = 0; u < D / 32; ++u) st.o[u] = f32x16{};
-  st.m = -INFINITY;
-  st.dsum = 0.f;
-  st.csum = 0.f;
-
-  const int nlast = L - 64 * (T - 1);  // valid keys in the last block
-
-  // ---- stage 1: exact blocks
-  if (keep_k > 0) {
-    TileRegs<D> regs;
-    int j = min(max(irow[0], 0), T - 1);
-    load_tile<D>(Kh, Vh, 64 * j, j == T - 1 ? nlast : 64, regs);
-    for (int it = 0; it < keep_k; ++it) {
-      const int nvalid = j == T - 1 ? nlast : 64;
-      __syncthreads();
-      store_tile<D>(regs, s);
-      __syncthreads();
-      if (it + 1 < keep_k) {
-        j = min(max(irow[it + 1], 0), T - 1);
-        load_tile<D>(Kh, Vh, 64 * j, j == T - 1 ? nlast : 64, regs);
+  __syncthreads();
+  if (w == 0) {
+    int base = 0;
+    for (int w0 = 0; w0 < nw; w0 += 64) {
+      const int wd = w0 + l;
+      uint32_t u = 0;
+      if (wd < nw) u = masks[wd] | masks[nw + wd] | masks[2 * nw + wd] | masks[3 * nw + wd];
+      const int cnt = __builtin_popcount(u);
+      int incl = cnt;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (l >= o) incl += v;
       }
-      const uint64_t km = nvalid == 64 ? 0ull : (~0ull << nvalid);
-      tile_step<D, false>(s, st, cl2, km, -1, 0.f);
+      int pos = base + incl - cnt;
+      while (u) {
+        ulist[pos++] = static_cast<uint16_t>(wd * 32 + __builtin_ctz(u));
+        u &= u - 1;
+      }
+      base += __shfl(incl, 63);
     }
+    if (l == 0) sh[0] = base;
   }
+  __syncthreads();
+  const int nu = sh[0];
+  const uint32_t* mymask = masks + w * nw;
+  const float* kb = kbar + static_cast<size_t>(bh) * T * D;
+  const float* vs = vsum + static_cast<size_t>(bh) * T * D;
+  const int nch = keep_k < T ? ceil_div(T, 32) : 0;
 
-  // ---- stage 2: zeroth-order scan over the centroids of U_i
-  if (keep_k < T) {
-    for (int wd = tid; wd < nw; wd += kAttnThreads) selmask[wd] = 0u;
+  bool active = qvalid;
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int u = 0; u < Geo<D>::NU; ++u) a.o[u][h] = f32x16{};
+      a.dsum[h] = 0.f;
+      a.csum[h] = 0.f;
+    }
+    a.over = false;
+
+    // ---- stages 1 and 2 as one stream of steps: the nu exact tiles of the
+    // union, then the nch chunks of 32 centroids. A single qk / pv code path
+    // serves both, so the O^T accumulators keep one register assignment.
+    const int nsteps = nu + nch;
+    Stage<D> st;
+    auto fetch = [&](int step) {
+      if (step < nu) {
+        const int j = ulist[step];
+        load_exact<D>(Kh, Vh, 64 * j, j == T - 1 ? nlast : 64, st);
+      } else {
+        load_centroids<D>(kb, vs, 32 * (step - nu), T, st);
+      }
+    };
+    auto put = [&](int step, uint16_t* kt) {
+      if (step < nu)
+        store_exact<D>(st, kt, kt + TILE);
+      else
+        store_centroids<D>(st, kt, kt + TILE);
+    };
+    if (nsteps > 0) {
+      fetch(0);
+      put(0, buf);
+    }
     __syncthreads();
-    for (int e = tid; e < keep_k; e += kAttnThreads) {
-      const int jj = min(max(irow[e], 0), T - 1);
-      atomicOr(&selmask[jj >> 5], 1u << (jj & 31));
-    }
-    for (int j0 = 0; j0 < T; j0 += 64) {
-      __syncthreads();
-      stage_centroids<D>(kbar + static_cast<size_t>(bh) * T * D, vsum + static_cast<size_t>(bh) * T * D, j0, T, s);
-      __syncthreads();
+    if (nsteps > 1) fetch(1);
+    for (int step = 0; step < nsteps; ++step) {
+      const uint16_t* kc = buf + (step & 1) * 2 * TILE;
+      const bool tail = step >= nu;
+      const int j = tail ? 0 : ulist[step];
+      bool work = active;
       uint64_t km = 0;
-      for (int b = 0; b < 2; ++b) {
-        const int wd = j0 / 32 + b;
-        const uint32_t word = wd < nw ? selmask[wd] : 0xFFFFFFFFu;
-        km |= static_cast<uint64_t>(word) << (32 * b);
+      int nsub = 2;
+      int nlast_key = -1;
+      if (!tail) {
+        work = work && ((mymask[j >> 5] >> (j & 31)) & 1u);
+        if (j == T - 1 && nlast < 64) km = ~0ull << nlast;
+      } else {
+        const int j0 = 32 * (step - nu);
+        km = 0xFFFFFFFF00000000ull | ((j0 >> 5) < nw ? mymask[j0 >> 5] : 0xFFFFFFFFu);
+        if (j0 + 32 > T) km |= ~0ull << (T - j0);
+        nsub = 1;
+        nlast_key = T - 1 - j0;
       }
-      if (j0 + 64 > T) km |= ~0ull << (T - j0);
-      tile_step<D, true>(s, st, cl2, km, T - 1 - j0, static_cast<float>(nlast));
+      if (work) {
+#pragma unroll 1
+        for (int t = 0; t < nsub; ++t) {
+          f32x16 sacc[2];
+          bf16x8 pb[2][2];
+          qk_half<D>(kc, a, t, sacc);
+          if (tail)
+            softmax_half<D, true, true>(sacc, a, t, cl2, km, nlast_key, static_cast<float>(nlast), pb);
+          else if (km)
+            softmax_half<D, true, false>(sacc, a, t, cl2, km, -1, 0.f, pb);
+          else
+            softmax_half<D, false, false>(sacc, a, t, cl2, 0ull, -1, 0.f, pb);
+          pv_half<D>(kc + TILE, t, pb, a);
+        }
+      }
+      if (step + 1 < nsteps) put(step + 1, buf + ((step + 1) & 1) * 2 * TILE);
+      if (step + 2 < nsteps) fetch(step + 2);
+      __syncthreads();
+    }
+
+    // ---- rerun the blocks whose logits outgrew their reference max
+    const bool mine = active && __any(a.over);
+    if (l == 0) sh[1 + w] = mine ? 1 : 0;
+    __syncthreads();
+    const bool any = sh[1] | sh[2] | sh[3] | sh[4];
+    __syncthreads();
+    if (!any) break;
+    active = mine;
+    if (mine) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) a.m[h] = a.mtrue[h];
     }
   }
 
   // ---- stage 3: global first-order correction, then N / D
-  const float csum = st.csum + __shfl_xor(st.csum, 32);
-  const float dsum = st.dsum + __shfl_xor(st.dsum, 32);
-  __syncthreads();
-  HtLds<D>& h = *reinterpret_cast<HtLds<D>*>(smem);
-  {
+  float csum[2], dsum[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    csum[h] = a.csum[h] + __shfl_xor(a.csum[h], 32);
+    dsum[h] = a.dsum[h] + __shfl_xor(a.dsum[h], 32);
+  }
+  if (nch > 0) {
+    // Hbar^T in bf16: ht[v][k] = Hbar[k][v], rows of D elements
     const float* Hh = Hbar + static_cast<size_t>(bh) * D * D;
-    for (int e = tid; e < D * D; e += kAttnThreads) {
-      const int kr = e / D, vc = e % D;  // Hbar[kr][vc] -> ht[vc][kr]
-      h.ht[vc][kr] = f32_to_bf16(Hh[e]);
-    }
-  }
-  __syncthreads();
-  const float cs = scale * csum;
-  const float inv = 1.f / dsum;
+    for (int item = tid; item < (D / 4) * Geo<D>::CG; item += kAttnThreads) {
+      const int kg = item / Geo<D>::CG, vg = item % Geo<D>::CG;
+      float f[4][8];
 #pragma unroll
-  for (int u = 0; u < D / 32; ++u) {
-    f32x16 r = f32x16{};
-    const uint16_t* hrow = &h.ht[32 * u + ql][8 * g];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      r = mfma32x32x16(*reinterpret_cast<const bf16x8*>(hrow + 16 * ks), st.qb[ks], r);
-    st.o[u] += cs * r;
-  }
-  if (qrow < L) {
-    uint16_t* op = O + head + static_cast<size_t>(qrow) * D;
-#pragma unroll
-    for (int u = 0; u < D / 32; ++u)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int dim = 32 * u + 8 * a + 4 * g;
-        const uint2 v = make_uint2(pack_bf16x2(st.o[u][4 * a] * inv, st.o[u][4 * a + 1] * inv),
-                                   pack_bf16x2(st.o[u][4 * a + 2] * inv, st.o[u][4 * a + 3] * inv));
-        *reinterpret_cast<uint2*>(op + dim) = v;
+      for (int e = 0; e < 4; ++e) {
+        const float4* src = reinterpret_cast<const float4*>(Hh + (4 * kg + e) * D + 8 * vg);
+        const float4 x = src[0], y = src[1];
+        f[e][0] = x.x; f[e][1] = x.y; f[e][2] = x.z; f[e][3] = x.w;
+        f[e][4] = y.x; f[e][5] = y.y; f[e][6] = y.z; f[e][7] = y.w;
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint2*>(buf + t_off(8 * vg + e, kg >> 1, D) + 4 * (kg & 1)) =
+            make_uint2(pack_bf16x2(f[0][e], f[1][e]), pack_bf16x2(f[2][e], f[3][e]));
+    }
+    __syncthreads();
+  }
+  if (qvalid) {
+#pragma unroll
+    for (int u = 0; u < Geo<D>::NU; ++u) {
+      f32x16 o0 = a.o[u][0], o1 = a.o[u][1];
+      if (nch > 0) {
+        f32x16 r0 = f32x16{}, r1 = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < Geo<D>::NK; ++ks) {
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(buf + t_off(32 * u + ql, 2 * ks + g, D));
+          r0 = mfma32x32x16(av, a.qb[0][ks], r0);
+          r1 = mfma32x32x16(av, a.qb[1][ks], r1);
+        }
+        o0 += (scale * csum[0]) * r0;
+        o1 += (scale * csum[1]) * r1;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = qblk * 64 + 32 * h + ql;
+        if (row < L) {
+          const float inv = 1.f / dsum[h];
+          const f32x16& o = h == 0 ? o0 : o1;
+          uint16_t* op = O + head + static_cast<size_t>(row) * D;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int dim = 32 * u + 8 * q + 4 * g;
+            *reinterpret_cast<uint2*>(op + dim) =
+                make_uint2(pack_bf16x2(o[4 * q] * inv, o[4 * q + 1] * inv),
+                           pack_bf16x2(o[4 * q + 2] * inv, o[4 * q + 3] * inv));
+          }
+        }
+      }
+    }
   }
 }
 
@@ -446,14 +577,14 @@ hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, cons
                        const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O,
                        hipStream_t s) {
   const int T = ceil_div(p.L, 64);
-  const size_t lds = std::max(sizeof(AttnLds<D>), sizeof(HtLds<D>)) + sizeof(uint32_t) * ceil_div(T, 32);
+  const int nw = ceil_div(T, 32);
+  const size_t lds = sizeof(uint16_t) * 4 * Geo<D>::TILE + sizeof(uint32_t) * kWaves * nw + 8 * sizeof(int) +
+                     sizeof(uint16_t) * T;
   const size_t lds_al = (lds + 15) / 16 * 16;
-  hipError_t e;
-  if (lds_al > 65536 &&
-      (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_bf16<D>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_al))) != hipSuccess)
-    return e;
-  const int nwg = T * p.B * p.H;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_bf16<D>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_al));
+  if (e != hipSuccess) return e;
+  const int nwg = ceil_div(T, kWaves) * p.B * p.H;
   hipLaunchKernelGGL(k_attn_bf16<D>, dim3(nwg), dim3(kAttnThreads), lds_al, s,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), kbar, vsum, Hbar, idx, static_cast<uint16_t*>(O), p.L, T,
