@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-qblocks", type=int, default=48, help="query blocks per head in the oracle sample")
     ap.add_argument("--cpu-heads", type=int, default=1)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a device-to-device copy of this many MiB (scales the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -130,6 +132,14 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
+    if a.copy_calibration_mib:
+        n = a.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
     from block_sparse_attention_pisa_amd import paro
     from workloads import WORKLOADS, make_inputs
 

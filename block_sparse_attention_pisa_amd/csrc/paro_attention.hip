@@ -9,23 +9,25 @@
 //    union tile (64 keys x d) is staged once into LDS for the 4 waves (the
 //    global loads of the next tile sit in registers while the current one is
 //    consumed; two LDS buffers; one barrier per tile). K is stored row-major
-//    and V transposed (V^T[dim][key]), both with XOR-swizzled 16-byte chunks,
-//    so every MFMA operand is one conflict-free ds_read_b128.
+//    and V transposed (V^T[dim][key]); rows are padded so that every MFMA
+//    operand is one conflict-free ds_read_b128 at a per-lane base plus a
+//    compile-time offset.
 //  * A wave computes S^T = K Q^T for its 64 queries as two 32-row halves on
 //    v_mfma_f32_32x32x16_bf16, both halves fed by the same K operand read; Q^T
 //    stays in registers. In the C layout of S^T each lane owns one query per
 //    half and 32 keys, so the softmax state is per lane.
 //  * O^T += V^T P^T with P straight from the S^T accumulators (K rows are read
 //    in a permuted order so each lane's 8 consecutive P values are 8
-//    consecutive keys of a V^T row). The O^T accumulators are only ever
-//    written by MFMAs inside the tile loops.
+//    consecutive keys of a V^T row). The O^T accumulators are only written by
+//    MFMAs inside the tile loop. A tile's two 32-key halves are independent
+//    chains, so one half's softmax can overlap the other's matrix work.
 //  * The softmax reference m is fixed by the first tile a wave sees and never
 //    moves, so O needs no rescaling: N and D share the factor exp(-m), which
 //    cancels in N / D. A tile whose maximum exceeds m by more than 2^64 (far
 //    beyond real attention logits) marks the wave, and after the pass the
 //    marked waves recompute their block with m set to the exact maximum
 //    recorded during the first pass.
-//  * Stage 2 runs the same tile code over all T centroids in chunks of 32
+//  * Stage 2 streams all T centroids in chunks of 32 through the same code
 //    (kbar as keys, vsum as values, converted to bf16 while staging), with the
 //    blocks of S_i and j >= T masked; the weights add n_j p to D and p to c.
 //  * Stage 3 forms r^T = Hbar^T q^T on MFMA (Hbar transposed into LDS in
@@ -48,20 +50,17 @@ constexpr float kOverflowSlack = 64.f;    // log2 units above the reference max 
 template <int D>
 struct Geo {
   static constexpr int CG = D / 8;                         // 16-byte chunks in a K row
-  static constexpr int TILE = 64 * D;                      // bf16 elements of a K or V tile
+  static constexpr int KS = D + 8;                         // K tile row stride (elements)
+  static constexpr int VS = 64 + 8;                        // V^T tile row stride
+  static constexpr int HS = D + 8;                         // Hbar^T row stride
+  static constexpr int KTILE = 64 * KS;
+  static constexpr int VTILE = D * VS;
+  static constexpr int BUF = KTILE + VTILE;                // one staging buffer (elements)
   static constexpr int NK = D / 16;                        // k-steps of S^T = K Q^T
   static constexpr int NU = D / 32;                        // 32-dim output tiles
   static constexpr int KPT = 64 * CG / kAttnThreads;       // K chunks staged per thread
+  static_assert(D * HS <= 2 * BUF, "Hbar^T must fit in the staging buffers");
 };
-
-// K tile: row-major [64 keys][D], chunk c of row r stored at c ^ kswz(r).
-template <int D>
-__device__ __forceinline__ int k_off(int row, int c) {
-  const int f = (((row & 7) << 1) | ((row >> 3) & 1)) & (Geo<D>::CG - 1);
-  return row * D + 8 * (c ^ f);
-}
-// Transposed tile with rows of `rlen` elements: chunk c of row r at c ^ (r & 7).
-__device__ __forceinline__ int t_off(int row, int c, int rlen) { return row * rlen + 8 * (c ^ (row & 7)); }
 
 // Key (tile row) that MFMA row m of S^T sub-tile t reads, chosen so that
 // accumulator register i of a lane in half g holds key 32 t + 16 (i/8) + 8 g + i%8.
@@ -69,7 +68,6 @@ __device__ __forceinline__ int perm_key(int t, int m) {
   const int a = m >> 3, g = (m >> 2) & 1, b = m & 3;
   return 32 * t + 16 * (a >> 1) + 8 * g + 4 * (a & 1) + b;
 }
-__device__ __forceinline__ int reg_key(int t, int i, int g) { return 32 * t + 16 * (i >> 3) + 8 * g + (i & 7); }
 
 __device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
   const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
@@ -78,12 +76,17 @@ __device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
 __device__ __forceinline__ uint4 to_bf16x8(const float4& a, const float4& b) {
   return make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
 }
+__device__ __forceinline__ float4 as_f4(const uint4& u) { return __builtin_bit_cast(float4, u); }
 
 // ------------------------------------------------------------ staging
-// One step's data in flight, KPT + 4 registers of 16 bytes per thread:
-//  exact tile (bf16): r[0..KPT) = K chunks (row-major), r[KPT..KPT+4) = 4 keys x 8 dims of V;
-//  centroid chunk (fp32, 32 centroids): r[0..KPT) = kbar chunks as float4 pairs,
-//  r[KPT..KPT+4) = 2 centroids x 8 dims of vsum.
+// One step's data in flight, KPT + 4 registers of 16 bytes per thread. Rows
+// past the valid range re-read the last valid row (finite values whose keys
+// are masked out), so the loads need no predication.
+//  exact tile (bf16): r[0..KPT) = K chunks, r[KPT..KPT+4) = 4 keys x 8 dims of V;
+//  centroid chunk (fp32, 32 centroids): r[0..KPT) = kbar chunks as float4
+//  pairs, r[KPT..KPT+4) = 2 centroids x 8 dims of vsum.
+// V items put consecutive lanes on consecutive key groups, so each LDS write
+// instruction fills whole V^T rows.
 template <int D>
 struct Stage {
   uint4 r[Geo<D>::KPT + 4];
@@ -96,36 +99,34 @@ __device__ __forceinline__ void load_exact(const uint16_t* __restrict__ Kh, cons
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int q = threadIdx.x + kAttnThreads * i;
-    const int row = q / CG, c = q % CG;
-    st.r[i] = row < nvalid ? *reinterpret_cast<const uint4*>(Kh + static_cast<size_t>(row0 + row) * D + 8 * c)
-                           : make_uint4(0, 0, 0, 0);
+    const int row = min(q / CG, nvalid - 1), c = q % CG;
+    st.r[i] = *reinterpret_cast<const uint4*>(Kh + static_cast<size_t>(row0 + row) * D + 8 * c);
   }
-  const int item = threadIdx.x;  // 16 key groups x CG dim groups
-  const int kg = item / CG, dg = item % CG;
+  const int item = threadIdx.x;  // 16 key groups (fast) x CG dim groups
+  const int kg = item & 15, dg = min(item >> 4, CG - 1);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int row = 4 * kg + e;
-    st.r[KPT + e] = (item < 16 * CG && row < nvalid)
-                        ? *reinterpret_cast<const uint4*>(Vh + static_cast<size_t>(row0 + row) * D + 8 * dg)
-                        : make_uint4(0, 0, 0, 0);
+    const int row = min(4 * kg + e, nvalid - 1);
+    st.r[KPT + e] = *reinterpret_cast<const uint4*>(Vh + static_cast<size_t>(row0 + row) * D + 8 * dg);
   }
 }
 template <int D>
-__device__ __forceinline__ void store_exact(const Stage<D>& st, uint16_t* kt, uint16_t* vt) {
-  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT;
+__device__ __forceinline__ void store_exact(const Stage<D>& st, uint16_t* buf) {
+  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT, KS = Geo<D>::KS, VS = Geo<D>::VS;
+  uint16_t* vt = buf + Geo<D>::KTILE;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int q = threadIdx.x + kAttnThreads * i;
-    *reinterpret_cast<uint4*>(kt + k_off<D>(q / CG, q % CG)) = st.r[i];
+    *reinterpret_cast<uint4*>(buf + (q / CG) * KS + 8 * (q % CG)) = st.r[i];
   }
   const int item = threadIdx.x;
-  if (item < 16 * CG) {
-    const int kg = item / CG, dg = item % CG;
+  const int kg = item & 15, dg = item >> 4;
+  if (dg < CG) {  // threads past 16 CG items (d = 64) only loaded duplicates
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t w0 = half16(st.r[KPT], e) | (half16(st.r[KPT + 1], e) << 16);
       const uint32_t w1 = half16(st.r[KPT + 2], e) | (half16(st.r[KPT + 3], e) << 16);
-      *reinterpret_cast<uint2*>(vt + t_off(8 * dg + e, kg >> 1, 64) + 4 * (kg & 1)) = make_uint2(w0, w1);
+      *reinterpret_cast<uint2*>(vt + (8 * dg + e) * VS + 4 * kg) = make_uint2(w0, w1);
     }
   }
 }
@@ -135,45 +136,43 @@ template <int D>
 __device__ __forceinline__ void load_centroids(const float* __restrict__ kb, const float* __restrict__ vs, int j0,
                                                int T, Stage<D>& st) {
   constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT;
-  const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int i = 0; i < KPT / 2; ++i) {
     const int q = threadIdx.x + kAttnThreads * i;
-    const int row = q / CG, c = q % CG;
-    const bool ok = j0 + row < T;
-    const uint4* src = reinterpret_cast<const uint4*>(kb + static_cast<size_t>(j0 + row) * D + 8 * c);
-    st.r[2 * i] = ok ? src[0] : z;
-    st.r[2 * i + 1] = ok ? src[1] : z;
+    const int row = min(j0 + q / CG, T - 1), c = q % CG;
+    const uint4* src = reinterpret_cast<const uint4*>(kb + static_cast<size_t>(row) * D + 8 * c);
+    st.r[2 * i] = src[0];
+    st.r[2 * i + 1] = src[1];
   }
-  const int item = threadIdx.x;  // 16 centroid pairs x CG dim groups
-  const int kp = item / CG, dg = item % CG;
+  const int item = threadIdx.x;  // 16 centroid pairs (fast) x CG dim groups
+  const int kp = item & 15, dg = min(item >> 4, CG - 1);
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const int row = 2 * kp + e;
-    const bool ok = item < 16 * CG && j0 + row < T;
-    const uint4* src = reinterpret_cast<const uint4*>(vs + static_cast<size_t>(j0 + row) * D + 8 * dg);
-    st.r[KPT + 2 * e] = ok ? src[0] : z;
-    st.r[KPT + 2 * e + 1] = ok ? src[1] : z;
+    const int row = min(j0 + 2 * kp + e, T - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(vs + static_cast<size_t>(row) * D + 8 * dg);
+    st.r[KPT + 2 * e] = src[0];
+    st.r[KPT + 2 * e + 1] = src[1];
   }
 }
-__device__ __forceinline__ float4 as_f4(const uint4& u) { return __builtin_bit_cast(float4, u); }
 template <int D>
-__device__ __forceinline__ void store_centroids(const Stage<D>& st, uint16_t* kt, uint16_t* vt) {
-  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT;
+__device__ __forceinline__ void store_centroids(const Stage<D>& st, uint16_t* buf) {
+  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT, KS = Geo<D>::KS, VS = Geo<D>::VS;
+  uint16_t* vt = buf + Geo<D>::KTILE;
 #pragma unroll
   for (int i = 0; i < KPT / 2; ++i) {
     const int q = threadIdx.x + kAttnThreads * i;
-    *reinterpret_cast<uint4*>(kt + k_off<D>(q / CG, q % CG)) = to_bf16x8(as_f4(st.r[2 * i]), as_f4(st.r[2 * i + 1]));
+    *reinterpret_cast<uint4*>(buf + (q / CG) * KS + 8 * (q % CG)) =
+        to_bf16x8(as_f4(st.r[2 * i]), as_f4(st.r[2 * i + 1]));
   }
   const int item = threadIdx.x;
-  if (item < 16 * CG) {
-    const int kp = item / CG, dg = item % CG;
+  const int kp = item & 15, dg = item >> 4;
+  if (dg < CG) {
     const float4 x0 = as_f4(st.r[KPT]), y0 = as_f4(st.r[KPT + 1]), x1 = as_f4(st.r[KPT + 2]), y1 = as_f4(st.r[KPT + 3]);
     const float a0[8] = {x0.x, x0.y, x0.z, x0.w, y0.x, y0.y, y0.z, y0.w};
     const float a1[8] = {x1.x, x1.y, x1.z, x1.w, y1.x, y1.y, y1.z, y1.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<uint32_t*>(vt + t_off(8 * dg + e, kp >> 2, 64) + 2 * (kp & 3)) = pack_bf16x2(a0[e], a1[e]);
+      *reinterpret_cast<uint32_t*>(vt + (8 * dg + e) * VS + 2 * kp) = pack_bf16x2(a0[e], a1[e]);
   }
 }
 
@@ -189,44 +188,50 @@ struct Acc {
   bool over;                  // some logit exceeded m + kOverflowSlack
 };
 
+// S^T of 32 keys (K rows read from kt + kbase: the lane's permuted row, its 8-dim half).
 template <int D>
-__device__ __forceinline__ void qk_half(const uint16_t* kt, const Acc<D>& a, int t, f32x16 (&s)[2]) {
-  const int l = threadIdx.x & 63, g = l >> 5, ql = l & 31;
+__device__ __forceinline__ void qk_half(const uint16_t* kt, const Acc<D>& a, f32x16 (&s)[2]) {
   s[0] = f32x16{};
   s[1] = f32x16{};
-  const int row = perm_key(t, ql);
 #pragma unroll
   for (int ks = 0; ks < Geo<D>::NK; ++ks) {
-    const bf16x8 av = *reinterpret_cast<const bf16x8*>(kt + k_off<D>(row, g + 2 * ks));
+    const bf16x8 av = *reinterpret_cast<const bf16x8*>(kt + 16 * ks);
     s[0] = mfma32x32x16(av, a.qb[0][ks], s[0]);
     s[1] = mfma32x32x16(av, a.qb[1][ks], s[1]);
   }
 }
 
+// O^T += V^T P^T for 32 keys (vt: the lane's V^T row base plus the key offset).
 template <int D>
-__device__ __forceinline__ void pv_half(const uint16_t* vt, int t, const bf16x8 (&pb)[2][2], Acc<D>& a) {
-  const int l = threadIdx.x & 63, g = l >> 5, ql = l & 31;
+__device__ __forceinline__ void pv_half(const uint16_t* vt, const bf16x8 (&pb)[2][2], Acc<D>& a) {
 #pragma unroll
   for (int u = 0; u < Geo<D>::NU; ++u)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt + t_off(32 * u + ql, 4 * t + 2 * s + g, 64));
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt + 32 * u * Geo<D>::VS + 16 * s);
       a.o[u][0] = mfma32x32x16(av, pb[0][s], a.o[u][0]);
       a.o[u][1] = mfma32x32x16(av, pb[1][s], a.o[u][1]);
     }
 }
 
+// The lane's 16 keys of 32-key sub-tile t as a 16-bit mask of a 64-bit key mask.
+__device__ __forceinline__ uint32_t lane_bits(uint64_t km, int t, int g) {
+  return static_cast<uint32_t>((km >> (32 * t + 8 * g)) & 0xFFu) |
+         (static_cast<uint32_t>((km >> (32 * t + 16 + 8 * g)) & 0xFFu) << 8);
+}
+
 // Softmax weights of one 32-key sub-tile against the fixed reference max.
+// kMask: keys with a set bit in lmask get weight 0. kTail: D gains n_j p
+// (n_j = 64 except nlast for the key flagged in llast) and c gains p.
 template <int D, bool kMask, bool kTail>
-__device__ __forceinline__ void softmax_half(f32x16 (&s)[2], Acc<D>& a, int t, float cl2, uint64_t keymask,
-                                             int nlast_key, float nlast, bf16x8 (&pb)[2][2]) {
-  const int g = (threadIdx.x & 63) >> 5;
+__device__ __forceinline__ void softmax_half(f32x16 (&s)[2], Acc<D>& a, float cl2, uint32_t lmask, uint32_t llast,
+                                             float nlast, bf16x8 (&pb)[2][2]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     float v = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (kMask && ((keymask >> reg_key(t, i, g)) & 1ull)) s[h][i] = -INFINITY;
+      if (kMask && ((lmask >> i) & 1u)) s[h][i] = -INFINITY;
       v = fmaxf(v, s[h][i]);
     }
     v = fmaxf(v, __shfl_xor(v, 32)) * cl2;
@@ -234,16 +239,26 @@ __device__ __forceinline__ void softmax_half(f32x16 (&s)[2], Acc<D>& a, int t, f
     if (a.m[h] == -INFINITY) a.m[h] = v;
     a.over = a.over || v > a.m[h] + kOverflowSlack;
     const float mref = a.m[h] == -INFINITY ? 0.f : a.m[h];
-    float ps = 0.f, pw = 0.f;
+    float ps = 0.f, pl = 0.f;
+    float pv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][i], cl2, -mref));
+      pv[i] = p;
       ps += p;
-      if (kTail) pw += reg_key(t, i, g) == nlast_key ? p * nlast : p * 64.f;
-      pb[h][i >> 3][i & 7] = static_cast<__bf16>(p);
+      if (kTail) pl += ((llast >> i) & 1u) ? p : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint4 w;
+      w.x = pack_bf16x2(pv[8 * c + 0], pv[8 * c + 1]);
+      w.y = pack_bf16x2(pv[8 * c + 2], pv[8 * c + 3]);
+      w.z = pack_bf16x2(pv[8 * c + 4], pv[8 * c + 5]);
+      w.w = pack_bf16x2(pv[8 * c + 6], pv[8 * c + 7]);
+      pb[h][c] = __builtin_bit_cast(bf16x8, w);
     }
     if (kTail) {
-      a.dsum[h] += pw;
+      a.dsum[h] += 64.f * ps + (nlast - 64.f) * pl;
       a.csum[h] += ps;
     } else {
       a.dsum[h] += ps;
@@ -256,13 +271,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const float* __restrict__ kbar, const float* __restrict__ vsum, const float* __restrict__ Hbar,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ O, int L, int T, int keep_k, float scale, int nwg) {
-  constexpr int TILE = Geo<D>::TILE;
+  constexpr int BUF = Geo<D>::BUF, KS = Geo<D>::KS, VS = Geo<D>::VS, HS = Geo<D>::HS;
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* buf = reinterpret_cast<uint16_t*>(smem);  // 2 x (K tile, V^T tile)
+  uint16_t* buf = reinterpret_cast<uint16_t*>(smem);  // 2 staging buffers
   const int nw = ceil_div(T, 32);
-  uint32_t* masks = reinterpret_cast<uint32_t*>(smem + sizeof(uint16_t) * 4 * TILE);  // [kWaves][nw]
-  int* sh = reinterpret_cast<int*>(masks + kWaves * nw);                             // nu, rerun flags
-  uint16_t* ulist = reinterpret_cast<uint16_t*>(sh + 8);                             // [T]
+  uint32_t* masks = reinterpret_cast<uint32_t*>(smem + sizeof(uint16_t) * 2 * BUF);  // [kWaves][nw]
+  int* sh = reinterpret_cast<int*>(masks + kWaves * nw);                            // nu, rerun flags
+  uint16_t* ulist = reinterpret_cast<uint16_t*>(sh + 8);                            // [T]
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so hand
   // each XCD a contiguous run of (head, query-block group) items.
@@ -280,6 +295,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   const uint16_t* Vh = V + head;
   const float cl2 = scale * kLog2e;
   const int nlast = L - 64 * (T - 1);
+  // per-lane operand offsets inside a staging buffer
+  const int koff = perm_key(0, ql) * KS + 8 * g;              // K rows of sub-tile 0 (+32 KS for 1)
+  const int voff = Geo<D>::KTILE + ql * VS + 8 * g;           // V^T rows 32 u + ql (+16 s + 32 t keys)
 
   Acc<D> a;
 #pragma unroll
@@ -346,8 +364,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     a.over = false;
 
     // ---- stages 1 and 2 as one stream of steps: the nu exact tiles of the
-    // union, then the nch chunks of 32 centroids. A single qk / pv code path
-    // serves both, so the O^T accumulators keep one register assignment.
+    // union, then the nch chunks of 32 centroids.
     const int nsteps = nu + nch;
     Stage<D> st;
     auto fetch = [&](int step) {
@@ -358,11 +375,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
         load_centroids<D>(kb, vs, 32 * (step - nu), T, st);
       }
     };
-    auto put = [&](int step, uint16_t* kt) {
+    auto put = [&](int step, uint16_t* b) {
       if (step < nu)
-        store_exact<D>(st, kt, kt + TILE);
+        store_exact<D>(st, b);
       else
-        store_centroids<D>(st, kt, kt + TILE);
+        store_centroids<D>(st, b);
     };
     if (nsteps > 0) {
       fetch(0);
@@ -370,42 +387,62 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     }
     __syncthreads();
     if (nsteps > 1) fetch(1);
-    for (int step = 0; step < nsteps; ++step) {
-      const uint16_t* kc = buf + (step & 1) * 2 * TILE;
-      const bool tail = step >= nu;
-      const int j = tail ? 0 : ulist[step];
-      bool work = active;
-      uint64_t km = 0;
-      int nsub = 2;
-      int nlast_key = -1;
-      if (!tail) {
-        work = work && ((mymask[j >> 5] >> (j & 31)) & 1u);
-        if (j == T - 1 && nlast < 64) km = ~0ull << nlast;
-      } else {
-        const int j0 = 32 * (step - nu);
-        km = 0xFFFFFFFF00000000ull | ((j0 >> 5) < nw ? mymask[j0 >> 5] : 0xFFFFFFFFu);
-        if (j0 + 32 > T) km |= ~0ull << (T - j0);
-        nsub = 1;
-        nlast_key = T - 1 - j0;
-      }
-      if (work) {
-#pragma unroll 1
-        for (int t = 0; t < nsub; ++t) {
-          f32x16 sacc[2];
-          bf16x8 pb[2][2];
-          qk_half<D>(kc, a, t, sacc);
-          if (tail)
-            softmax_half<D, true, true>(sacc, a, t, cl2, km, nlast_key, static_cast<float>(nlast), pb);
-          else if (km)
-            softmax_half<D, true, false>(sacc, a, t, cl2, km, -1, 0.f, pb);
-          else
-            softmax_half<D, false, false>(sacc, a, t, cl2, 0ull, -1, 0.f, pb);
-          pv_half<D>(kc + TILE, t, pb, a);
-        }
-      }
-      if (step + 1 < nsteps) put(step + 1, buf + ((step + 1) & 1) * 2 * TILE);
+    // Three loops over consecutive step ranges, one compute variant each, so
+    // the O^T accumulators keep one register assignment inside every loop:
+    // full exact tiles, then the partial last block (always last in the
+    // ascending union), then the centroid chunks.
+    const int nfull = (nu > 0 && ulist[nu - 1] == T - 1 && nlast < 64) ? nu - 1 : nu;
+    auto advance = [&](int step) {
+      if (step + 1 < nsteps) put(step + 1, buf + ((step + 1) & 1) * BUF);
       if (step + 2 < nsteps) fetch(step + 2);
       __syncthreads();
+    };
+    for (int step = 0; step < nfull; ++step) {
+      const uint16_t* bc = buf + (step & 1) * BUF;
+      const int j = ulist[step];
+      if (active && ((mymask[j >> 5] >> (j & 31)) & 1u)) {
+        f32x16 s0[2], s1[2];
+        bf16x8 p0[2][2], p1[2][2];
+        qk_half<D>(bc + koff, a, s0);
+        qk_half<D>(bc + koff + 32 * KS, a, s1);
+        softmax_half<D, false, false>(s0, a, cl2, 0u, 0u, 0.f, p0);
+        pv_half<D>(bc + voff, p0, a);
+        softmax_half<D, false, false>(s1, a, cl2, 0u, 0u, 0.f, p1);
+        pv_half<D>(bc + voff + 32, p1, a);
+      }
+      advance(step);
+    }
+    for (int step = nfull; step < nu; ++step) {
+      const uint16_t* bc = buf + (step & 1) * BUF;
+      const int j = ulist[step];
+      if (active && ((mymask[j >> 5] >> (j & 31)) & 1u)) {
+        const uint64_t km = ~0ull << nlast;
+        f32x16 s0[2], s1[2];
+        bf16x8 p0[2][2], p1[2][2];
+        qk_half<D>(bc + koff, a, s0);
+        qk_half<D>(bc + koff + 32 * KS, a, s1);
+        softmax_half<D, true, false>(s0, a, cl2, lane_bits(km, 0, g), 0u, 0.f, p0);
+        pv_half<D>(bc + voff, p0, a);
+        softmax_half<D, true, false>(s1, a, cl2, lane_bits(km, 1, g), 0u, 0.f, p1);
+        pv_half<D>(bc + voff + 32, p1, a);
+      }
+      advance(step);
+    }
+    for (int step = nu; step < nsteps; ++step) {
+      const uint16_t* bc = buf + (step & 1) * BUF;
+      if (active) {
+        const int j0 = 32 * (step - nu);
+        uint64_t km = 0xFFFFFFFF00000000ull | ((j0 >> 5) < nw ? mymask[j0 >> 5] : 0xFFFFFFFFu);
+        if (j0 + 32 > T) km |= ~0ull << (T - j0);
+        const int lk = T - 1 - j0;  // chunk-local index of the last (partial) block, if present
+        const uint64_t kl = (lk >= 0 && lk < 32) ? (1ull << lk) : 0ull;
+        f32x16 s0[2];
+        bf16x8 p0[2][2];
+        qk_half<D>(bc + koff, a, s0);
+        softmax_half<D, true, true>(s0, a, cl2, lane_bits(km, 0, g), lane_bits(kl, 0, g), static_cast<float>(nlast), p0);
+        pv_half<D>(bc + voff, p0, a);
+      }
+      advance(step);
     }
 
     // ---- rerun the blocks whose logits outgrew their reference max
@@ -430,10 +467,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     dsum[h] = a.dsum[h] + __shfl_xor(a.dsum[h], 32);
   }
   if (nch > 0) {
-    // Hbar^T in bf16: ht[v][k] = Hbar[k][v], rows of D elements
+    // Hbar^T in bf16: ht[v][k] = Hbar[k][v], rows padded to HS
     const float* Hh = Hbar + static_cast<size_t>(bh) * D * D;
     for (int item = tid; item < (D / 4) * Geo<D>::CG; item += kAttnThreads) {
-      const int kg = item / Geo<D>::CG, vg = item % Geo<D>::CG;
+      const int kg = item % (D / 4), vg = item / (D / 4);
       float f[4][8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -444,12 +481,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint2*>(buf + t_off(8 * vg + e, kg >> 1, D) + 4 * (kg & 1)) =
+        *reinterpret_cast<uint2*>(buf + (8 * vg + e) * HS + 4 * kg) =
             make_uint2(pack_bf16x2(f[0][e], f[1][e]), pack_bf16x2(f[2][e], f[3][e]));
     }
     __syncthreads();
   }
   if (qvalid) {
+    const uint16_t* hrow = buf + ql * HS + 8 * g;
 #pragma unroll
     for (int u = 0; u < Geo<D>::NU; ++u) {
       f32x16 o0 = a.o[u][0], o1 = a.o[u][1];
@@ -457,7 +495,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
         f32x16 r0 = f32x16{}, r1 = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < Geo<D>::NK; ++ks) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(buf + t_off(32 * u + ql, 2 * ks + g, D));
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(hrow + 32 * u * HS + 16 * ks);
           r0 = mfma32x32x16(av, a.qb[0][ks], r0);
           r1 = mfma32x32x16(av, a.qb[1][ks], r1);
         }
@@ -578,7 +616,7 @@ hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, cons
                        hipStream_t s) {
   const int T = ceil_div(p.L, 64);
   const int nw = ceil_div(T, 32);
-  const size_t lds = sizeof(uint16_t) * 4 * Geo<D>::TILE + sizeof(uint32_t) * kWaves * nw + 8 * sizeof(int) +
+  const size_t lds = sizeof(uint16_t) * 2 * Geo<D>::BUF + sizeof(uint32_t) * kWaves * nw + 8 * sizeof(int) +
                      sizeof(uint16_t) * T;
   const size_t lds_al = (lds + 15) / 16 * 16;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_bf16<D>),

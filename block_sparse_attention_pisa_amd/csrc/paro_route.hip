@@ -13,6 +13,8 @@
 //      LDS histogram), then writes the winners in ascending j with a
 //      ballot / mbcnt compaction. Exact ties go to the lower j, so the result
 //      is a deterministic integer function of the scores.
+#include <algorithm>
+
 #include "paro_common.h"
 
 namespace paro {
@@ -31,6 +33,11 @@ __device__ __forceinline__ uint64_t score_key(double s) {
 }
 
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
 
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void k_route(const E* __restrict__ Q, const float* __restrict__ kbar,
@@ -39,9 +46,9 @@ __global__ __launch_bounds__(kThreads) void k_route(const E* __restrict__ Q, con
                                                     double lambda) {
   extern __shared__ __align__(16) unsigned char smem[];
   double* qbar = reinterpret_cast<double*>(smem);                      // [D][R]
-  double* score = qbar + D * kMaxRows;                                  // [R][T]
-  uint32_t* hist = reinterpret_cast<uint32_t*>(score + static_cast<size_t>(R) * T);  // [4][256]
-  double* qred = reinterpret_cast<double*>(hist + 4 * 256);             // [4][D] partials
+  uint32_t* hist = reinterpret_cast<uint32_t*>(qbar + D * kMaxRows);    // [4][256]
+  double* score = reinterpret_cast<double*>(hist + 4 * 256);            // [R][T]
+  double* qred = score;  // qbar partials [2 * rows per sweep][D], used before any score exists
 
   const int bh = blockIdx.y;
   const int i0 = blockIdx.x * R;
@@ -51,44 +58,101 @@ __global__ __launch_bounds__(kThreads) void k_route(const E* __restrict__ Q, con
   const float* kb = kbar + static_cast<size_t>(bh) * T * D;
   const double* Mh = M + static_cast<size_t>(bh) * T;
 
-  // 1. qbar (fp64 sums of the valid rows)
-  constexpr int P = kThreads / D;
-  constexpr int TP = kBlock / P;
-  const int a = t % D, part = t / D;
-  for (int r = 0; r < nrows; ++r) {
-    const int row0 = (i0 + r) * kBlock, nvalid = min(kBlock, L - row0);
-    double sum = 0.0;
-    for (int q = part * TP; q < min(nvalid, part * TP + TP); ++q)
-      sum += load_elem<E>(Qh + static_cast<size_t>(row0 + q) * D + a);
-    qred[part * D + a] = sum;
+  // 1. qbar (fp64 sums of the valid rows). Thread t reads 16-byte pieces of
+  //    rows t / G, t / G + 256 / G, ... at dim group t % G (G pieces per row);
+  //    the loads of two query blocks are in flight together.
+  constexpr int EPL = 16 / sizeof(E);  // elements per 16-byte piece
+  constexpr int G = D / EPL;           // pieces per row
+  constexpr int RS = kThreads / G;     // rows covered per sweep
+  constexpr int SW = kBlock / RS;      // sweeps per block
+  const int dg = t % G, ro = t / G;
+  for (int r0 = 0; r0 < nrows; r0 += 2) {
+    uint4 raw[2][SW];
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = r0 + rr;
+      const int row0 = (i0 + r) * kBlock, nvalid = r < nrows ? min(kBlock, L - row0) : 0;
+#pragma unroll
+      for (int sw = 0; sw < SW; ++sw) {
+        const int tok = ro + RS * sw;
+        raw[rr][sw] = tok < nvalid
+                          ? *reinterpret_cast<const uint4*>(Qh + static_cast<size_t>(row0 + tok) * D + EPL * dg)
+                          : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      double acc[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = 0.0;
+#pragma unroll
+      for (int sw = 0; sw < SW; ++sw) {
+        const E* x = reinterpret_cast<const E*>(&raw[rr][sw]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += load_elem<E>(x + e);
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qred[(rr * RS + ro) * D + EPL * dg + e] = acc[e];
+    }
     __syncthreads();
-    if (t < D) {
-      double s = 0.0;
-      for (int p = 0; p < P; ++p) s += qred[p * D + a];
-      qbar[a * kMaxRows + r] = s / nvalid;
+    for (int e = t; e < 2 * D; e += kThreads) {
+      const int rr = e / D, a = e % D, r = r0 + rr;
+      if (r < nrows) {
+        const int row0 = (i0 + r) * kBlock, nvalid = min(kBlock, L - row0);
+        double sum = 0.0;
+        for (int p = 0; p < RS; ++p) sum += qred[(rr * RS + p) * D + a];
+        qbar[a * kMaxRows + r] = sum / nvalid;
+      }
     }
     __syncthreads();
   }
 
-  // 2. scores
-  for (int j = t; j < T; j += kThreads) {
-    double acc[kMaxRows];
+  // 2. scores: each thread handles centroids j and j + 256 together, with
+  //    8 loads of 16 bytes per centroid in flight; qbar is read as LDS broadcasts.
+  for (int ja = t; ja < T; ja += 2 * kThreads) {
+    const int jb = ja + kThreads;
+    const bool okb = jb < T;
+    double acc_a[kMaxRows], acc_b[kMaxRows];
 #pragma unroll
-    for (int r = 0; r < kMaxRows; ++r) acc[r] = 0.0;
-    const float4* krow = reinterpret_cast<const float4*>(kb + static_cast<size_t>(j) * D);
-    for (int a4 = 0; a4 < D / 4; ++a4) {
-      const float4 kv = krow[a4];
-      const float ke[4] = {kv.x, kv.y, kv.z, kv.w};
+    for (int r = 0; r < kMaxRows; ++r) {
+      acc_a[r] = 0.0;
+      acc_b[r] = 0.0;
+    }
+    const float4* rowa = reinterpret_cast<const float4*>(kb + static_cast<size_t>(ja) * D);
+    const float4* rowb = reinterpret_cast<const float4*>(kb + static_cast<size_t>(okb ? jb : ja) * D);
+#pragma unroll 1
+    for (int a0 = 0; a0 < D / 4; a0 += 8) {
+      float4 ka[8], kc[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const double kd = ke[e];
-        const double* qa = qbar + (4 * a4 + e) * kMaxRows;
+      for (int u = 0; u < 8; ++u) {
+        ka[u] = rowa[a0 + u];
+        kc[u] = rowb[a0 + u];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the 16 loads in flight together
 #pragma unroll
-        for (int r = 0; r < kMaxRows; ++r) acc[r] += qa[r] * kd;
+      for (int u = 0; u < 8; ++u) {
+        const float xa[4] = {ka[u].x, ka[u].y, ka[u].z, ka[u].w};
+        const float xb[4] = {kc[u].x, kc[u].y, kc[u].z, kc[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double* qa = qbar + (4 * (a0 + u) + e) * kMaxRows;
+#pragma unroll
+          for (int r = 0; r < kMaxRows; ++r) {
+            acc_a[r] += qa[r] * static_cast<double>(xa[e]);
+            acc_b[r] += qa[r] * static_cast<double>(xb[e]);
+          }
+        }
       }
     }
-    const double lm = lambda * Mh[j];
-    for (int r = 0; r < nrows; ++r) score[static_cast<size_t>(r) * T + j] = scale * acc[r] + lm;
+    const double lma = lambda * Mh[ja];
+    const double lmb = okb ? lambda * Mh[jb] : 0.0;
+#pragma unroll
+    for (int r = 0; r < kMaxRows; ++r) {
+      if (r < nrows) {
+        score[static_cast<size_t>(r) * T + ja] = scale * acc_a[r] + lma;
+        if (okb) score[static_cast<size_t>(r) * T + jb] = scale * acc_b[r] + lmb;
+      }
+    }
   }
   __syncthreads();
 
@@ -97,20 +161,34 @@ __global__ __launch_bounds__(kThreads) void k_route(const E* __restrict__ Q, con
   for (int r = w; r < nrows; r += 4) {
     const double* sc = score + static_cast<size_t>(r) * T;
     int32_t* out = idx + (static_cast<size_t>(bh) * T + i0 + r) * keep_k;
-    uint64_t prefix = 0, mask = 0;
-    int remaining = keep_k;  // how many of the keys matching prefix are still needed
+    // Radix select over the digits below the common prefix of the row's keys:
+    // keys are order-preserving images of the scores, so the first digits of
+    // a row usually agree and would all hit one histogram bin.
+    uint64_t kmin = ~0ull, kmax = 0ull;
+    for (int j = l; j < T; j += 64) {
+      const uint64_t key = score_key(sc[j]);
+      kmin = key < kmin ? key : kmin;
+      kmax = key > kmax ? key : kmax;
+    }
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint64_t a0 = shfl_xor_u64(kmin, o), a1 = shfl_xor_u64(kmax, o);
+      kmin = a0 < kmin ? a0 : kmin;
+      kmax = a1 > kmax ? a1 : kmax;
+    }
+    int top = kmin == kmax ? -8 : (63 - __builtin_clzll(kmin ^ kmax)) / 8 * 8;  // digit holding the top differing bit
+    uint64_t mask = top + 8 >= 64 ? 0ull : ~((1ull << (top + 8)) - 1);
+    uint64_t prefix = kmax & mask;
+    int remaining = keep_k;  // how many keys equal to prefix (on the mask bits) are still needed
     if (keep_k < T) {
-      for (int shift = 56; shift >= 0; shift -= 8) {
+      for (int shift = top; shift >= 0; shift -= 8) {
         for (int b = l; b < 256; b += 64) h[b] = 0;
-        __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_wave_barrier();
         for (int j = l; j < T; j += 64) {
           const uint64_t key = score_key(sc[j]);
           if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
         }
-        __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_wave_barrier();
-        // lane l owns digits 4l..4l+3; count of all digits above this lane's
+        // lane l owns digits 4l..4l+3
         uint32_t c[4];
         for (int e = 0; e < 4; ++e) c[e] = h[4 * l + e];
         const uint32_t mine = c[0] + c[1] + c[2] + c[3];
@@ -122,12 +200,13 @@ __global__ __launch_bounds__(kThreads) void k_route(const E* __restrict__ Q, con
         }
         const uint32_t above = incl - mine;
         int found = -1;
-        uint32_t cum = above;
+        uint32_t cum = above, binc = 0;
         int newrem = 0;
         for (int e = 3; e >= 0; --e) {
           if (found < 0 && cum < static_cast<uint32_t>(remaining) && cum + c[e] >= static_cast<uint32_t>(remaining)) {
             found = 4 * l + e;
             newrem = remaining - static_cast<int>(cum);
+            binc = c[e];
           }
           cum += c[e];
         }
@@ -135,12 +214,14 @@ __global__ __launch_bounds__(kThreads) void k_route(const E* __restrict__ Q, con
         const int src = __builtin_ctzll(bal);
         const int digit = __shfl(found, src);
         remaining = __shfl(newrem, src);
+        const int bin_count = __shfl(static_cast<int>(binc), src);
         prefix |= static_cast<uint64_t>(digit) << shift;
         mask |= 255ull << shift;
+        if (remaining == bin_count) break;  // the whole bin is taken: no finer digit needed
       }
     }
-    // prefix is now the keep_k-th largest key; take every key above it and
-    // the first `remaining` keys equal to it, in ascending j.
+    // Take every key whose masked bits exceed prefix, and the first
+    // `remaining` (in ascending j) whose masked bits equal it.
     int written = 0, eq_seen = 0;
     for (int base = 0; base < T; base += 64) {
       const int j = base + l;
@@ -149,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void k_route(const E* __restrict__ Q, con
         if (keep_k >= T) {
           gt = true;
         } else {
-          const uint64_t key = score_key(sc[j]);
+          const uint64_t key = score_key(sc[j]) & mask;
           gt = key > prefix;
           eq = key == prefix;
         }
@@ -169,8 +250,8 @@ __global__ __launch_bounds__(kThreads) void k_route(const E* __restrict__ Q, con
 }
 
 size_t route_lds_bytes(int T, int d, int R) {
-  return sizeof(double) * (static_cast<size_t>(d) * kMaxRows + static_cast<size_t>(R) * T) +
-         4 * 256 * sizeof(uint32_t) + sizeof(double) * 4 * d;
+  const size_t scores = static_cast<size_t>(R) * T, partials = 2 * (kThreads / (d * 2 / 16)) * static_cast<size_t>(d);
+  return sizeof(double) * (static_cast<size_t>(d) * kMaxRows + std::max(scores, partials)) + 4 * 256 * sizeof(uint32_t);
 }
 
 template <typename E, int D>

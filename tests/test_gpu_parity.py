@@ -123,3 +123,22 @@ def test_deterministic_bitwise():
         outs.append([x.cpu() for x in (*stats, idx, o)])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("keep", [1, 5, 11])
+def test_route_exact_ties_and_equal_scores(keep):
+    """Duplicated kv blocks tie exactly (lower block index wins); constant keys
+    and values make every score equal (the first keep blocks win)."""
+    d, nb = 128, 13
+    g = np.random.default_rng(keep)
+    base = torch.from_numpy(g.standard_normal((4, 64, d)).astype(np.float32))
+    order = [0, 1, 0, 2, 3, 1, 2, 0, 3, 3, 1, 2, 0]
+    k = torch.cat([base[i] for i in order])[None, None].to(torch.bfloat16)
+    v = torch.cat([base[(i + 1) % 4] for i in order])[None, None].to(torch.bfloat16)
+    q = torch.from_numpy(g.standard_normal((1, 1, 64 * nb, d)).astype(np.float32)).to(torch.bfloat16)
+    for kk, vv in ((k, v), (torch.ones_like(k), torch.ones_like(v))):
+        (qd, kd, vd), stats, idx = run_gpu(q, kk, vv, keep, 0.1)
+        qn, kn, vn = (x[0, 0].double().numpy() for x in (q, kk, vv))
+        st = pisa.block_stats(kn, vn, 64)
+        ir, sc = pisa.route(qn, st["kbar"], st["M"], keep, 0.1, 1 / np.sqrt(d), 64)
+        assert (idx.cpu().numpy()[0, 0] == ir).all()
