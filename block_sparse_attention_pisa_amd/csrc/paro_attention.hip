@@ -3,29 +3,29 @@
 // "hardware implementation": stage 1 exact, stage 2 zeroth-order scan,
 // stage 3 global first-order correction, then o = N / D).
 //
-// bf16 kernel (k_attn_bf16): a workgroup of 4 waves serves 4 consecutive
-// query blocks of one (batch, head), one wave per block of 64 rows.
+// bf16 kernel (k_attn_bf16): a workgroup of 8 waves serves 4 consecutive
+// query blocks of one (batch, head); each block of 64 rows is split between
+// two waves of 32 rows, so every wave fits in 256 registers and each SIMD
+// runs two waves whose matrix and vector work interleave.
 //  * The exact lists of the 4 blocks are merged into their sorted union; each
-//    union tile (64 keys x d) is staged once into LDS for the 4 waves (the
-//    global loads of the next tile sit in registers while the current one is
-//    consumed; two LDS buffers; one barrier per tile). K is stored row-major
-//    and V transposed (V^T[dim][key]); rows are padded so that every MFMA
-//    operand is one conflict-free ds_read_b128 at a per-lane base plus a
-//    compile-time offset.
-//  * A wave computes S^T = K Q^T for its 64 queries as two 32-row halves on
-//    v_mfma_f32_32x32x16_bf16, both halves fed by the same K operand read; Q^T
-//    stays in registers. In the C layout of S^T each lane owns one query per
-//    half and 32 keys, so the softmax state is per lane.
+//    union tile (64 keys x d) is staged once into LDS for all 8 waves (the
+//    global loads of the tile after next sit in registers while the current
+//    one is consumed; two LDS buffers; one LDS-only barrier per tile). K is
+//    stored row-major and V transposed (V^T[dim][key]); rows are padded so
+//    every MFMA operand is one conflict-free ds_read_b128 at a per-lane base
+//    plus a compile-time offset.
+//  * A wave computes S^T = K Q^T for its 32 queries on
+//    v_mfma_f32_32x32x16_bf16 with Q^T held in registers. In the C layout of
+//    S^T each lane owns one query and 32 keys of the tile, so the softmax
+//    state is per lane.
 //  * O^T += V^T P^T with P straight from the S^T accumulators (K rows are read
 //    in a permuted order so each lane's 8 consecutive P values are 8
-//    consecutive keys of a V^T row). The O^T accumulators are only written by
-//    MFMAs inside the tile loop. A tile's two 32-key halves are independent
-//    chains, so one half's softmax can overlap the other's matrix work.
+//    consecutive keys of a V^T row).
 //  * The softmax reference m is fixed by the first tile a wave sees and never
 //    moves, so O needs no rescaling: N and D share the factor exp(-m), which
 //    cancels in N / D. A tile whose maximum exceeds m by more than 2^64 (far
 //    beyond real attention logits) marks the wave, and after the pass the
-//    marked waves recompute their block with m set to the exact maximum
+//    marked waves recompute their rows with m set to the exact maximum
 //    recorded during the first pass.
 //  * Stage 2 streams all T centroids in chunks of 32 through the same code
 //    (kbar as keys, vsum as values, converted to bf16 while staging), with the
@@ -43,7 +43,8 @@ namespace paro {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kWaves = 4;                 // query blocks per workgroup
+constexpr int kQB = 4;                    // query blocks per workgroup
+constexpr int kWaves = 2 * kQB;           // two 32-row waves per query block
 constexpr int kAttnThreads = 64 * kWaves;
 constexpr float kOverflowSlack = 64.f;    // log2 units above the reference max that trigger a rerun
 
@@ -58,8 +59,12 @@ struct Geo {
   static constexpr int BUF = KTILE + VTILE;                // one staging buffer (elements)
   static constexpr int NK = D / 16;                        // k-steps of S^T = K Q^T
   static constexpr int NU = D / 32;                        // 32-dim output tiles
-  static constexpr int KPT = 64 * CG / kAttnThreads;       // K chunks staged per thread
+  static constexpr int KPT = 64 * CG / kAttnThreads;       // exact-tile K chunks staged per thread
+  static constexpr int KCT = (32 * CG + kAttnThreads - 1) / kAttnThreads;  // centroid K chunks per thread
+  static constexpr int NR = (KPT > 2 * KCT ? KPT : 2 * KCT) + 2;          // staging registers (16 B)
+  static constexpr int VI = NR - 2;                                       // first V register
   static_assert(D * HS <= 2 * BUF, "Hbar^T must fit in the staging buffers");
+  static_assert(32 * CG == kAttnThreads || 32 * CG * 2 == kAttnThreads, "V items per thread");
 };
 
 // Key (tile row) that MFMA row m of S^T sub-tile t reads, chosen so that
@@ -79,55 +84,54 @@ __device__ __forceinline__ uint4 to_bf16x8(const float4& a, const float4& b) {
 __device__ __forceinline__ float4 as_f4(const uint4& u) { return __builtin_bit_cast(float4, u); }
 
 // ------------------------------------------------------------ staging
-// One step's data in flight, KPT + 4 registers of 16 bytes per thread. Rows
-// past the valid range re-read the last valid row (finite values whose keys
-// are masked out), so the loads need no predication.
-//  exact tile (bf16): r[0..KPT) = K chunks, r[KPT..KPT+4) = 4 keys x 8 dims of V;
-//  centroid chunk (fp32, 32 centroids): r[0..KPT) = kbar chunks as float4
-//  pairs, r[KPT..KPT+4) = 2 centroids x 8 dims of vsum.
-// V items put consecutive lanes on consecutive key groups, so each LDS write
-// instruction fills whole V^T rows.
+// One step's data in flight, NR registers of 16 bytes per thread:
+//  exact tile (bf16): r[0..KPT) = K chunks; r[VI..VI+2) = 2 keys x 8 dims of V;
+//  centroid chunk (fp32, 32 centroids): r[0..2 KCT) = kbar chunks as float4
+//  pairs; r[VI..VI+2) = 1 centroid x 8 dims of vsum.
+// V items put consecutive lanes on consecutive keys, so each LDS write
+// instruction fills whole V^T rows. Rows past the valid range re-read the last
+// valid row (finite values whose keys are masked out): no predicated loads.
 template <int D>
 struct Stage {
-  uint4 r[Geo<D>::KPT + 4];
+  uint4 r[Geo<D>::NR];
 };
 
 template <int D>
 __device__ __forceinline__ void load_exact(const uint16_t* __restrict__ Kh, const uint16_t* __restrict__ Vh,
                                            int row0, int nvalid, Stage<D>& st) {
-  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT;
+  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT, VI = Geo<D>::VI;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int q = threadIdx.x + kAttnThreads * i;
     const int row = min(q / CG, nvalid - 1), c = q % CG;
     st.r[i] = *reinterpret_cast<const uint4*>(Kh + static_cast<size_t>(row0 + row) * D + 8 * c);
   }
-  const int item = threadIdx.x;  // 16 key groups (fast) x CG dim groups
-  const int kg = item & 15, dg = min(item >> 4, CG - 1);
+  // item: 32 key pairs (fast) x CG dim groups; with d = 64 the upper half of
+  // the threads repeats the lower half's loads and stores nothing
+  const int item = threadIdx.x % (32 * CG);
+  const int kp = item & 31, dg = item >> 5;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int row = min(4 * kg + e, nvalid - 1);
-    st.r[KPT + e] = *reinterpret_cast<const uint4*>(Vh + static_cast<size_t>(row0 + row) * D + 8 * dg);
+  for (int e = 0; e < 2; ++e) {
+    const int row = min(2 * kp + e, nvalid - 1);
+    st.r[VI + e] = *reinterpret_cast<const uint4*>(Vh + static_cast<size_t>(row0 + row) * D + 8 * dg);
   }
 }
 template <int D>
 __device__ __forceinline__ void store_exact(const Stage<D>& st, uint16_t* buf) {
-  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT, KS = Geo<D>::KS, VS = Geo<D>::VS;
+  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT, KS = Geo<D>::KS, VS = Geo<D>::VS, VI = Geo<D>::VI;
   uint16_t* vt = buf + Geo<D>::KTILE;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     const int q = threadIdx.x + kAttnThreads * i;
     *reinterpret_cast<uint4*>(buf + (q / CG) * KS + 8 * (q % CG)) = st.r[i];
   }
-  const int item = threadIdx.x;
-  const int kg = item & 15, dg = item >> 4;
-  if (dg < CG) {  // threads past 16 CG items (d = 64) only loaded duplicates
+  if (threadIdx.x < 32 * CG) {
+    const int item = threadIdx.x;
+    const int kp = item & 31, dg = item >> 5;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t w0 = half16(st.r[KPT], e) | (half16(st.r[KPT + 1], e) << 16);
-      const uint32_t w1 = half16(st.r[KPT + 2], e) | (half16(st.r[KPT + 3], e) << 16);
-      *reinterpret_cast<uint2*>(vt + (8 * dg + e) * VS + 4 * kg) = make_uint2(w0, w1);
-    }
+    for (int e = 0; e < 8; ++e)
+      *reinterpret_cast<uint32_t*>(vt + (8 * dg + e) * VS + 2 * kp) =
+          half16(st.r[VI], e) | (half16(st.r[VI + 1], e) << 16);
   }
 }
 // Tail chunk of 32 centroids [j0, j0 + 32): kbar rows -> K tile rows 0..31,
@@ -135,83 +139,72 @@ __device__ __forceinline__ void store_exact(const Stage<D>& st, uint16_t* buf) {
 template <int D>
 __device__ __forceinline__ void load_centroids(const float* __restrict__ kb, const float* __restrict__ vs, int j0,
                                                int T, Stage<D>& st) {
-  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT;
+  constexpr int CG = Geo<D>::CG, KCT = Geo<D>::KCT, VI = Geo<D>::VI;
 #pragma unroll
-  for (int i = 0; i < KPT / 2; ++i) {
-    const int q = threadIdx.x + kAttnThreads * i;
+  for (int i = 0; i < KCT; ++i) {
+    const int q = min(static_cast<int>(threadIdx.x) + kAttnThreads * i, 32 * CG - 1);
     const int row = min(j0 + q / CG, T - 1), c = q % CG;
     const uint4* src = reinterpret_cast<const uint4*>(kb + static_cast<size_t>(row) * D + 8 * c);
     st.r[2 * i] = src[0];
     st.r[2 * i + 1] = src[1];
   }
-  const int item = threadIdx.x;  // 16 centroid pairs (fast) x CG dim groups
-  const int kp = item & 15, dg = min(item >> 4, CG - 1);
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int row = min(j0 + 2 * kp + e, T - 1);
-    const uint4* src = reinterpret_cast<const uint4*>(vs + static_cast<size_t>(row) * D + 8 * dg);
-    st.r[KPT + 2 * e] = src[0];
-    st.r[KPT + 2 * e + 1] = src[1];
-  }
+  const int item = threadIdx.x % (32 * CG);  // 32 centroids (fast) x CG dim groups
+  const int kc = item & 31, dg = item >> 5;
+  const uint4* src = reinterpret_cast<const uint4*>(vs + static_cast<size_t>(min(j0 + kc, T - 1)) * D + 8 * dg);
+  st.r[VI] = src[0];
+  st.r[VI + 1] = src[1];
 }
 template <int D>
 __device__ __forceinline__ void store_centroids(const Stage<D>& st, uint16_t* buf) {
-  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT, KS = Geo<D>::KS, VS = Geo<D>::VS;
+  constexpr int CG = Geo<D>::CG, KCT = Geo<D>::KCT, KS = Geo<D>::KS, VS = Geo<D>::VS, VI = Geo<D>::VI;
   uint16_t* vt = buf + Geo<D>::KTILE;
 #pragma unroll
-  for (int i = 0; i < KPT / 2; ++i) {
+  for (int i = 0; i < KCT; ++i) {
     const int q = threadIdx.x + kAttnThreads * i;
-    *reinterpret_cast<uint4*>(buf + (q / CG) * KS + 8 * (q % CG)) =
-        to_bf16x8(as_f4(st.r[2 * i]), as_f4(st.r[2 * i + 1]));
+    if (q < 32 * CG)
+      *reinterpret_cast<uint4*>(buf + (q / CG) * KS + 8 * (q % CG)) =
+          to_bf16x8(as_f4(st.r[2 * i]), as_f4(st.r[2 * i + 1]));
   }
-  const int item = threadIdx.x;
-  const int kp = item & 15, dg = item >> 4;
-  if (dg < CG) {
-    const float4 x0 = as_f4(st.r[KPT]), y0 = as_f4(st.r[KPT + 1]), x1 = as_f4(st.r[KPT + 2]), y1 = as_f4(st.r[KPT + 3]);
-    const float a0[8] = {x0.x, x0.y, x0.z, x0.w, y0.x, y0.y, y0.z, y0.w};
-    const float a1[8] = {x1.x, x1.y, x1.z, x1.w, y1.x, y1.y, y1.z, y1.w};
+  if (threadIdx.x < 32 * CG) {
+    const int item = threadIdx.x;
+    const int kc = item & 31, dg = item >> 5;
+    const float4 x = as_f4(st.r[VI]), y = as_f4(st.r[VI + 1]);
+    const float a0[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<uint32_t*>(vt + (8 * dg + e) * VS + 2 * kp) = pack_bf16x2(a0[e], a1[e]);
+    for (int e = 0; e < 8; ++e) vt[(8 * dg + e) * VS + kc] = f32_to_bf16(a0[e]);
   }
 }
 
 // ------------------------------------------------------------ compute
 template <int D>
 struct Acc {
-  bf16x8 qb[2][Geo<D>::NK];   // B operand Q^T of half h: query 32 h + lane % 32, dims 16 s + 8 g .. + 8
-  f32x16 o[Geo<D>::NU][2];    // O^T: dims 32 u + 8 (i / 4) + 4 g + i % 4, query 32 h + lane % 32
-  float m[2];                 // reference max (log2 units), -inf until the first tile
-  float mtrue[2];             // exact running max, for a rerun
-  float dsum[2];              // this lane's part of D
-  float csum[2];              // this lane's part of c
-  bool over;                  // some logit exceeded m + kOverflowSlack
+  bf16x8 qb[Geo<D>::NK];   // B operand Q^T: query lane % 32 of the wave's rows, dims 16 s + 8 g .. + 8
+  f32x16 o[Geo<D>::NU];    // O^T: dims 32 u + 8 (i / 4) + 4 g + i % 4, query lane % 32
+  float m;                 // reference max (log2 units), -inf until the first tile
+  float mtrue;             // exact running max, for a rerun
+  float dsum;              // this lane's part of D
+  float csum;              // this lane's part of c
+  bool over;               // some logit exceeded m + kOverflowSlack
 };
 
-// S^T of 32 keys (K rows read from kt + kbase: the lane's permuted row, its 8-dim half).
+// S^T of 32 keys (kt: the lane's permuted K row and 8-dim half).
 template <int D>
-__device__ __forceinline__ void qk_half(const uint16_t* kt, const Acc<D>& a, f32x16 (&s)[2]) {
-  s[0] = f32x16{};
-  s[1] = f32x16{};
+__device__ __forceinline__ f32x16 qk_half(const uint16_t* kt, const Acc<D>& a) {
+  f32x16 s = f32x16{};
 #pragma unroll
-  for (int ks = 0; ks < Geo<D>::NK; ++ks) {
-    const bf16x8 av = *reinterpret_cast<const bf16x8*>(kt + 16 * ks);
-    s[0] = mfma32x32x16(av, a.qb[0][ks], s[0]);
-    s[1] = mfma32x32x16(av, a.qb[1][ks], s[1]);
-  }
+  for (int ks = 0; ks < Geo<D>::NK; ++ks)
+    s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kt + 16 * ks), a.qb[ks], s);
+  return s;
 }
 
 // O^T += V^T P^T for 32 keys (vt: the lane's V^T row base plus the key offset).
 template <int D>
-__device__ __forceinline__ void pv_half(const uint16_t* vt, const bf16x8 (&pb)[2][2], Acc<D>& a) {
+__device__ __forceinline__ void pv_half(const uint16_t* vt, const bf16x8 (&pb)[2], Acc<D>& a) {
 #pragma unroll
   for (int u = 0; u < Geo<D>::NU; ++u)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt + 32 * u * Geo<D>::VS + 16 * s);
-      a.o[u][0] = mfma32x32x16(av, pb[0][s], a.o[u][0]);
-      a.o[u][1] = mfma32x32x16(av, pb[1][s], a.o[u][1]);
-    }
+    for (int s = 0; s < 2; ++s)
+      a.o[u] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(vt + 32 * u * Geo<D>::VS + 16 * s), pb[s], a.o[u]);
 }
 
 // The lane's 16 keys of 32-key sub-tile t as a 16-bit mask of a 64-bit key mask.
@@ -224,45 +217,42 @@ __device__ __forceinline__ uint32_t lane_bits(uint64_t km, int t, int g) {
 // kMask: keys with a set bit in lmask get weight 0. kTail: D gains n_j p
 // (n_j = 64 except nlast for the key flagged in llast) and c gains p.
 template <int D, bool kMask, bool kTail>
-__device__ __forceinline__ void softmax_half(f32x16 (&s)[2], Acc<D>& a, float cl2, uint32_t lmask, uint32_t llast,
-                                             float nlast, bf16x8 (&pb)[2][2]) {
+__device__ __forceinline__ void softmax_half(f32x16& s, Acc<D>& a, float cl2, uint32_t lmask, uint32_t llast,
+                                             float nlast, bf16x8 (&pb)[2]) {
+  float v = -INFINITY;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float v = -INFINITY;
+  for (int i = 0; i < 16; ++i) {
+    if (kMask && ((lmask >> i) & 1u)) s[i] = -INFINITY;
+    v = fmaxf(v, s[i]);
+  }
+  v = fmaxf(v, __shfl_xor(v, 32)) * cl2;
+  a.mtrue = fmaxf(a.mtrue, v);
+  if (a.m == -INFINITY) a.m = v;
+  a.over = a.over || v > a.m + kOverflowSlack;
+  const float mref = a.m == -INFINITY ? 0.f : a.m;
+  float pv[16];
+  float ps = 0.f, pl = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (kMask && ((lmask >> i) & 1u)) s[h][i] = -INFINITY;
-      v = fmaxf(v, s[h][i]);
-    }
-    v = fmaxf(v, __shfl_xor(v, 32)) * cl2;
-    a.mtrue[h] = fmaxf(a.mtrue[h], v);
-    if (a.m[h] == -INFINITY) a.m[h] = v;
-    a.over = a.over || v > a.m[h] + kOverflowSlack;
-    const float mref = a.m[h] == -INFINITY ? 0.f : a.m[h];
-    float ps = 0.f, pl = 0.f;
-    float pv[16];
+  for (int i = 0; i < 16; ++i) {
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cl2, -mref));
+    pv[i] = p;
+    ps += p;
+    if (kTail) pl += ((llast >> i) & 1u) ? p : 0.f;
+  }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][i], cl2, -mref));
-      pv[i] = p;
-      ps += p;
-      if (kTail) pl += ((llast >> i) & 1u) ? p : 0.f;
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      uint4 w;
-      w.x = pack_bf16x2(pv[8 * c + 0], pv[8 * c + 1]);
-      w.y = pack_bf16x2(pv[8 * c + 2], pv[8 * c + 3]);
-      w.z = pack_bf16x2(pv[8 * c + 4], pv[8 * c + 5]);
-      w.w = pack_bf16x2(pv[8 * c + 6], pv[8 * c + 7]);
-      pb[h][c] = __builtin_bit_cast(bf16x8, w);
-    }
-    if (kTail) {
-      a.dsum[h] += 64.f * ps + (nlast - 64.f) * pl;
-      a.csum[h] += ps;
-    } else {
-      a.dsum[h] += ps;
-    }
+  for (int c = 0; c < 2; ++c) {
+    uint4 w;
+    w.x = pack_bf16x2(pv[8 * c + 0], pv[8 * c + 1]);
+    w.y = pack_bf16x2(pv[8 * c + 2], pv[8 * c + 3]);
+    w.z = pack_bf16x2(pv[8 * c + 4], pv[8 * c + 5]);
+    w.w = pack_bf16x2(pv[8 * c + 6], pv[8 * c + 7]);
+    pb[c] = __builtin_bit_cast(bf16x8, w);
+  }
+  if (kTail) {
+    a.dsum += 64.f * ps + (nlast - 64.f) * pl;
+    a.csum += ps;
+  } else {
+    a.dsum += ps;
   }
 }
 
@@ -275,20 +265,22 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* buf = reinterpret_cast<uint16_t*>(smem);  // 2 staging buffers
   const int nw = ceil_div(T, 32);
-  uint32_t* masks = reinterpret_cast<uint32_t*>(smem + sizeof(uint16_t) * 2 * BUF);  // [kWaves][nw]
-  int* sh = reinterpret_cast<int*>(masks + kWaves * nw);                            // nu, rerun flags
-  uint16_t* ulist = reinterpret_cast<uint16_t*>(sh + 8);                            // [T]
+  uint32_t* masks = reinterpret_cast<uint32_t*>(smem + sizeof(uint16_t) * 2 * BUF);  // [kQB][nw]
+  int* sh = reinterpret_cast<int*>(masks + kQB * nw);                               // nu, rerun flags
+  uint16_t* ulist = reinterpret_cast<uint16_t*>(sh + 12);                           // [T]
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so hand
   // each XCD a contiguous run of (head, query-block group) items.
   int wg = blockIdx.x;
   const int n8 = (nwg / 8) * 8;
   if (wg < n8) wg = (wg % 8) * (nwg / 8) + wg / 8;
-  const int ngrp = ceil_div(T, kWaves);
+  const int ngrp = ceil_div(T, kQB);
   const int grp = wg % ngrp, bh = wg / ngrp;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, ql = l & 31;
-  const int qblk = grp * kWaves + w;
+  const int qi = w >> 1;                       // query block of this wave within the group
+  const int qblk = grp * kQB + qi;
+  const int row = qblk * 64 + 32 * (w & 1) + ql;  // this lane's query row
   const bool qvalid = qblk < T;
   const size_t head = static_cast<size_t>(bh) * L * D;
   const uint16_t* Kh = K + head;
@@ -300,30 +292,28 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   const int voff = Geo<D>::KTILE + ql * VS + 8 * g;           // V^T rows 32 u + ql (+16 s + 32 t keys)
 
   Acc<D> a;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = qblk * 64 + 32 * h + ql;
+  {
     const uint16_t* qp = Q + head + static_cast<size_t>(row) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < Geo<D>::NK; ++ks) {
       const uint4 v = (qvalid && row < L) ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
-      a.qb[h][ks] = __builtin_bit_cast(bf16x8, v);
+      a.qb[ks] = __builtin_bit_cast(bf16x8, v);
     }
-    a.m[h] = -INFINITY;
-    a.mtrue[h] = -INFINITY;
+    a.m = -INFINITY;
+    a.mtrue = -INFINITY;
   }
 
   // ---- membership masks of the 4 exact lists and their sorted union
-  for (int e = tid; e < kWaves * nw; e += kAttnThreads) masks[e] = 0u;
-  __syncthreads();
-  if (qvalid) {
+  for (int e = tid; e < kQB * nw; e += kAttnThreads) masks[e] = 0u;
+  lds_barrier();
+  if (qvalid && (w & 1) == 0) {
     const int32_t* irow = idx + (static_cast<size_t>(bh) * T + qblk) * keep_k;
     for (int e = l; e < keep_k; e += 64) {
       const int j = min(max(irow[e], 0), T - 1);
-      atomicOr(&masks[w * nw + (j >> 5)], 1u << (j & 31));
+      atomicOr(&masks[qi * nw + (j >> 5)], 1u << (j & 31));
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (w == 0) {
     int base = 0;
     for (int w0 = 0; w0 < nw; w0 += 64) {
@@ -345,21 +335,24 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     }
     if (l == 0) sh[0] = base;
   }
-  __syncthreads();
+  lds_barrier();
   const int nu = sh[0];
-  const uint32_t* mymask = masks + w * nw;
+  const uint32_t* mymask = masks + qi * nw;
   const float* kb = kbar + static_cast<size_t>(bh) * T * D;
   const float* vs = vsum + static_cast<size_t>(bh) * T * D;
   const int nch = keep_k < T ? ceil_div(T, 32) : 0;
 
   bool active = qvalid;
+#pragma unroll
+  for (int u = 0; u < Geo<D>::NU; ++u) a.o[u] = f32x16{};
+  a.dsum = 0.f;
+  a.csum = 0.f;
   for (int pass = 0; pass < 2; ++pass) {
+    if (pass > 0 && active) {  // only rerunning waves start over; the others keep their sums
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int u = 0; u < Geo<D>::NU; ++u) a.o[u][h] = f32x16{};
-      a.dsum[h] = 0.f;
-      a.csum[h] = 0.f;
+      for (int u = 0; u < Geo<D>::NU; ++u) a.o[u] = f32x16{};
+      a.dsum = 0.f;
+      a.csum = 0.f;
     }
     a.over = false;
 
@@ -385,26 +378,24 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       fetch(0);
       put(0, buf);
     }
-    __syncthreads();
+    lds_barrier();
     if (nsteps > 1) fetch(1);
-    // Three loops over consecutive step ranges, one compute variant each, so
-    // the O^T accumulators keep one register assignment inside every loop:
+    // Three loops over consecutive step ranges, one compute variant each:
     // full exact tiles, then the partial last block (always last in the
     // ascending union), then the centroid chunks.
     const int nfull = (nu > 0 && ulist[nu - 1] == T - 1 && nlast < 64) ? nu - 1 : nu;
     auto advance = [&](int step) {
       if (step + 1 < nsteps) put(step + 1, buf + ((step + 1) & 1) * BUF);
       if (step + 2 < nsteps) fetch(step + 2);
-      __syncthreads();
+      lds_barrier();
     };
     for (int step = 0; step < nfull; ++step) {
       const uint16_t* bc = buf + (step & 1) * BUF;
       const int j = ulist[step];
       if (active && ((mymask[j >> 5] >> (j & 31)) & 1u)) {
-        f32x16 s0[2], s1[2];
-        bf16x8 p0[2][2], p1[2][2];
-        qk_half<D>(bc + koff, a, s0);
-        qk_half<D>(bc + koff + 32 * KS, a, s1);
+        f32x16 s0 = qk_half<D>(bc + koff, a);
+        f32x16 s1 = qk_half<D>(bc + koff + 32 * KS, a);
+        bf16x8 p0[2], p1[2];
         softmax_half<D, false, false>(s0, a, cl2, 0u, 0u, 0.f, p0);
         pv_half<D>(bc + voff, p0, a);
         softmax_half<D, false, false>(s1, a, cl2, 0u, 0u, 0.f, p1);
@@ -417,10 +408,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       const int j = ulist[step];
       if (active && ((mymask[j >> 5] >> (j & 31)) & 1u)) {
         const uint64_t km = ~0ull << nlast;
-        f32x16 s0[2], s1[2];
-        bf16x8 p0[2][2], p1[2][2];
-        qk_half<D>(bc + koff, a, s0);
-        qk_half<D>(bc + koff + 32 * KS, a, s1);
+        f32x16 s0 = qk_half<D>(bc + koff, a);
+        f32x16 s1 = qk_half<D>(bc + koff + 32 * KS, a);
+        bf16x8 p0[2], p1[2];
         softmax_half<D, true, false>(s0, a, cl2, lane_bits(km, 0, g), 0u, 0.f, p0);
         pv_half<D>(bc + voff, p0, a);
         softmax_half<D, true, false>(s1, a, cl2, lane_bits(km, 1, g), 0u, 0.f, p1);
@@ -436,36 +426,30 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
         if (j0 + 32 > T) km |= ~0ull << (T - j0);
         const int lk = T - 1 - j0;  // chunk-local index of the last (partial) block, if present
         const uint64_t kl = (lk >= 0 && lk < 32) ? (1ull << lk) : 0ull;
-        f32x16 s0[2];
-        bf16x8 p0[2][2];
-        qk_half<D>(bc + koff, a, s0);
+        f32x16 s0 = qk_half<D>(bc + koff, a);
+        bf16x8 p0[2];
         softmax_half<D, true, true>(s0, a, cl2, lane_bits(km, 0, g), lane_bits(kl, 0, g), static_cast<float>(nlast), p0);
         pv_half<D>(bc + voff, p0, a);
       }
       advance(step);
     }
 
-    // ---- rerun the blocks whose logits outgrew their reference max
+    // ---- rerun the rows whose logits outgrew their reference max
     const bool mine = active && __any(a.over);
     if (l == 0) sh[1 + w] = mine ? 1 : 0;
-    __syncthreads();
-    const bool any = sh[1] | sh[2] | sh[3] | sh[4];
-    __syncthreads();
+    lds_barrier();
+    bool any = false;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) any = any || sh[1 + v];
+    lds_barrier();
     if (!any) break;
     active = mine;
-    if (mine) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) a.m[h] = a.mtrue[h];
-    }
+    if (mine) a.m = a.mtrue;
   }
 
   // ---- stage 3: global first-order correction, then N / D
-  float csum[2], dsum[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    csum[h] = a.csum[h] + __shfl_xor(a.csum[h], 32);
-    dsum[h] = a.dsum[h] + __shfl_xor(a.dsum[h], 32);
-  }
+  const float csum = a.csum + __shfl_xor(a.csum, 32);
+  const float dsum = a.dsum + __shfl_xor(a.dsum, 32);
   if (nch > 0) {
     // Hbar^T in bf16: ht[v][k] = Hbar[k][v], rows padded to HS
     const float* Hh = Hbar + static_cast<size_t>(bh) * D * D;
@@ -484,38 +468,29 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
         *reinterpret_cast<uint2*>(buf + (8 * vg + e) * HS + 4 * kg) =
             make_uint2(pack_bf16x2(f[0][e], f[1][e]), pack_bf16x2(f[2][e], f[3][e]));
     }
-    __syncthreads();
+    lds_barrier();
   }
+  // MFMAs need the whole wave: only the stores are guarded per lane.
   if (qvalid) {
     const uint16_t* hrow = buf + ql * HS + 8 * g;
+    const float inv = 1.f / dsum;
+    uint16_t* op = O + head + static_cast<size_t>(row) * D;
 #pragma unroll
     for (int u = 0; u < Geo<D>::NU; ++u) {
-      f32x16 o0 = a.o[u][0], o1 = a.o[u][1];
+      f32x16 o = a.o[u];
       if (nch > 0) {
-        f32x16 r0 = f32x16{}, r1 = f32x16{};
+        f32x16 r = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < Geo<D>::NK; ++ks) {
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(hrow + 32 * u * HS + 16 * ks);
-          r0 = mfma32x32x16(av, a.qb[0][ks], r0);
-          r1 = mfma32x32x16(av, a.qb[1][ks], r1);
-        }
-        o0 += (scale * csum[0]) * r0;
-        o1 += (scale * csum[1]) * r1;
+        for (int ks = 0; ks < Geo<D>::NK; ++ks)
+          r = mfma32x32x16(*reinterpret_cast<const bf16x8*>(hrow + 32 * u * HS + 16 * ks), a.qb[ks], r);
+        o += (scale * csum) * r;
       }
+      if (row < L) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = qblk * 64 + 32 * h + ql;
-        if (row < L) {
-          const float inv = 1.f / dsum[h];
-          const f32x16& o = h == 0 ? o0 : o1;
-          uint16_t* op = O + head + static_cast<size_t>(row) * D;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int dim = 32 * u + 8 * q + 4 * g;
-            *reinterpret_cast<uint2*>(op + dim) =
-                make_uint2(pack_bf16x2(o[4 * q] * inv, o[4 * q + 1] * inv),
-                           pack_bf16x2(o[4 * q + 2] * inv, o[4 * q + 3] * inv));
-          }
+        for (int q = 0; q < 4; ++q) {
+          const int dim = 32 * u + 8 * q + 4 * g;
+          *reinterpret_cast<uint2*>(op + dim) = make_uint2(pack_bf16x2(o[4 * q] * inv, o[4 * q + 1] * inv),
+                                                           pack_bf16x2(o[4 * q + 2] * inv, o[4 * q + 3] * inv));
         }
       }
     }
@@ -616,13 +591,13 @@ hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, cons
                        hipStream_t s) {
   const int T = ceil_div(p.L, 64);
   const int nw = ceil_div(T, 32);
-  const size_t lds = sizeof(uint16_t) * 2 * Geo<D>::BUF + sizeof(uint32_t) * kWaves * nw + 8 * sizeof(int) +
+  const size_t lds = sizeof(uint16_t) * 2 * Geo<D>::BUF + sizeof(uint32_t) * kQB * nw + 12 * sizeof(int) +
                      sizeof(uint16_t) * T;
   const size_t lds_al = (lds + 15) / 16 * 16;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_bf16<D>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_al));
   if (e != hipSuccess) return e;
-  const int nwg = ceil_div(T, kWaves) * p.B * p.H;
+  const int nwg = ceil_div(T, kQB) * p.B * p.H;
   hipLaunchKernelGGL(k_attn_bf16<D>, dim3(nwg), dim3(kAttnThreads), lds_al, s,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), kbar, vsum, Hbar, idx, static_cast<uint16_t*>(O), p.L, T,

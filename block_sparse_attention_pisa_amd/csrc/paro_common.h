@@ -84,6 +84,18 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Workgroup barrier for data exchanged through LDS only: waits for this
+// wave's LDS operations (lgkmcnt(0)) but leaves global loads in flight, unlike
+// __syncthreads(), whose release fence also drains every outstanding global
+// load. The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt and expcnt at their maxima, lgkmcnt = 0
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace paro
 
 // ----------------------------------------------------- launcher prototypes

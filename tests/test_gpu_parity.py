@@ -142,3 +142,28 @@ def test_route_exact_ties_and_equal_scores(keep):
         st = pisa.block_stats(kn, vn, 64)
         ir, sc = pisa.route(qn, st["kbar"], st["M"], keep, 0.1, 1 / np.sqrt(d), 64)
         assert (idx.cpu().numpy()[0, 0] == ir).all()
+
+
+def test_logit_jump_rerun_keeps_every_row_exact():
+    """A kv block whose logits sit ~88 nats above the first tile's forces the
+    kernel's rerun path for the query blocks that list it; the other blocks of
+    the same workgroup must keep their own results."""
+    B, H, d, nb = 1, 1, 128, 8
+    L = 64 * nb
+    g = np.random.default_rng(7)
+    e0 = np.zeros(d, dtype=np.float32)
+    e0[0] = 1.0
+    q = (0.1 * g.standard_normal((L, d)) + e0).astype(np.float32)
+    k = (0.5 * g.standard_normal((L, d))).astype(np.float32)
+    k[5 * 64:6 * 64] = 1000.0 * e0 + 0.5 * g.standard_normal((64, d))
+    v = g.standard_normal((L, d)).astype(np.float32)
+    qt, kt, vt = (torch.from_numpy(x)[None, None].to(torch.bfloat16) for x in (q, k, v))
+    idx = np.array([[0, 5], [0, 5], [0, 1], [0, 1], [0, 5], [2, 3], [1, 5], [0, 7]], dtype=np.int32)
+    qd, kd, vd = (x.cuda() for x in (qt, kt, vt))
+    stats = paro.precompute(kd, vd)
+    o = paro.attention(qd, kd, vd, *stats[:3], torch.from_numpy(idx)[None, None].cuda(), 2).float().cpu().numpy()
+    qn, kn, vn = (x[0, 0].double().numpy() for x in (qt, kt, vt))
+    st = pisa.block_stats(kn, vn, 64)
+    ref = pisa.attention(qn, kn, vn, st, idx.astype(np.int64), 1 / np.sqrt(d), 64)
+    assert np.isfinite(o).all()
+    check_attention(o[0, 0], ref, "bf16")
