@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic_video720p_75600.json")
-ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_pisa_amd", "csrc", "paro_attention.hip")
+ATTN_SRCS = [os.path.join(ROOT, "block_sparse_attention_pisa_amd", "csrc", f)
+             for f in ("paro_attention.hip", "paro_common.h")]
 
 
 def parse():
@@ -76,7 +77,7 @@ def traffic_entry():
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in ATTN_SRCS)).hexdigest()
         if rec.get("source_sha256") != sha:
             return None
         return rec["hbm_bytes_per_launch"]
