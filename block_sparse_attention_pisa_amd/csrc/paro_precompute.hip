@@ -13,12 +13,14 @@
 //                        K_j^T V_j runs on bf16 MFMA 16x16x32 (exact products,
 //                        fp32 accumulation) from LDS tiles transposed so that
 //                        tokens are contiguous.
-//   2. k_hbar_reduce   : fixed-order fp64 sum of the chunk partials -> Hbar.
-//   3. k_block_spectral: re-reads K and V, rebuilds H_j in registers, forms
-//                        A = H_j - Hbar and finds its largest singular value
-//                        by restarted Lanczos on A^T A (fp32 vectors, fp64
-//                        scalars); the final ||A x|| / ||x|| is accumulated in
-//                        fp64. H_j never reaches memory.
+//   2. k_hbar_reduce   : fixed-order fp64 sum of the chunk partials -> Hbar
+//                        (and a register-order copy of it in the workspace).
+//   3. k_block_spectral: one workgroup of two waves per block; re-reads K_j
+//                        and V_j, rebuilds A = H_j - Hbar in registers on
+//                        MFMA and finds its largest singular value by
+//                        restarted Lanczos on A^T A (fp32 vectors, fp64
+//                        tridiagonal eigenproblem); the final ||A x|| / ||x||
+//                        is accumulated in fp64. H_j never reaches memory.
 // No float atomics anywhere: results are bitwise reproducible.
 #include "paro_common.h"
 
@@ -213,352 +215,476 @@ __global__ __launch_bounds__(kThreads) void k_block_stats(const E* __restrict__ 
       for (int r = 0; r < 4; ++r) out[acc_row<D>(mi, r) * D + acc_col(nt)] = acc.v[mi][nt][r];
 }
 
+// ------------------------------------------------------------ kernel 3 layout
+// A = H_j - Hbar is split over the two waves of a k_block_spectral workgroup
+// in the C layout of the 16x16 MFMA: wave w, lane l (g = l / 16, c = l % 16)
+// holds v[ti][tj][r] = A[16 (MT w + ti) + 4 g + r][16 tj + c].
+template <int D>
+struct PairA {
+  static constexpr int MT = D / 32;  // 16-row tiles per wave
+  static constexpr int NT = D / 16;  // 16-column tiles
+  f32x4 v[MT][NT];
+};
+
+// Position of Hbar[row][col] in the per-lane order of PairA (so that each
+// lane loads its share of Hbar with 16-byte loads).
+template <int D>
+__device__ __forceinline__ int pair_perm_index(int row, int col) {
+  constexpr int MT = PairA<D>::MT, NT = PairA<D>::NT;
+  const int w = row / (D / 2), rr = row % (D / 2);
+  const int ti = rr / 16, g = (rr % 16) / 4, r = rr % 4;
+  const int tj = col / 16, c = col % 16;
+  return (((w * 64 + 16 * g + c) * MT + ti) * NT + tj) * 4 + r;
+}
+
 // ------------------------------------------------------------ kernel 2
+// Fixed-order fp64 sum of the chunk partials -> Hbar (row-major), plus a copy
+// of Hbar in PairA order for kernel 3.
+template <int D>
 __global__ __launch_bounds__(256) void k_hbar_reduce(const float* __restrict__ ws, float* __restrict__ Hbar,
-                                                     int D2, int nchunk, int T) {
+                                                     float* __restrict__ hperm, int nchunk, int T) {
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= D2) return;
+  if (e >= D * D) return;
   double sum = 0.0;
-  for (int c = 0; c < nchunk; ++c) sum += ws[(static_cast<size_t>(bh) * nchunk + c) * D2 + e];
-  Hbar[static_cast<size_t>(bh) * D2 + e] = static_cast<float>(sum / T);
+  for (int c = 0; c < nchunk; ++c) sum += ws[(static_cast<size_t>(bh) * nchunk + c) * D * D + e];
+  const float h = static_cast<float>(sum / T);
+  Hbar[static_cast<size_t>(bh) * D * D + e] = h;
+  hperm[static_cast<size_t>(bh) * D * D + pair_perm_index<D>(e / D, e % D)] = h;
 }
 
 // ------------------------------------------------------------ kernel 3
-// M_j by restarted Lanczos on B = A^T A (A = H_j - Hbar). Each cycle runs
-// kLanczosK steps w = B v_k with classical Gram-Schmidt against the whole
-// basis (fp32 vectors, fp64 dot products), finds the top eigenpair of the
-// small tridiagonal matrix (64-point Sturm multisection across the lanes of
-// one wave, then inverse iteration), restarts from the Ritz vector, and
-// stops when the Ritz residual bound res^2 / (gap * theta) is negligible.
+// M_j = sigma_max(A), A = H_j - Hbar, by Lanczos on A^T A. One workgroup of
+// two waves per block: each wave keeps half of the rows of A in registers
+// (rebuilt from K_j, V_j on MFMA), so y = A x needs no communication and
+// A^T y needs one exchange of a D-vector through LDS per step. Everything
+// in the column space of A (the Lanczos vectors, their coefficients and the
+// small tridiagonal eigenproblem) is computed by both waves on bitwise
+// identical data, so the waves take identical decisions without further
+// synchronisation.
+//   * Vectors: fp32, lane l holds entries 16 tj + c (tj < D / 16); dot
+//     products are 16-lane DPP sums. Classical Gram-Schmidt against the
+//     whole basis (kept in LDS, one copy per wave).
+//   * After kLanczosCheck and after kLanczosK steps the Ritz pair of the
+//     tridiagonal is computed (64-point Sturm multisection across the lanes,
+//     then inverse iteration); the block stops when the residual bound
+//     res^2 / (gap * theta) < kLanczosTol, otherwise the process restarts
+//     from the Ritz vector after kLanczosK steps.
+//   * M_j = ||A x|| / ||x|| is then evaluated in fp64 from the fp32 Ritz
+//     vector, so its error is quadratic in the angle of x.
 // Power iteration alone needs thousands of steps when sigma_2 / sigma_1 is
-// close to 1 (blocks of i.i.d. keys); this reaches the fp32 floor in one
-// cycle for almost every block. M_j = ||A x|| / ||x|| is then evaluated in
-// fp64 from the fp32 Ritz vector, so its error is quadratic in the angle.
+// close to 1 (blocks of i.i.d. keys); Lanczos converges in 5 to 8 steps for
+// almost every block of the video workloads.
 constexpr int kLanczosK = 8;
+constexpr int kLanczosCheck = 6;
 constexpr int kLanczosCycles = 16;
-constexpr double kLanczosTol = 1e-10;
+constexpr double kLanczosTol = 1e-9;
+constexpr int kPairThreads = 128;
 
 __device__ __forceinline__ float start_sign(int row) {
   return ((static_cast<uint32_t>(row + 1) * 2654435761u) >> 16) & 1u ? -1.f : 1.f;
 }
 
-template <int D>
-struct SpectralLds {
-  float xpart[16][D];           // column partials of A^T y (one row per 16-lane group)
-  float vk[kLanczosK + 1][D];   // Lanczos basis
-  float xs[D];                  // Ritz vector of the last cycle
-  double alpha[kLanczosK];
-  double beta[kLanczosK];
-  double red2[16];
-  double x2;
-  int flag;                     // 0 running, 1 converged, 2 A == 0
+template <typename E, int D>
+struct PairLds {
+  union {
+    struct {
+      E kt[D][kLdT];
+      E vt[D][kLdT];
+    } tile;
+    struct {
+      float basis[2][kLanczosK + 1][D];  // per wave; vector entry 16 tj + c stored at c * NT + tj
+      float zx[2][2][D];                 // [parity][wave] partial A^T y, same order
+    } lz;
+  } u;
+  float kbar[D];
+  float vsum[D];
+  float al[2][kLanczosK];
+  float be[2][kLanczosK];
+  double red[2][4];
 };
 
-// xpart[group][col] = sum over this lane's rows of A[row][col] * y[row].
-template <int D>
-__device__ __forceinline__ void write_col_partials(const HAcc<D>& A, const float (&y)[D / 64][4],
-                                                   SpectralLds<D>& sp) {
-  const int grp = threadIdx.x / 16;
+template <int NT>
+__device__ __forceinline__ void load_vec(const float* base, int c, float (&x)[NT]) {
 #pragma unroll
-  for (int nt = 0; nt < HAcc<D>::NTT; ++nt) {
-    float p = 0.f;
+  for (int q = 0; q < NT / 4; ++q) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(base + c * NT + 4 * q);
 #pragma unroll
-    for (int mi = 0; mi < HAcc<D>::MTW; ++mi)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p += A.v[mi][nt][r] * y[mi][r];
-    sp.xpart[grp][acc_col(nt)] = p;
+    for (int e = 0; e < 4; ++e) x[4 * q + e] = v[e];
   }
 }
+template <int NT>
+__device__ __forceinline__ void store_vec(float* base, int c, const float (&x)[NT]) {
+#pragma unroll
+  for (int q = 0; q < NT / 4; ++q)
+    *reinterpret_cast<f32x4*>(base + c * NT + 4 * q) = f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+}
+// Dot product of two column-space vectors (bitwise identical in every lane).
+template <int NT>
+__device__ __forceinline__ float vdot(const float (&a)[NT], const float (&b)[NT]) {
+  float p = 0.f;
+#pragma unroll
+  for (int tj = 0; tj < NT; ++tj) p += a[tj] * b[tj];
+  return row_sum16(p);
+}
 
-// xpart <- column partials of A^T (A x) for x = vk[k] (all threads).
+// y = A x for this wave's rows (y[ti][r] is row 16 (MT w + ti) + 4 g + r).
 template <int D>
-__device__ __forceinline__ void apply_ata(const HAcc<D>& A, SpectralLds<D>& sp, int k) {
-  constexpr int MTW = HAcc<D>::MTW, NTT = HAcc<D>::NTT;
-  float xc[NTT];
+__device__ __forceinline__ void pair_ax(const PairA<D>& A, const float (&x)[D / 16], float (&y)[D / 32][4]) {
 #pragma unroll
-  for (int nt = 0; nt < NTT; ++nt) xc[nt] = sp.vk[k][acc_col(nt)];
-  float y[MTW][4];
-#pragma unroll
-  for (int mi = 0; mi < MTW; ++mi)
+  for (int ti = 0; ti < PairA<D>::MT; ++ti)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float p = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < NTT; ++nt) p += A.v[mi][nt][r] * xc[nt];
-      y[mi][r] = row_sum16(p);
+      for (int tj = 0; tj < PairA<D>::NT; ++tj) p += A.v[ti][tj][r] * x[tj];
+      y[ti][r] = row_sum16(p);
     }
-  write_col_partials<D>(A, y, sp);
 }
-
-// One Lanczos step on wave 0 (lane l holds entries l + 64 e).
+// z = (partial over this wave's rows of) A^T y, summed over the 4 lane groups.
 template <int D>
-__device__ __forceinline__ void lanczos_step(SpectralLds<D>& sp, int k, int l) {
-  constexpr int E = D / 64;
-  float w0[E], w[E];
+__device__ __forceinline__ void pair_aty(const PairA<D>& A, const float (&y)[D / 32][4], float (&z)[D / 16]) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    float s = 0.f;
+  for (int tj = 0; tj < PairA<D>::NT; ++tj) {
+    float q = 0.f;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) s += sp.xpart[q][l + 64 * e];
-    w0[e] = s;
-    w[e] = s;
-  }
-  double alpha = 0.0;
+    for (int ti = 0; ti < PairA<D>::MT; ++ti)
 #pragma unroll
-  for (int kk = 0; kk < kLanczosK; ++kk) {
-    if (kk <= k) {
-      double part = 0.0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) part += static_cast<double>(w0[e]) * sp.vk[kk][l + 64 * e];
-      const double c = wave_sum_f64(part);
-      if (kk == k) alpha = c;
-      const float cf = static_cast<float>(c);
-#pragma unroll
-      for (int e = 0; e < E; ++e) w[e] -= cf * sp.vk[kk][l + 64 * e];
-    }
-  }
-  double n = 0.0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) n += static_cast<double>(w[e]) * w[e];
-  const double beta = sqrt(wave_sum_f64(n));
-  const float inv = beta > 0.0 ? static_cast<float>(1.0 / beta) : 0.f;
-#pragma unroll
-  for (int e = 0; e < E; ++e) sp.vk[k + 1][l + 64 * e] = w[e] * inv;
-  if (l == 0) {
-    sp.alpha[k] = alpha;
-    sp.beta[k] = beta;
+      for (int r = 0; r < 4; ++r) q += A.v[ti][tj][r] * y[ti][r];
+    q += __shfl_xor(q, 16);
+    q += __shfl_xor(q, 32);
+    z[tj] = q;
   }
 }
 
 // Number of eigenvalues below x of the tridiagonal (al, be): sign changes of
-// the Sturm sequence p_i = det(T_i - x I), evaluated without division.
-__device__ __forceinline__ int sturm_below(const double (&al)[kLanczosK], const double (&be)[kLanczosK], double x) {
-  double p0 = 1.0, p1 = al[0] - x;
-  int changes = p1 < 0.0 ? 1 : 0;
+// the Sturm sequence p_i = det(T_i - x I), evaluated without division. The
+// caller scales T so that its entries are at most 1 in magnitude, which keeps
+// every p_i far from the fp32 range limits for m <= 8.
+template <int m>
+__device__ __forceinline__ int sturm_below(const float (&al)[m], const float (&be)[m], float x) {
+  float p0 = 1.f, p1 = al[0] - x;
+  int changes = p1 < 0.f ? 1 : 0;
 #pragma unroll
-  for (int i = 1; i < kLanczosK; ++i) {
-    const double p2 = (al[i] - x) * p1 - be[i - 1] * be[i - 1] * p0;
-    changes += ((p2 < 0.0) != (p1 < 0.0)) ? 1 : 0;
+  for (int i = 1; i < m; ++i) {
+    const float p2 = (al[i] - x) * p1 - be[i - 1] * be[i - 1] * p0;
+    changes += ((p2 < 0.f) != (p1 < 0.f)) ? 1 : 0;
     p0 = p1;
     p1 = p2;
   }
   return changes;
 }
 
-// Bracket the m-th largest eigenvalue inside [lo, hi] by 64-point multisection.
-__device__ __forceinline__ void multisect(const double (&al)[kLanczosK], const double (&be)[kLanczosK], int m,
-                                          int rounds, double& lo, double& hi, int l) {
-  for (int r = 0; r < rounds; ++r) {
-    const double step = (hi - lo) / 65.0;
-    const double x = lo + step * (l + 1);
-    const bool above = kLanczosK - sturm_below(al, be, x) >= m;  // x still below theta_m
-    const int c = __builtin_popcountll(__ballot(above));
-    const double nlo = c > 0 ? lo + step * c : lo;
-    const double nhi = c < 64 ? lo + step * (c + 1) : hi;
+// Bracket the q-th largest eigenvalue inside [lo, hi] by 64-point multisection.
+template <int m>
+__device__ __forceinline__ void multisect(const float (&al)[m], const float (&be)[m], int q, int rounds,
+                                          float& lo, float& hi, int l) {
+  for (int rd = 0; rd < rounds; ++rd) {
+    const float step = (hi - lo) * (1.f / 65.f);
+    const float x = lo + step * static_cast<float>(l + 1);
+    const bool above = m - sturm_below<m>(al, be, x) >= q;  // x still below theta_q
+    const int cnt = __builtin_popcountll(__ballot(above));
+    const float nlo = cnt > 0 ? lo + step * static_cast<float>(cnt) : lo;
+    const float nhi = cnt < 64 ? lo + step * static_cast<float>(cnt + 1) : hi;
     lo = nlo;
     hi = nhi;
   }
 }
 
-// End of a cycle on wave 0: Ritz pair, convergence test, restart vector.
-template <int D>
-__device__ __forceinline__ void lanczos_restart(SpectralLds<D>& sp, int l, bool last) {
-  constexpr int K = kLanczosK, E = D / 64;
-  double al[K], be[K];
+// Ritz pair of the m-step tridiagonal of this wave: writes the (unnormalised)
+// Ritz vector to x and returns whether the residual bound is met. Computed in
+// fp32 on T / ||T|| (the Lanczos coefficients are fp32 quantities; M_j itself
+// is evaluated afterwards in fp64 from the vector).
+template <int m, int D>
+__device__ __forceinline__ bool ritz_step(const float* al_s, const float* be_s, const float (*basis)[D], int l,
+                                          int c, float (&x)[D / 16]) {
+  constexpr int NT = D / 16;
+  float al[m], be[m];
+  float lo = 0.f, hi = 0.f;
 #pragma unroll
-  for (int i = 0; i < K; ++i) {
-    al[i] = sp.alpha[i];
-    be[i] = sp.beta[i];
+  for (int i = 0; i < m; ++i) {
+    al[i] = al_s[i];
+    be[i] = be_s[i];
   }
-  double lo = al[0], hi = al[0];
 #pragma unroll
-  for (int i = 0; i < K; ++i) {
-    const double r = (i > 0 ? fabs(be[i - 1]) : 0.0) + (i < K - 1 ? fabs(be[i]) : 0.0);
-    lo = fmin(lo, al[i] - r);
-    hi = fmax(hi, al[i] + r);
+  for (int i = 0; i < m; ++i) {
+    const float rr = (i > 0 ? fabsf(be[i - 1]) : 0.f) + (i < m - 1 ? fabsf(be[i]) : 0.f);
+    lo = i == 0 ? al[0] - rr : fminf(lo, al[i] - rr);
+    hi = i == 0 ? al[0] + rr : fmaxf(hi, al[i] + rr);
   }
-  double lo1 = lo, hi1 = hi, lo2 = lo, hi2 = hi;
-  multisect(al, be, 1, 9, lo1, hi1, l);
-  multisect(al, be, 2, 5, lo2, hi2, l);
-  const double theta = 0.5 * (lo1 + hi1);
+  const float scale = fmaxf(fabsf(lo), fabsf(hi));
+  if (!(scale > 0.f)) {  // T == 0: the start vector is in the null space of A
+    load_vec<NT>(basis[0], c, x);
+    return true;
+  }
+  const float inv_scale = 1.f / scale;
+#pragma unroll
+  for (int i = 0; i < m; ++i) {
+    al[i] *= inv_scale;
+    be[i] *= inv_scale;
+  }
+  float lo1 = lo * inv_scale, hi1 = hi * inv_scale, lo2 = lo1, hi2 = hi1;
+  multisect<m>(al, be, 1, 4, lo1, hi1, l);
+  multisect<m>(al, be, 2, 3, lo2, hi2, l);
+  const float theta = 0.5f * (lo1 + hi1);
   // inverse iteration with (mu I - T), mu just above theta: positive definite
-  const double mu = theta + fmax(fabs(theta) * 1e-13, 1e-300);
-  double s[K];
+  const float mu = hi1 + fmaxf(fabsf(theta) * 1e-6f, 1e-30f);
+  float sv[m];
 #pragma unroll
-  for (int i = 0; i < K; ++i) s[i] = 1.0;
-  for (int pass = 0; pass < 2; ++pass) {
-    double cp[K], bp[K];
-    double den = mu - al[0];
-    den = fmax(den, 1e-300);
-    cp[0] = -be[0] / den;
-    bp[0] = s[0] / den;
+  for (int i = 0; i < m; ++i) sv[i] = 1.f;
 #pragma unroll
-    for (int i = 1; i < K; ++i) {
-      den = (mu - al[i]) + be[i - 1] * cp[i - 1];
-      den = fmax(den, 1e-300);
-      cp[i] = -be[i] / den;
-      bp[i] = (s[i] + be[i - 1] * bp[i - 1]) / den;
+  for (int pass = 0; pass < 3; ++pass) {
+    float cp[m], bp[m];
+    float rden = __builtin_amdgcn_rcpf(fmaxf(mu - al[0], 1e-30f));
+    cp[0] = -be[0] * rden;
+    bp[0] = sv[0] * rden;
+#pragma unroll
+    for (int i = 1; i < m; ++i) {
+      rden = __builtin_amdgcn_rcpf(fmaxf((mu - al[i]) + be[i - 1] * cp[i - 1], 1e-30f));
+      cp[i] = -be[i] * rden;
+      bp[i] = (sv[i] + be[i - 1] * bp[i - 1]) * rden;
     }
-    s[K - 1] = bp[K - 1];
+    sv[m - 1] = bp[m - 1];
 #pragma unroll
-    for (int i = K - 2; i >= 0; --i) s[i] = bp[i] - cp[i] * s[i + 1];
-    double n = 0.0;
+    for (int i = m - 2; i >= 0; --i) sv[i] = bp[i] - cp[i] * sv[i + 1];
+    float n = 0.f;
 #pragma unroll
-    for (int i = 0; i < K; ++i) n += s[i] * s[i];
-    const double inv = 1.0 / sqrt(n);
+    for (int i = 0; i < m; ++i) n += sv[i] * sv[i];
+    const float inv = __builtin_amdgcn_rsqf(n);
 #pragma unroll
-    for (int i = 0; i < K; ++i) s[i] *= inv;
+    for (int i = 0; i < m; ++i) sv[i] *= inv;
   }
-  const double res = fabs(be[K - 1] * s[K - 1]);
-  const double gap = theta - hi2;
-  const bool conv = res == 0.0 || (gap > 0.0 && theta > 0.0 && res * res < kLanczosTol * gap * theta);
-  float x[E];
-  double n = 0.0;
+  // residual ||A^T A x - theta x|| = |beta_m s_m|; everything in units of scale
+  const float res = fabsf(be[m - 1] * sv[m - 1]);
+  const float gap = theta - hi2;
+  const bool conv = res == 0.f || (gap > 0.f && theta > 0.f &&
+                                   static_cast<double>(res) * res < kLanczosTol * gap * theta);
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    float acc = 0.f;
+  for (int tj = 0; tj < NT; ++tj) x[tj] = 0.f;
 #pragma unroll
-    for (int i = 0; i < K; ++i) acc += static_cast<float>(s[i]) * sp.vk[i][l + 64 * e];
-    x[e] = acc;
-    n += static_cast<double>(acc) * acc;
+  for (int i = 0; i < m; ++i) {
+    float b[NT];
+    load_vec<NT>(basis[i], c, b);
+#pragma unroll
+    for (int tj = 0; tj < NT; ++tj) x[tj] += sv[i] * b[tj];
   }
-  n = wave_sum_f64(n);
-  const float inv = n > 0.0 ? static_cast<float>(1.0 / sqrt(n)) : 0.f;
+  return conv;
+}
+
+// Stage rows [row0, row0 + nvalid) transposed into LDS with the two waves.
+template <int D>
+__device__ __forceinline__ void pair_stage(const uint16_t* __restrict__ src, int row0, int nvalid,
+                                           uint16_t (*dst)[kLdT]) {
+  constexpr int DG = D / 8;
+  for (int item = threadIdx.x; item < 16 * DG; item += kPairThreads) {
+    const int tg = item / DG, dg = item % DG;
+    uint4 r[4];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    sp.xs[l + 64 * e] = x[e];
-    sp.vk[0][l + 64 * e] = x[e] * inv;
+    for (int q = 0; q < 4; ++q) {
+      const int tok = 4 * tg + q;
+      r[q] = tok < nvalid
+                 ? *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row0 + tok) * D + 8 * dg)
+                 : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w0 = half16(r[0], e) | (half16(r[1], e) << 16);
+      const uint32_t w1 = half16(r[2], e) | (half16(r[3], e) << 16);
+      *reinterpret_cast<uint2*>(&dst[8 * dg + e][4 * tg]) = make_uint2(w0, w1);
+    }
   }
-  if (l == 0) sp.flag = (conv || last) ? 1 : 0;
+}
+template <int D>
+__device__ __forceinline__ void pair_stage(const float* __restrict__ src, int row0, int nvalid,
+                                           float (*dst)[kLdT]) {
+  for (int e = threadIdx.x; e < kBlock * D; e += kPairThreads) {
+    const int tok = e / D, dim = e % D;
+    dst[dim][tok] = tok < nvalid ? src[static_cast<size_t>(row0 + tok) * D + dim] : 0.f;
+  }
+}
+
+// A += K_j^T V_j for this wave's rows.
+template <int D>
+__device__ __forceinline__ void pair_ktv(const PairLds<uint16_t, D>& s, PairA<D>& A, int w, int l) {
+  constexpr int MT = PairA<D>::MT, NT = PairA<D>::NT;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    bf16x8 a[MT];
+#pragma unroll
+    for (int ti = 0; ti < MT; ++ti)
+      a[ti] = *reinterpret_cast<const bf16x8*>(&s.u.tile.kt[16 * (MT * w + ti) + l % 16][32 * ks + 8 * (l / 16)]);
+#pragma unroll
+    for (int tj = 0; tj < NT; ++tj) {
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&s.u.tile.vt[16 * tj + l % 16][32 * ks + 8 * (l / 16)]);
+#pragma unroll
+      for (int ti = 0; ti < MT; ++ti) A.v[ti][tj] = mfma16x16x32(a[ti], b, A.v[ti][tj]);
+    }
+  }
+}
+template <int D>
+__device__ __forceinline__ void pair_ktv(const PairLds<float, D>& s, PairA<D>& A, int w, int l) {
+  const int g = l / 16, c = l % 16;
+#pragma unroll
+  for (int ti = 0; ti < PairA<D>::MT; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < PairA<D>::NT; ++tj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * (PairA<D>::MT * w + ti) + 4 * g + r, col = 16 * tj + c;
+        float sum = 0.f;
+#pragma unroll 4
+        for (int t = 0; t < kBlock; ++t) sum += s.u.tile.kt[row][t] * s.u.tile.vt[col][t];
+        A.v[ti][tj][r] += sum;
+      }
 }
 
 template <typename E, int D>
-__global__ __launch_bounds__(kThreads) void k_block_spectral(const E* __restrict__ K, const E* __restrict__ V,
-                                                             const float* __restrict__ kbar,
-                                                             const float* __restrict__ vsum,
-                                                             const float* __restrict__ Hbar,
-                                                             double* __restrict__ M, int L, int T, int G2) {
+__global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_block_spectral(const E* __restrict__ K, const E* __restrict__ V,
+                                                                 const float* __restrict__ kbar,
+                                                                 const float* __restrict__ vsum,
+                                                                 const float* __restrict__ hperm,
+                                                                 double* __restrict__ M, int L, int T) {
   extern __shared__ __align__(16) unsigned char smem[];
-  TileLds<E, D>& s = *reinterpret_cast<TileLds<E, D>*>(smem);
-  SpectralLds<D>& sp = *reinterpret_cast<SpectralLds<D>*>(smem + sizeof(TileLds<E, D>));
-  constexpr int MTW = HAcc<D>::MTW, NTT = HAcc<D>::NTT, NE = D / 64;
-  const int bh = blockIdx.y;
-  const int t = threadIdx.x, w = t / 64, l = t % 64;
-  const E* Kh = K + static_cast<size_t>(bh) * L * D;
-  const E* Vh = V + static_cast<size_t>(bh) * L * D;
+  PairLds<E, D>& s = *reinterpret_cast<PairLds<E, D>*>(smem);
+  constexpr int MT = PairA<D>::MT, NT = PairA<D>::NT;
+  const int j = blockIdx.x, bh = blockIdx.y;
+  const int t = threadIdx.x, w = t / 64, l = t % 64, g = l / 16, c = l % 16;
+  const int row0 = j * kBlock, nvalid = min(kBlock, L - row0);
 
-  HAcc<D> hb;  // Hbar in the accumulator layout
-  const float* Hh = Hbar + static_cast<size_t>(bh) * D * D;
+  // A starts as -Hbar (this lane's entries, 16-byte loads of the permuted copy)
+  PairA<D> A;
+  {
+    const f32x4* hp = reinterpret_cast<const f32x4*>(hperm + static_cast<size_t>(bh) * D * D) + (w * 64 + l) * MT * NT;
 #pragma unroll
-  for (int mi = 0; mi < MTW; ++mi)
+    for (int ti = 0; ti < MT; ++ti)
 #pragma unroll
-    for (int nt = 0; nt < NTT; ++nt)
+      for (int tj = 0; tj < NT; ++tj) A.v[ti][tj] = -hp[ti * NT + tj];
+  }
+  pair_stage<D>(K + static_cast<size_t>(bh) * L * D, row0, nvalid, s.u.tile.kt);
+  pair_stage<D>(V + static_cast<size_t>(bh) * L * D, row0, nvalid, s.u.tile.vt);
+  if (t < D) {
+    const size_t o = (static_cast<size_t>(bh) * T + j) * D + t;
+    s.kbar[t] = kbar[o];
+    s.vsum[t] = vsum[o];
+  }
+  __syncthreads();
+  // A = K_j^T V_j - kbar_j^T vsum_j - Hbar
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hb.v[mi][nt][r] = Hh[acc_row<D>(mi, r) * D + acc_col(nt)];
+  for (int ti = 0; ti < MT; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < NT; ++tj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        A.v[ti][tj][r] -= s.kbar[16 * (MT * w + ti) + 4 * g + r] * s.vsum[16 * tj + c];
+  pair_ktv<D>(s, A, w, l);
+  lds_barrier();  // the staged tiles are dead from here on (the basis reuses their LDS)
 
-  const int j0 = blockIdx.x * G2, j1 = min(T, j0 + G2);
-  for (int j = j0; j < j1; ++j) {
-    const int row0 = j * kBlock, nvalid = min(kBlock, L - row0);
-    __syncthreads();
-    stage_transposed<D>(Kh, row0, nvalid, s.kt);
-    stage_transposed<D>(Vh, row0, nvalid, s.vt);
-    if (t < D) {
-      const size_t o = (static_cast<size_t>(bh) * T + j) * D + t;
-      s.kbar[t] = kbar[o];
-      s.vsum[t] = vsum[o];
+  float(*basis)[D] = s.u.lz.basis[w];
+  int par = 0;
+  // z <- A^T A-like product: y = A x (if x given) then A^T y, summed over both waves
+  auto exchange = [&](float (&z)[NT]) {
+    if (g == 0) store_vec<NT>(s.u.lz.zx[par][w], c, z);
+    lds_barrier();
+    float z0[NT], z1[NT];
+    load_vec<NT>(s.u.lz.zx[par][0], c, z0);
+    load_vec<NT>(s.u.lz.zx[par][1], c, z1);
+#pragma unroll
+    for (int tj = 0; tj < NT; ++tj) z[tj] = z0[tj] + z1[tj];
+    par ^= 1;
+  };
+
+  // start vector x = A^T r for a fixed +-1 pattern r over the rows
+  float x[NT];
+  {
+    float y[MT][4];
+#pragma unroll
+    for (int ti = 0; ti < MT; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[ti][r] = start_sign(16 * (MT * w + ti) + 4 * g + r);
+    pair_aty<D>(A, y, x);
+    exchange(x);
+    // r in the null space of A^T: start from a fixed +-1 pattern over the columns
+    if (!(vdot<NT>(x, x) > 0.f)) {
+#pragma unroll
+      for (int tj = 0; tj < NT; ++tj) x[tj] = start_sign(D + 16 * tj + c);
     }
-    __syncthreads();
-    HAcc<D> A;
-#pragma unroll
-    for (int mi = 0; mi < MTW; ++mi)
-#pragma unroll
-      for (int nt = 0; nt < NTT; ++nt) A.v[mi][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accumulate_ktv<D>(s, A);
-    subtract_rank1(s, A);
-#pragma unroll
-    for (int mi = 0; mi < MTW; ++mi)
-#pragma unroll
-      for (int nt = 0; nt < NTT; ++nt) A.v[mi][nt] -= hb.v[mi][nt];
-
-    // start vector A^T r with a fixed +-1 pattern r over the rows
+  }
+  bool done = false;
+  for (int cyc = 0; cyc < kLanczosCycles && !done; ++cyc) {
+    float v[NT];
     {
-      float y[MTW][4];
+      const float n2 = vdot<NT>(x, x);
+      const float inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
 #pragma unroll
-      for (int mi = 0; mi < MTW; ++mi)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y[mi][r] = start_sign(acc_row<D>(mi, r));
-      write_col_partials<D>(A, y, sp);
+      for (int tj = 0; tj < NT; ++tj) v[tj] = x[tj] * inv;
     }
-    __syncthreads();
-    if (w == 0) {
-      float x[NE];
-      double n = 0.0;
-#pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        float sum = 0.f;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) sum += sp.xpart[q][l + 64 * e];
-        x[e] = sum;
-        n += static_cast<double>(sum) * sum;
+    if (g == 0) store_vec<NT>(basis[0], c, v);
+    for (int k = 0; k < kLanczosK; ++k) {
+      float z[NT];
+      {
+        float y[MT][4];
+        pair_ax<D>(A, v, y);
+        pair_aty<D>(A, y, z);
       }
-      n = wave_sum_f64(n);
-      const float inv = n > 0.0 ? static_cast<float>(1.0 / sqrt(n)) : 0.f;
+      exchange(z);
+      float wv[NT];
 #pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        sp.vk[0][l + 64 * e] = x[e] * inv;
-        sp.xs[l + 64 * e] = x[e];
-      }
-      if (l == 0) sp.flag = n > 0.0 ? 0 : 2;
-    }
-    __syncthreads();
-    const bool zero = sp.flag == 2;
-    if (!zero) {
-      for (int cyc = 0; cyc < kLanczosCycles; ++cyc) {
-        for (int k = 0; k < kLanczosK; ++k) {
-          apply_ata<D>(A, sp, k);
-          __syncthreads();
-          if (w == 0) lanczos_step<D>(sp, k, l);
-          __syncthreads();
+      for (int tj = 0; tj < NT; ++tj) wv[tj] = z[tj];
+      float alpha = 0.f;
+      for (int kk = 0; kk <= k; ++kk) {
+        float b[NT];
+        if (kk == k) {
+#pragma unroll
+          for (int tj = 0; tj < NT; ++tj) b[tj] = v[tj];
+        } else {
+          load_vec<NT>(basis[kk], c, b);
         }
-        if (w == 0) lanczos_restart<D>(sp, l, cyc == kLanczosCycles - 1);
-        __syncthreads();
-        if (sp.flag == 1) break;
+        const float cc = vdot<NT>(z, b);
+        if (kk == k) alpha = cc;
+#pragma unroll
+        for (int tj = 0; tj < NT; ++tj) wv[tj] -= cc * b[tj];
       }
-    }
-    // M_j = ||A x|| / ||x|| in fp64 from the fp32 Ritz vector.
-    double mval = 0.0;
-    if (!zero) {
-      float xc[NTT];
+      const float beta = sqrtf(vdot<NT>(wv, wv));
+      const float binv = beta > 0.f ? __builtin_amdgcn_rcpf(beta) : 0.f;
 #pragma unroll
-      for (int nt = 0; nt < NTT; ++nt) xc[nt] = sp.xs[acc_col(nt)];
-      double ysq = 0.0;
-#pragma unroll
-      for (int mi = 0; mi < MTW; ++mi)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          double p = 0.0;
-#pragma unroll
-          for (int nt = 0; nt < NTT; ++nt) p += static_cast<double>(A.v[mi][nt][r]) * xc[nt];
-          p = row_sum16(p);
-          ysq += p * p;
+      for (int tj = 0; tj < NT; ++tj) v[tj] = wv[tj] * binv;
+      if (g == 0) store_vec<NT>(basis[k + 1], c, v);
+      if (l == 0) {
+        s.al[w][k] = alpha;
+        s.be[w][k] = beta;
+      }
+      if (k + 1 == kLanczosCheck) {
+        if (ritz_step<kLanczosCheck, D>(s.al[w], s.be[w], basis, l, c, x)) {
+          done = true;
+          break;
         }
-      if (l % 16 == 0) sp.red2[t / 16] = ysq;
-      if (w == 0) {
-        double x2 = 0.0;
-#pragma unroll
-        for (int e = 0; e < NE; ++e) x2 += static_cast<double>(sp.xs[l + 64 * e]) * sp.xs[l + 64 * e];
-        x2 = wave_sum_f64(x2);
-        if (l == 0) sp.x2 = x2;
-      }
-      __syncthreads();
-      if (t == 0) {
-        double ys = 0.0;
-        for (int q = 0; q < 16; ++q) ys += sp.red2[q];
-        mval = sqrt(ys / sp.x2);
+      } else if (k + 1 == kLanczosK) {
+        done = ritz_step<kLanczosK, D>(s.al[w], s.be[w], basis, l, c, x);
       }
     }
-    if (t == 0) M[static_cast<size_t>(bh) * T + j] = mval;
+  }
+  // M_j = ||A x|| / ||x|| in fp64 from the fp32 Ritz vector.
+  double ysq = 0.0;
+#pragma unroll
+  for (int ti = 0; ti < MT; ++ti)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      double p = 0.0;
+#pragma unroll
+      for (int tj = 0; tj < NT; ++tj) p += static_cast<double>(A.v[ti][tj][r]) * x[tj];
+      p = row_sum16(p);
+      ysq += p * p;
+    }
+  double x2 = 0.0;
+#pragma unroll
+  for (int tj = 0; tj < NT; ++tj) x2 += static_cast<double>(x[tj]) * x[tj];
+  x2 = row_sum16(x2);
+  if (c == 0) s.red[w][g] = ysq;
+  lds_barrier();
+  if (t == 0) {
+    const double ys = ((s.red[0][0] + s.red[0][1]) + (s.red[0][2] + s.red[0][3])) +
+                      ((s.red[1][0] + s.red[1][1]) + (s.red[1][2] + s.red[1][3]));
+    M[static_cast<size_t>(bh) * T + j] = x2 > 0.0 ? sqrt(ys / x2) : 0.0;
   }
 }
 
@@ -579,7 +705,7 @@ hipError_t launch_typed(const paro_problem& p, const E* K, const E* V, float* kb
   int G = 1;
   const int nchunk = stats_chunks<E, D>(p, &G);
   const size_t lds1 = sizeof(TileLds<E, D>);
-  const size_t lds3 = sizeof(TileLds<E, D>) + sizeof(SpectralLds<D>);
+  const size_t lds3 = sizeof(PairLds<E, D>);
   hipError_t e;
   if (lds1 > 65536 && (e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_block_stats<E, D>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -589,15 +715,16 @@ hipError_t launch_typed(const paro_problem& p, const E* K, const E* V, float* kb
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                static_cast<int>(lds3))) != hipSuccess)
     return e;
+  float* partials = static_cast<float*>(ws);
+  float* hperm = partials + static_cast<size_t>(bh) * nchunk * D * D;
   hipLaunchKernelGGL((k_block_stats<E, D>), dim3(nchunk, bh), dim3(kThreads), lds1, st, K, V, kbar, vsum,
-                     static_cast<float*>(ws), p.L, T, G, nchunk);
+                     partials, p.L, T, G, nchunk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_hbar_reduce, dim3(ceil_div(D * D, 256), bh), dim3(256), 0, st,
-                     static_cast<const float*>(ws), Hbar, D * D, nchunk, T);
+  hipLaunchKernelGGL(k_hbar_reduce<D>, dim3(ceil_div(D * D, 256), bh), dim3(256), 0, st,
+                     static_cast<const float*>(partials), Hbar, hperm, nchunk, T);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int G2 = max(1, min(16, ceil_div(T * bh, 4096)));
-  hipLaunchKernelGGL((k_block_spectral<E, D>), dim3(ceil_div(T, G2), bh), dim3(kThreads), lds3, st, K, V, kbar,
-                     vsum, Hbar, M, p.L, T, G2);
+  hipLaunchKernelGGL((k_block_spectral<E, D>), dim3(T, bh), dim3(kPairThreads), lds3, st, K, V, kbar, vsum,
+                     static_cast<const float*>(hperm), M, p.L, T);
   return hipGetLastError();
 }
 
@@ -606,7 +733,8 @@ hipError_t launch_typed(const paro_problem& p, const E* K, const E* V, float* kb
 size_t precompute_workspace_bytes(const paro_problem& p) {
   int G = 1;
   const int nchunk = stats_chunks<float, 64>(p, &G);
-  return static_cast<size_t>(p.B) * p.H * nchunk * p.d * p.d * sizeof(float);
+  // per (b, h): nchunk partial H sums, then Hbar in PairA order
+  return static_cast<size_t>(p.B) * p.H * (nchunk + 1) * p.d * p.d * sizeof(float);
 }
 
 hipError_t launch_precompute(const paro_problem& p, const void* K, const void* V, float* kbar, float* vsum,
