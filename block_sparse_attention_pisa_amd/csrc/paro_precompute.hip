@@ -64,35 +64,57 @@ __device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
-// Stage rows [row0, row0 + nvalid) of a [L, D] bf16 matrix into dst[dim][token],
-// zero-filling tokens >= nvalid. Each item moves 4 tokens x 8 dims: four
-// 16-byte global loads (coalesced along d), eight 8-byte LDS writes.
+// Transposed staging of a 64 x D tile (rows [row0, row0 + nvalid) of a
+// [L, D] matrix) into dst[dim][token], tokens >= nvalid zero-filled. Item i
+// moves tokens 4 tg .. 4 tg + 3 (tg = i % 16) of dims 8 dg .. 8 dg + 7
+// (dg = i / 16): four 16-byte global loads, eight 8-byte LDS writes. The 16
+// lanes of a DPP row hold the 16 token groups of one dim group, so each LDS
+// write instruction fills whole 128-byte row segments, and the column sums
+// of the tile are one 16-lane reduction away.
 template <int D>
-__device__ __forceinline__ void stage_transposed(const uint16_t* __restrict__ src, int row0,
-                                                 int nvalid, uint16_t (*dst)[kLdT]) {
-  constexpr int DG = D / 8;
-  for (int item = threadIdx.x; item < 16 * DG; item += kThreads) {
-    const int tg = item / DG, dg = item % DG;
-    uint4 r[4];
+__device__ __forceinline__ void load_item(const uint16_t* __restrict__ src, int row0, int nvalid, int item,
+                                          uint4 (&r)[4]) {
+  const int tg = item % 16, dg = item / 16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int tok = 4 * tg + q;
-      r[q] = tok < nvalid
-                 ? *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row0 + tok) * D + 8 * dg)
-                 : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t w0 = half16(r[0], e) | (half16(r[1], e) << 16);
-      const uint32_t w1 = half16(r[2], e) | (half16(r[3], e) << 16);
-      *reinterpret_cast<uint2*>(&dst[8 * dg + e][4 * tg]) = make_uint2(w0, w1);
-    }
+  for (int q = 0; q < 4; ++q) {
+    const int tok = 4 * tg + q;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row0 + min(tok, nvalid - 1)) * D +
+                                                     8 * dg);
+    r[q] = tok < nvalid ? v : make_uint4(0, 0, 0, 0);
   }
 }
-template <int D>
+__device__ __forceinline__ void store_item(uint16_t (*dst)[kLdT], int item, const uint4 (&r)[4]) {
+  const int tg = item % 16, dg = item / 16;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t w0 = half16(r[0], e) | (half16(r[1], e) << 16);
+    const uint32_t w1 = half16(r[2], e) | (half16(r[3], e) << 16);
+    *reinterpret_cast<uint2*>(&dst[8 * dg + e][4 * tg]) = make_uint2(w0, w1);
+  }
+}
+// Sums over the 64 tokens of the item's 8 dims (valid in every lane of the row).
+__device__ __forceinline__ void item_colsum(const uint4 (&r)[4], float (&cs)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float s4 = (bf16_to_f32(half16(r[0], e)) + bf16_to_f32(half16(r[1], e))) +
+                     (bf16_to_f32(half16(r[2], e)) + bf16_to_f32(half16(r[3], e)));
+    cs[e] = row_sum16(s4);
+  }
+}
+
+template <int D, int NTHR>
+__device__ __forceinline__ void stage_transposed(const uint16_t* __restrict__ src, int row0, int nvalid,
+                                                 uint16_t (*dst)[kLdT]) {
+  for (int item = threadIdx.x; item < 2 * D; item += NTHR) {
+    uint4 r[4];
+    load_item<D>(src, row0, nvalid, item, r);
+    store_item(dst, item, r);
+  }
+}
+template <int D, int NTHR>
 __device__ __forceinline__ void stage_transposed(const float* __restrict__ src, int row0, int nvalid,
                                                  float (*dst)[kLdT]) {
-  for (int e = threadIdx.x; e < kBlock * D; e += kThreads) {
+  for (int e = threadIdx.x; e < kBlock * D; e += NTHR) {
     const int tok = e / D, dim = e % D;
     dst[dim][tok] = tok < nvalid ? src[static_cast<size_t>(row0 + tok) * D + dim] : 0.f;
   }
@@ -101,7 +123,7 @@ __device__ __forceinline__ void stage_transposed(const float* __restrict__ src, 
 __device__ __forceinline__ float tile_val(uint16_t x) { return bf16_to_f32(x); }
 __device__ __forceinline__ float tile_val(float x) { return x; }
 
-// Column sums of the staged tiles; writes s.kbar (mean over nvalid) and s.vsum.
+// Column sums of staged fp32 tiles; writes s.kbar (mean over nvalid) and s.vsum.
 template <typename E, int D>
 __device__ __forceinline__ void column_sums(TileLds<E, D>& s, int nvalid) {
   constexpr int P = kThreads / D;
@@ -176,6 +198,10 @@ __device__ __forceinline__ void subtract_rank1(const TileLds<E, D>& s, HAcc<D>& 
 }
 
 // ------------------------------------------------------------ kernel 1
+// One workgroup per chunk of G consecutive blocks of one (batch, head). For
+// bf16 the next block's K and V sit in registers (one staging item per
+// thread) while the current block is reduced, and the column sums come from
+// those registers; only LDS barriers separate the steps.
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void k_block_stats(const E* __restrict__ K, const E* __restrict__ V,
                                                           float* __restrict__ kbar, float* __restrict__ vsum,
@@ -191,20 +217,65 @@ __global__ __launch_bounds__(kThreads) void k_block_stats(const E* __restrict__ 
 #pragma unroll
     for (int nt = 0; nt < HAcc<D>::NTT; ++nt) acc.v[mi][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int j0 = c * G, j1 = min(T, j0 + G);
-  for (int j = j0; j < j1; ++j) {
-    const int row0 = j * kBlock, nvalid = min(kBlock, L - row0);
-    __syncthreads();
-    stage_transposed<D>(Kh, row0, nvalid, s.kt);
-    stage_transposed<D>(Vh, row0, nvalid, s.vt);
-    __syncthreads();
-    column_sums(s, nvalid);
-    if (threadIdx.x < D) {
-      const size_t o = (static_cast<size_t>(bh) * T + j) * D + threadIdx.x;
-      kbar[o] = s.kbar[threadIdx.x];
-      vsum[o] = s.vsum[threadIdx.x];
+  if constexpr (sizeof(E) == 2) {
+    static_assert(2 * D <= kThreads, "one staging item per thread");
+    const int item = threadIdx.x;
+    const bool has_item = item < 2 * D;
+    uint4 rk[4], rv[4];
+    if (has_item) {
+      load_item<D>(Kh, j0 * kBlock, min(kBlock, L - j0 * kBlock), item, rk);
+      load_item<D>(Vh, j0 * kBlock, min(kBlock, L - j0 * kBlock), item, rv);
     }
-    accumulate_ktv<D>(s, acc);
-    subtract_rank1(s, acc);
+    for (int j = j0; j < j1; ++j) {
+      const int row0 = j * kBlock, nvalid = min(kBlock, L - row0);
+      lds_barrier();  // the previous block's tiles have been consumed
+      if (has_item) {
+        store_item(s.kt, item, rk);
+        store_item(s.vt, item, rv);
+        float ks[8], vs[8];
+        item_colsum(rk, ks);
+        item_colsum(rv, vs);
+        if (item % 16 == 0) {
+          const int dg = item / 16;
+          const size_t o = (static_cast<size_t>(bh) * T + j) * D + 8 * dg;
+          const float fn = static_cast<float>(nvalid);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            ks[e] = ks[e] / fn;
+            s.kbar[8 * dg + e] = ks[e];
+            s.vsum[8 * dg + e] = vs[e];
+          }
+          *reinterpret_cast<f32x4*>(kbar + o) = f32x4{ks[0], ks[1], ks[2], ks[3]};
+          *reinterpret_cast<f32x4*>(kbar + o + 4) = f32x4{ks[4], ks[5], ks[6], ks[7]};
+          *reinterpret_cast<f32x4*>(vsum + o) = f32x4{vs[0], vs[1], vs[2], vs[3]};
+          *reinterpret_cast<f32x4*>(vsum + o + 4) = f32x4{vs[4], vs[5], vs[6], vs[7]};
+        }
+        if (j + 1 < j1) {
+          const int nr0 = row0 + kBlock, nv = min(kBlock, L - nr0);
+          load_item<D>(Kh, nr0, nv, item, rk);
+          load_item<D>(Vh, nr0, nv, item, rv);
+        }
+      }
+      lds_barrier();
+      accumulate_ktv<D>(s, acc);
+      subtract_rank1(s, acc);
+    }
+  } else {
+    for (int j = j0; j < j1; ++j) {
+      const int row0 = j * kBlock, nvalid = min(kBlock, L - row0);
+      __syncthreads();
+      stage_transposed<D, kThreads>(Kh, row0, nvalid, s.kt);
+      stage_transposed<D, kThreads>(Vh, row0, nvalid, s.vt);
+      __syncthreads();
+      column_sums(s, nvalid);
+      if (threadIdx.x < D) {
+        const size_t o = (static_cast<size_t>(bh) * T + j) * D + threadIdx.x;
+        kbar[o] = s.kbar[threadIdx.x];
+        vsum[o] = s.vsum[threadIdx.x];
+      }
+      accumulate_ktv<D>(s, acc);
+      subtract_rank1(s, acc);
+    }
   }
   float* out = ws + (static_cast<size_t>(bh) * nchunk + c) * D * D;
 #pragma unroll
@@ -471,38 +542,6 @@ __device__ __forceinline__ bool ritz_step(const float* al_s, const float* be_s, 
   return conv;
 }
 
-// Stage rows [row0, row0 + nvalid) transposed into LDS with the two waves.
-template <int D>
-__device__ __forceinline__ void pair_stage(const uint16_t* __restrict__ src, int row0, int nvalid,
-                                           uint16_t (*dst)[kLdT]) {
-  constexpr int DG = D / 8;
-  for (int item = threadIdx.x; item < 16 * DG; item += kPairThreads) {
-    const int tg = item / DG, dg = item % DG;
-    uint4 r[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int tok = 4 * tg + q;
-      r[q] = tok < nvalid
-                 ? *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row0 + tok) * D + 8 * dg)
-                 : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t w0 = half16(r[0], e) | (half16(r[1], e) << 16);
-      const uint32_t w1 = half16(r[2], e) | (half16(r[3], e) << 16);
-      *reinterpret_cast<uint2*>(&dst[8 * dg + e][4 * tg]) = make_uint2(w0, w1);
-    }
-  }
-}
-template <int D>
-__device__ __forceinline__ void pair_stage(const float* __restrict__ src, int row0, int nvalid,
-                                           float (*dst)[kLdT]) {
-  for (int e = threadIdx.x; e < kBlock * D; e += kPairThreads) {
-    const int tok = e / D, dim = e % D;
-    dst[dim][tok] = tok < nvalid ? src[static_cast<size_t>(row0 + tok) * D + dim] : 0.f;
-  }
-}
-
 // A += K_j^T V_j for this wave's rows.
 template <int D>
 __device__ __forceinline__ void pair_ktv(const PairLds<uint16_t, D>& s, PairA<D>& A, int w, int l) {
@@ -560,8 +599,8 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
       for (int tj = 0; tj < NT; ++tj) A.v[ti][tj] = -hp[ti * NT + tj];
   }
-  pair_stage<D>(K + static_cast<size_t>(bh) * L * D, row0, nvalid, s.u.tile.kt);
-  pair_stage<D>(V + static_cast<size_t>(bh) * L * D, row0, nvalid, s.u.tile.vt);
+  stage_transposed<D, kPairThreads>(K + static_cast<size_t>(bh) * L * D, row0, nvalid, s.u.tile.kt);
+  stage_transposed<D, kPairThreads>(V + static_cast<size_t>(bh) * L * D, row0, nvalid, s.u.tile.vt);
   if (t < D) {
     const size_t o = (static_cast<size_t>(bh) * T + j) * D + t;
     s.kbar[t] = kbar[o];

@@ -38,7 +38,8 @@
  *   validated on the host before anything is launched; on an error nothing
  *   is launched and no output is touched. The library never prints or aborts.
  *   NaN/Inf inputs are not detected.
-  * - Supported: block == 64; d in {64, 128}; 1 <= B, H; B*H <= 65535; 1 <= L; B*H*L*d < 2^31;
+ * - Supported: block == 64; d in {64, 128}; 1 <= B, H; B*H <= 65535; 1 <= L;
+ *   B*H*L*d < 2^31;
  *   T <= PARO_MAX_BLOCKS.
  */
 #ifndef PARO_H_
