@@ -46,7 +46,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kQB = 4;                    // query blocks per workgroup
 constexpr int kWaves = 2 * kQB;           // two 32-row waves per query block
 constexpr int kAttnThreads = 64 * kWaves;
-constexpr float kOverflowSlack = 64.f;    // log2 units above the reference max that trigger a rerun
 
 template <int D>
 struct Geo {
@@ -84,37 +83,72 @@ __device__ __forceinline__ uint4 to_bf16x8(const float4& a, const float4& b) {
 __device__ __forceinline__ float4 as_f4(const uint4& u) { return __builtin_bit_cast(float4, u); }
 
 // ------------------------------------------------------------ staging
+// Global loads are raw buffer loads: the buffer descriptor (base and size,
+// in scalar registers) is built per tile, so each thread's offsets inside a
+// tile are constants and rows past the end of the tensor read as zeros
+// (their keys are masked out; their values carry zero weight).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // One step's data in flight, NR registers of 16 bytes per thread:
 //  exact tile (bf16): r[0..KPT) = K chunks; r[VI..VI+2) = 2 keys x 8 dims of V;
 //  centroid chunk (fp32, 32 centroids): r[0..2 KCT) = kbar chunks as float4
 //  pairs; r[VI..VI+2) = 1 centroid x 8 dims of vsum.
 // V items put consecutive lanes on consecutive keys, so each LDS write
-// instruction fills whole V^T rows. Rows past the valid range re-read the last
-// valid row (finite values whose keys are masked out): no predicated loads.
+// instruction fills whole V^T rows.
 template <int D>
 struct Stage {
   uint4 r[Geo<D>::NR];
 };
 
+// Per-thread byte offsets of the staging loads inside a tile (constant).
 template <int D>
-__device__ __forceinline__ void load_exact(const uint16_t* __restrict__ Kh, const uint16_t* __restrict__ Vh,
-                                           int row0, int nvalid, Stage<D>& st) {
-  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT, VI = Geo<D>::VI;
+struct StageOffs {
+  uint32_t k[Geo<D>::KPT];   // K chunk i: row q / CG, chunk q % CG (q = tid + threads * i)
+  uint32_t v;                // V rows 2 kp, 2 kp + 1 (this one and + D * 2), dims 8 dg
+  uint32_t ck[Geo<D>::KCT];  // kbar chunk i (fp32 rows, 32 bytes)
+  uint32_t cv;               // vsum row kc, dims 8 dg (32 bytes)
+  __device__ __forceinline__ void init() {
+    constexpr int CG = Geo<D>::CG;
+    const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int q = threadIdx.x + kAttnThreads * i;
-    const int row = min(q / CG, nvalid - 1), c = q % CG;
-    st.r[i] = *reinterpret_cast<const uint4*>(Kh + static_cast<size_t>(row0 + row) * D + 8 * c);
-  }
-  // item: 32 key pairs (fast) x CG dim groups; with d = 64 the upper half of
-  // the threads repeats the lower half's loads and stores nothing
-  const int item = threadIdx.x % (32 * CG);
-  const int kp = item & 31, dg = item >> 5;
+    for (int i = 0; i < Geo<D>::KPT; ++i) {
+      const int q = tid + kAttnThreads * i;
+      k[i] = static_cast<uint32_t>((q / CG) * D * 2 + 16 * (q % CG));
+    }
+    const int item = tid % (32 * CG);
+    const int kp = item & 31, dg = item >> 5;
+    v = static_cast<uint32_t>(2 * kp * D * 2 + 16 * dg);
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int row = min(2 * kp + e, nvalid - 1);
-    st.r[VI + e] = *reinterpret_cast<const uint4*>(Vh + static_cast<size_t>(row0 + row) * D + 8 * dg);
+    for (int i = 0; i < Geo<D>::KCT; ++i) {
+      const int q = min(tid + kAttnThreads * i, 32 * CG - 1);
+      ck[i] = static_cast<uint32_t>((q / CG) * D * 4 + 32 * (q % CG));
+    }
+    cv = static_cast<uint32_t>(kp * D * 4 + 32 * dg);
   }
+};
+
+// Exact tile of kv-block j (uniform): K rows and V rows of the block.
+template <int D>
+__device__ __forceinline__ void load_exact(const uint16_t* __restrict__ Kh, const uint16_t* __restrict__ Vh, int j,
+                                           int L, const StageOffs<D>& of, Stage<D>& st) {
+  constexpr int KPT = Geo<D>::KPT, VI = Geo<D>::VI;
+  const uint32_t bytes = static_cast<uint32_t>(L - 64 * j) * D * 2;
+  const auto rk = make_rsrc(Kh + static_cast<size_t>(64 * j) * D, bytes);
+  const auto rv = make_rsrc(Vh + static_cast<size_t>(64 * j) * D, bytes);
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) st.r[i] = bload(rk, of.k[i]);
+  st.r[VI] = bload(rv, of.v);
+  st.r[VI + 1] = bload(rv, of.v + D * 2);
+}
+// Interleave the 16-bit elements e of two rows: low half from a, high from b.
+__device__ __forceinline__ uint32_t pair16(uint32_t a, uint32_t b, bool high) {
+  return __builtin_amdgcn_perm(b, a, high ? 0x07060302u : 0x05040100u);
 }
 template <int D>
 __device__ __forceinline__ void store_exact(const Stage<D>& st, uint16_t* buf) {
@@ -128,31 +162,30 @@ __device__ __forceinline__ void store_exact(const Stage<D>& st, uint16_t* buf) {
   if (threadIdx.x < 32 * CG) {
     const int item = threadIdx.x;
     const int kp = item & 31, dg = item >> 5;
+    const uint32_t a[4] = {st.r[VI].x, st.r[VI].y, st.r[VI].z, st.r[VI].w};
+    const uint32_t b[4] = {st.r[VI + 1].x, st.r[VI + 1].y, st.r[VI + 1].z, st.r[VI + 1].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<uint32_t*>(vt + (8 * dg + e) * VS + 2 * kp) =
-          half16(st.r[VI], e) | (half16(st.r[VI + 1], e) << 16);
+      *reinterpret_cast<uint32_t*>(vt + (8 * dg + e) * VS + 2 * kp) = pair16(a[e >> 1], b[e >> 1], e & 1);
   }
 }
-// Tail chunk of 32 centroids [j0, j0 + 32): kbar rows -> K tile rows 0..31,
-// vsum rows -> keys 0..31 of the V^T tile (fp32 converted to bf16 on store).
+// Tail chunk of 32 centroids [j0, j0 + 32) (j0 uniform): kbar rows -> K tile
+// rows 0..31, vsum rows -> keys 0..31 of the V^T tile (fp32 converted to bf16
+// on store).
 template <int D>
 __device__ __forceinline__ void load_centroids(const float* __restrict__ kb, const float* __restrict__ vs, int j0,
-                                               int T, Stage<D>& st) {
-  constexpr int CG = Geo<D>::CG, KCT = Geo<D>::KCT, VI = Geo<D>::VI;
+                                               int T, const StageOffs<D>& of, Stage<D>& st) {
+  constexpr int KCT = Geo<D>::KCT, VI = Geo<D>::VI;
+  const uint32_t bytes = static_cast<uint32_t>(T - j0) * D * 4;
+  const auto rk = make_rsrc(kb + static_cast<size_t>(j0) * D, bytes);
+  const auto rv = make_rsrc(vs + static_cast<size_t>(j0) * D, bytes);
 #pragma unroll
   for (int i = 0; i < KCT; ++i) {
-    const int q = min(static_cast<int>(threadIdx.x) + kAttnThreads * i, 32 * CG - 1);
-    const int row = min(j0 + q / CG, T - 1), c = q % CG;
-    const uint4* src = reinterpret_cast<const uint4*>(kb + static_cast<size_t>(row) * D + 8 * c);
-    st.r[2 * i] = src[0];
-    st.r[2 * i + 1] = src[1];
+    st.r[2 * i] = bload(rk, of.ck[i]);
+    st.r[2 * i + 1] = bload(rk, of.ck[i] + 16);
   }
-  const int item = threadIdx.x % (32 * CG);  // 32 centroids (fast) x CG dim groups
-  const int kc = item & 31, dg = item >> 5;
-  const uint4* src = reinterpret_cast<const uint4*>(vs + static_cast<size_t>(min(j0 + kc, T - 1)) * D + 8 * dg);
-  st.r[VI] = src[0];
-  st.r[VI + 1] = src[1];
+  st.r[VI] = bload(rv, of.cv);
+  st.r[VI + 1] = bload(rv, of.cv + 16);
 }
 template <int D>
 __device__ __forceinline__ void store_centroids(const Stage<D>& st, uint16_t* buf) {
@@ -180,11 +213,11 @@ template <int D>
 struct Acc {
   bf16x8 qb[Geo<D>::NK];   // B operand Q^T: query lane % 32 of the wave's rows, dims 16 s + 8 g .. + 8
   f32x16 o[Geo<D>::NU];    // O^T: dims 32 u + 8 (i / 4) + 4 g + i % 4, query lane % 32
-  float m;                 // reference max (log2 units), -inf until the first tile
-  float mtrue;             // exact running max, for a rerun
+  float m;                 // reference max (log2 units), -inf until the first tile with a valid key
+  float nm;                // -m
   float dsum;              // this lane's part of D
   float csum;              // this lane's part of c
-  bool over;               // some logit exceeded m + kOverflowSlack
+  bool over;               // some logit exceeded m + 64 (log2 units)
 };
 
 // S^T of 32 keys (kt: the lane's permuted K row and 8-dim half).
@@ -207,53 +240,69 @@ __device__ __forceinline__ void pv_half(const uint16_t* vt, const bf16x8 (&pb)[2
       a.o[u] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(vt + 32 * u * Geo<D>::VS + 16 * s), pb[s], a.o[u]);
 }
 
-// The lane's 16 keys of 32-key sub-tile t as a 16-bit mask of a 64-bit key mask.
-__device__ __forceinline__ uint32_t lane_bits(uint64_t km, int t, int g) {
-  return static_cast<uint32_t>((km >> (32 * t + 8 * g)) & 0xFFu) |
-         (static_cast<uint32_t>((km >> (32 * t + 16 + 8 * g)) & 0xFFu) << 8);
+// Lane predicate for accumulator register i of a 32-key S^T half: whether the
+// key the lane holds (16 (i / 8) + 8 g + i % 8, g = lane / 32) has its bit set
+// in the wave-uniform key mask km. Built as a scalar lane mask, so applying it
+// costs one v_cndmask per register.
+__device__ __forceinline__ bool key_bit(uint32_t km, int i) {
+  const int b0 = 16 * (i >> 3) + (i & 7);
+  const uint64_t lo = ((km >> b0) & 1u) ? 0x00000000FFFFFFFFull : 0ull;
+  const uint64_t hi = ((km >> (b0 + 8)) & 1u) ? 0xFFFFFFFF00000000ull : 0ull;
+  return __builtin_amdgcn_inverse_ballot_w64(lo | hi);
 }
 
-// Softmax weights of one 32-key sub-tile against the fixed reference max.
-// kMask: keys with a set bit in lmask get weight 0. kTail: D gains n_j p
-// (n_j = 64 except nlast for the key flagged in llast) and c gains p.
-template <int D, bool kMask, bool kTail>
-__device__ __forceinline__ void softmax_half(f32x16& s, Acc<D>& a, float cl2, uint32_t lmask, uint32_t llast,
-                                             float nlast, bf16x8 (&pb)[2]) {
+// Maximum logit (log2 units) of this lane's query over the 32 keys.
+__device__ __forceinline__ float half_max(const f32x16& s, float cl2) {
   float v = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (kMask && ((lmask >> i) & 1u)) s[i] = -INFINITY;
-    v = fmaxf(v, s[i]);
+  for (int i = 0; i < 16; ++i) v = fmaxf(v, s[i]);
+  return fmaxf(v, __shfl_xor(v, 32)) * cl2;
+}
+// The same with the keys of the wave-uniform mask km left out.
+__device__ __forceinline__ float half_max_masked(const f32x16& s, float cl2, uint32_t km) {
+  float v = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v = fmaxf(v, key_bit(km, i) ? -INFINITY : s[i]);
+  return fmaxf(v, __shfl_xor(v, 32)) * cl2;
+}
+
+// Softmax weights of one 32-key sub-tile against the fixed reference max
+// (no data-dependent branches); returns this lane's sum of the bf16-rounded
+// weights, which is also what the numerator sees.
+// kMask: keys whose bit is set in the wave-uniform mask km get weight 0.
+// kLast: pl receives the (bf16-rounded) weight of the key flagged in kl.
+// A weight of 2^64 or more (logits far above the reference) sets a.over.
+template <int D, bool kMask, bool kLast>
+__device__ __forceinline__ float softmax_half(f32x16& s, Acc<D>& a, float cl2, uint32_t km, uint32_t kl,
+                                              bf16x8 (&pb)[2], float& pl) {
+  if (kMask) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = key_bit(km, i) ? -INFINITY : s[i];
   }
-  v = fmaxf(v, __shfl_xor(v, 32)) * cl2;
-  a.mtrue = fmaxf(a.mtrue, v);
-  if (a.m == -INFINITY) a.m = v;
-  a.over = a.over || v > a.m + kOverflowSlack;
-  const float mref = a.m == -INFINITY ? 0.f : a.m;
   float pv[16];
-  float ps = 0.f, pl = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cl2, -mref));
-    pv[i] = p;
-    ps += p;
-    if (kTail) pl += ((llast >> i) & 1u) ? p : 0.f;
-  }
+  for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cl2, a.nm));
+  uint32_t w[8];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    uint4 w;
-    w.x = pack_bf16x2(pv[8 * c + 0], pv[8 * c + 1]);
-    w.y = pack_bf16x2(pv[8 * c + 2], pv[8 * c + 3]);
-    w.z = pack_bf16x2(pv[8 * c + 4], pv[8 * c + 5]);
-    w.w = pack_bf16x2(pv[8 * c + 6], pv[8 * c + 7]);
-    pb[c] = __builtin_bit_cast(bf16x8, w);
+  for (int c = 0; c < 8; ++c) w[c] = pack_bf16x2(pv[2 * c], pv[2 * c + 1]);
+  pb[0] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  pb[1] = __builtin_bit_cast(bf16x8, make_uint4(w[4], w[5], w[6], w[7]));
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[c]), ones, ps0, false);
+    ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[4 + c]), ones, ps1, false);
   }
-  if (kTail) {
-    a.dsum += 64.f * ps + (nlast - 64.f) * pl;
-    a.csum += ps;
-  } else {
-    a.dsum += ps;
+  const float ps = ps0 + ps1;
+  if (kLast) {
+    float x = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x += key_bit(kl, i) ? bf16_to_f32(f32_to_bf16(pv[i])) : 0.f;
+    pl = x;
   }
+  a.over = a.over || !(ps < 0x1p64f);
+  return ps;
 }
 
 template <int D>
@@ -300,8 +349,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       a.qb[ks] = __builtin_bit_cast(bf16x8, v);
     }
     a.m = -INFINITY;
-    a.mtrue = -INFINITY;
+    a.nm = 0.f;
   }
+  StageOffs<D> of;
+  of.init();
 
   // ---- membership masks of the 4 exact lists and their sorted union
   for (int e = tid; e < kQB * nw; e += kAttnThreads) masks[e] = 0u;
@@ -347,91 +398,169 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   for (int u = 0; u < Geo<D>::NU; ++u) a.o[u] = f32x16{};
   a.dsum = 0.f;
   a.csum = 0.f;
-  for (int pass = 0; pass < 2; ++pass) {
-    if (pass > 0 && active) {  // only rerunning waves start over; the others keep their sums
-#pragma unroll
-      for (int u = 0; u < Geo<D>::NU; ++u) a.o[u] = f32x16{};
-      a.dsum = 0.f;
-      a.csum = 0.f;
-    }
-    a.over = false;
 
-    // ---- stages 1 and 2 as one stream of steps: the nu exact tiles of the
-    // union, then the nch chunks of 32 centroids.
-    const int nsteps = nu + nch;
-    Stage<D> st;
-    auto fetch = [&](int step) {
-      if (step < nu) {
-        const int j = ulist[step];
-        load_exact<D>(Kh, Vh, 64 * j, j == T - 1 ? nlast : 64, st);
-      } else {
-        load_centroids<D>(kb, vs, 32 * (step - nu), T, st);
-      }
-    };
-    auto put = [&](int step, uint16_t* b) {
-      if (step < nu)
-        store_exact<D>(st, b);
-      else
-        store_centroids<D>(st, b);
-    };
-    if (nsteps > 0) {
-      fetch(0);
-      put(0, buf);
+  // One stream of staged steps: step 0 = centroid chunk 0 (it also sets the
+  // softmax reference), steps 1..nu = the exact tiles of the union, then
+  // centroid chunks 1..nch-1. Chunk c covers blocks [32 c, 32 c + 32).
+  const int nsteps = 1 + nu + (nch > 1 ? nch - 1 : 0);
+  Stage<D> st;
+  auto fetch = [&](int step) {
+    if (step >= 1 && step <= nu) {
+      const int j = __builtin_amdgcn_readfirstlane(ulist[step - 1]);
+      load_exact<D>(Kh, Vh, j, L, of, st);
+    } else {
+      load_centroids<D>(kb, vs, step == 0 ? 0 : 32 * (step - nu), T, of, st);
     }
+  };
+  auto put = [&](int step, uint16_t* b) {
+    if (step >= 1 && step <= nu)
+      store_exact<D>(st, b);
+    else
+      store_centroids<D>(st, b);
+  };
+  auto advance = [&](int step) {
+    if (step + 1 < nsteps) put(step + 1, buf + ((step + 1) & 1) * BUF);
+    if (step + 2 < nsteps) fetch(step + 2);
+    lds_barrier();
+  };
+  auto start = [&]() {
+    fetch(0);
+    put(0, buf);
     lds_barrier();
     if (nsteps > 1) fetch(1);
-    // Three loops over consecutive step ranges, one compute variant each:
-    // full exact tiles, then the partial last block (always last in the
-    // ascending union), then the centroid chunks.
-    const int nfull = (nu > 0 && ulist[nu - 1] == T - 1 && nlast < 64) ? nu - 1 : nu;
-    auto advance = [&](int step) {
-      if (step + 1 < nsteps) put(step + 1, buf + ((step + 1) & 1) * BUF);
-      if (step + 2 < nsteps) fetch(step + 2);
-      lds_barrier();
-    };
-    for (int step = 0; step < nfull; ++step) {
+  };
+  auto mine_tile = [&](int step) {
+    const int j = ulist[step - 1];
+    return active && ((mymask[j >> 5] >> (j & 31)) & 1u);
+  };
+  // keys of centroid chunk c left out of the tail: the blocks of S_i (this
+  // wave's membership word c) and blocks >= T
+  auto chunk_mask = [&](int c) {
+    uint32_t km = __builtin_amdgcn_readfirstlane(mymask[c]);
+    const int left = T - 32 * c;
+    if (left < 32) km |= ~0u << left;
+    return km;
+  };
+  const uint32_t past_T0 = T < 32 ? ~0u << T : 0u;  // keys of chunk 0 at blocks >= T
+  const uint64_t past_nlast = ~0ull << nlast;        // keys past the end of the last block
+  // exact tiles 1..nfull are full blocks; a partial last block is always last
+  const int nfull = (nu > 0 && ulist[nu - 1] == T - 1 && nlast < 64) ? nu - 1 : nu;
+
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass > 0) {
+      // A wave whose logits outgrew the reference by 2^64 or more: find the
+      // exact maximum of everything it weighs (exact keys, and centroids,
+      // which never exceed the keys of their own block), then start over.
+      float mx = -INFINITY;
+      start();
+      for (int step = 0; step < nsteps; ++step) {
+        const uint16_t* bc = buf + (step & 1) * BUF;
+        if (step >= 1 && step <= nu) {
+          if (mine_tile(step)) {
+            const uint64_t km = step > nfull ? past_nlast : 0ull;
+            const f32x16 s0 = qk_half<D>(bc + koff, a);
+            const f32x16 s1 = qk_half<D>(bc + koff + 32 * KS, a);
+            mx = fmaxf(mx, fmaxf(half_max_masked(s0, cl2, static_cast<uint32_t>(km)),
+                                 half_max_masked(s1, cl2, static_cast<uint32_t>(km >> 32))));
+          }
+        } else if (active) {
+          const int c = step == 0 ? 0 : step - nu;
+          const f32x16 s0 = qk_half<D>(bc + koff, a);
+          const int left = T - 32 * c;
+          mx = fmaxf(mx, half_max_masked(s0, cl2, left < 32 ? ~0u << left : 0u));
+        }
+        advance(step);
+      }
+      if (active) {
+        a.m = mx;
+        a.nm = -mx;
+#pragma unroll
+        for (int u = 0; u < Geo<D>::NU; ++u) a.o[u] = f32x16{};
+        a.dsum = 0.f;
+        a.csum = 0.f;
+      }
+    }
+    a.over = false;
+    start();
+    float pl = 0.f;
+    // ---- step 0: centroid chunk 0
+    {
+      if (active) {
+        f32x16 s0 = qk_half<D>(buf + koff, a);
+        if (pass == 0) {
+          // reference: the largest centroid logit of the chunk; a centroid
+          // logit is the mean of its block's key logits, so the reference
+          // never exceeds the largest logit that carries weight
+          const float v = half_max_masked(s0, cl2, past_T0);
+          a.m = v;
+          a.nm = -v;
+        }
+        if (nch > 0) {
+          bf16x8 p0[2];
+          const float ps = softmax_half<D, true, true>(s0, a, cl2, chunk_mask(0), nch == 1 ? 1u << (T - 1) : 0u,
+                                                       p0, pl);
+          pv_half<D>(buf + voff, p0, a);
+          a.dsum += 64.f * ps + (static_cast<float>(nlast) - 64.f) * pl;
+          a.csum += ps;
+        }
+      }
+      advance(0);
+    }
+    // ---- exact tiles: full blocks, then the partial last block
+    for (int step = 1; step <= nfull; ++step) {
       const uint16_t* bc = buf + (step & 1) * BUF;
-      const int j = ulist[step];
-      if (active && ((mymask[j >> 5] >> (j & 31)) & 1u)) {
+      if (mine_tile(step)) {
         f32x16 s0 = qk_half<D>(bc + koff, a);
         f32x16 s1 = qk_half<D>(bc + koff + 32 * KS, a);
         bf16x8 p0[2], p1[2];
-        softmax_half<D, false, false>(s0, a, cl2, 0u, 0u, 0.f, p0);
+        float ps = softmax_half<D, false, false>(s0, a, cl2, 0u, 0u, p0, pl);
         pv_half<D>(bc + voff, p0, a);
-        softmax_half<D, false, false>(s1, a, cl2, 0u, 0u, 0.f, p1);
+        ps += softmax_half<D, false, false>(s1, a, cl2, 0u, 0u, p1, pl);
         pv_half<D>(bc + voff + 32, p1, a);
+        a.dsum += ps;
       }
       advance(step);
     }
-    for (int step = nfull; step < nu; ++step) {
+    for (int step = nfull + 1; step <= nu; ++step) {
       const uint16_t* bc = buf + (step & 1) * BUF;
-      const int j = ulist[step];
-      if (active && ((mymask[j >> 5] >> (j & 31)) & 1u)) {
-        const uint64_t km = ~0ull << nlast;
+      if (mine_tile(step)) {
         f32x16 s0 = qk_half<D>(bc + koff, a);
         f32x16 s1 = qk_half<D>(bc + koff + 32 * KS, a);
         bf16x8 p0[2], p1[2];
-        softmax_half<D, true, false>(s0, a, cl2, lane_bits(km, 0, g), 0u, 0.f, p0);
+        float ps = softmax_half<D, true, false>(s0, a, cl2, static_cast<uint32_t>(past_nlast), 0u, p0, pl);
         pv_half<D>(bc + voff, p0, a);
-        softmax_half<D, true, false>(s1, a, cl2, lane_bits(km, 1, g), 0u, 0.f, p1);
+        ps += softmax_half<D, true, false>(s1, a, cl2, static_cast<uint32_t>(past_nlast >> 32), 0u, p1, pl);
         pv_half<D>(bc + voff + 32, p1, a);
+        a.dsum += ps;
       }
       advance(step);
     }
-    for (int step = nu; step < nsteps; ++step) {
+    // ---- centroid chunks 1..nch-2, then the last chunk (block T - 1 with its
+    // weight n_{T-1})
+    for (int step = nu + 1; step < nsteps - 1; ++step) {
       const uint16_t* bc = buf + (step & 1) * BUF;
       if (active) {
-        const int j0 = 32 * (step - nu);
-        uint64_t km = 0xFFFFFFFF00000000ull | ((j0 >> 5) < nw ? mymask[j0 >> 5] : 0xFFFFFFFFu);
-        if (j0 + 32 > T) km |= ~0ull << (T - j0);
-        const int lk = T - 1 - j0;  // chunk-local index of the last (partial) block, if present
-        const uint64_t kl = (lk >= 0 && lk < 32) ? (1ull << lk) : 0ull;
         f32x16 s0 = qk_half<D>(bc + koff, a);
         bf16x8 p0[2];
-        softmax_half<D, true, true>(s0, a, cl2, lane_bits(km, 0, g), lane_bits(kl, 0, g), static_cast<float>(nlast), p0);
+        const float ps = softmax_half<D, true, false>(s0, a, cl2, chunk_mask(step - nu), 0u, p0, pl);
         pv_half<D>(bc + voff, p0, a);
+        a.dsum += 64.f * ps;
+        a.csum += ps;
       }
       advance(step);
+    }
+    if (nch > 1) {
+      const int step = nsteps - 1, c = nch - 1;
+      const uint16_t* bc = buf + (step & 1) * BUF;
+      if (active) {
+        f32x16 s0 = qk_half<D>(bc + koff, a);
+        bf16x8 p0[2];
+        const float ps = softmax_half<D, true, true>(s0, a, cl2, chunk_mask(c), 1u << (T - 1 - 32 * c), p0, pl);
+        pv_half<D>(bc + voff, p0, a);
+        a.dsum += 64.f * ps + (static_cast<float>(nlast) - 64.f) * pl;
+        a.csum += ps;
+      }
+      lds_barrier();
     }
 
     // ---- rerun the rows whose logits outgrew their reference max
@@ -444,7 +573,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     lds_barrier();
     if (!any) break;
     active = mine;
-    if (mine) a.m = a.mtrue;
   }
 
   // ---- stage 3: global first-order correction, then N / D
