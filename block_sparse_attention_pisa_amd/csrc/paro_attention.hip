@@ -305,6 +305,84 @@ __device__ __forceinline__ float softmax_half(f32x16& s, Acc<D>& a, float cl2, u
   return ps;
 }
 
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
+
+// One exact tile (64 keys) for this wave's 32 queries: S^T = K Q^T for both
+// 32-key halves, the weights of each half, O^T += V^T P^T. Written as a
+// software pipeline so the matrix cores and the vector ALU overlap inside
+// the wave: the K operands of half 1 load during the MFMAs of half 0, the
+// softmax of half 0 runs between the MFMAs of half 1, the softmax of half 1
+// between the P V MFMAs of half 0, and every V operand is read one phase
+// ahead. kMask: the uniform 64-bit key mask km zeroes keys (partial block).
+// Returns this lane's sum of the weights.
+template <int D, bool kMask>
+__device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int voff, Acc<D>& a, float cl2,
+                                            uint64_t km) {
+  constexpr int NK = Geo<D>::NK, NU = Geo<D>::NU, KS = Geo<D>::KS, VS = Geo<D>::VS;
+  constexpr int NV = 2 * NU;
+  constexpr int kValu = kMask ? 68 : 52;  // VALU instructions of one softmax half (approximate)
+  const uint16_t* kp = bc + koff;
+  const uint16_t* vp = bc + voff;
+  bf16x8 k0[NK], k1[NK], v0[NV], v1[NV];
+  // region 1: K operands of half 0
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) k0[ks] = *reinterpret_cast<const bf16x8*>(kp + 16 * ks);
+  __builtin_amdgcn_sched_barrier(0);
+  // region 2: S^T half 0 | K operands of half 1
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) k1[ks] = *reinterpret_cast<const bf16x8*>(kp + 32 * KS + 16 * ks);
+  f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) s0 = mfma32x32x16(k0[ks], a.qb[ks], s0);
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // region 3: S^T half 1 | softmax of half 0 | V operands of half 0
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) v0[2 * u + h] = *reinterpret_cast<const bf16x8*>(vp + 32 * u * VS + 16 * h);
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) s1 = mfma32x32x16(k1[ks], a.qb[ks], s1);
+  float pl = 0.f;
+  bf16x8 p0[2], p1[2];
+  float ps = softmax_half<D, kMask, false>(s0, a, cl2, static_cast<uint32_t>(km), 0u, p0, pl);
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, (kValu + NK - 1) / NK, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, (NV + NK - 1) / NK, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // region 4: P V half 0 | softmax of half 1 | V operands of half 1
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) v1[2 * u + h] = *reinterpret_cast<const bf16x8*>(vp + 32 + 32 * u * VS + 16 * h);
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) a.o[u] = mfma32x32x16(v0[2 * u + h], p0[h], a.o[u]);
+  ps += softmax_half<D, kMask, false>(s1, a, cl2, static_cast<uint32_t>(km >> 32), 0u, p1, pl);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, (kValu + NV - 1) / NV, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // region 5: P V half 1
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) a.o[u] = mfma32x32x16(v1[2 * u + h], p1[h], a.o[u]);
+  return ps;
+}
+
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -509,30 +587,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     // ---- exact tiles: full blocks, then the partial last block
     for (int step = 1; step <= nfull; ++step) {
       const uint16_t* bc = buf + (step & 1) * BUF;
-      if (mine_tile(step)) {
-        f32x16 s0 = qk_half<D>(bc + koff, a);
-        f32x16 s1 = qk_half<D>(bc + koff + 32 * KS, a);
-        bf16x8 p0[2], p1[2];
-        float ps = softmax_half<D, false, false>(s0, a, cl2, 0u, 0u, p0, pl);
-        pv_half<D>(bc + voff, p0, a);
-        ps += softmax_half<D, false, false>(s1, a, cl2, 0u, 0u, p1, pl);
-        pv_half<D>(bc + voff + 32, p1, a);
-        a.dsum += ps;
-      }
+      if (mine_tile(step)) a.dsum += exact_tile<D, false>(bc, koff, voff, a, cl2, 0ull);
       advance(step);
     }
     for (int step = nfull + 1; step <= nu; ++step) {
       const uint16_t* bc = buf + (step & 1) * BUF;
-      if (mine_tile(step)) {
-        f32x16 s0 = qk_half<D>(bc + koff, a);
-        f32x16 s1 = qk_half<D>(bc + koff + 32 * KS, a);
-        bf16x8 p0[2], p1[2];
-        float ps = softmax_half<D, true, false>(s0, a, cl2, static_cast<uint32_t>(past_nlast), 0u, p0, pl);
-        pv_half<D>(bc + voff, p0, a);
-        ps += softmax_half<D, true, false>(s1, a, cl2, static_cast<uint32_t>(past_nlast >> 32), 0u, p1, pl);
-        pv_half<D>(bc + voff + 32, p1, a);
-        a.dsum += ps;
-      }
+      if (mine_tile(step)) a.dsum += exact_tile<D, true>(bc, koff, voff, a, cl2, past_nlast);
       advance(step);
     }
     // ---- centroid chunks 1..nch-2, then the last chunk (block T - 1 with its
