@@ -9,6 +9,8 @@ the kv-blocks exact). Prints one JSON line:
   roofline   the attention kernel against the bf16 MFMA peak, from its
              algorithmic FLOPs (exact blocks + zeroth-order terms of U_i +
              correction) over its mean launch time measured with HIP events
+  exact_phase   the same attention kernel on the all-exact (keep = 100%)
+                control of the long-video shape, against the bf16 MFMA peak
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -38,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video720p_75600")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-exact-phase", action="store_true",
+                    help="skip the all-exact control run that isolates the exact phase")
     ap.add_argument("--cpu-qblocks", type=int, default=48, help="query blocks per head in the oracle sample")
     ap.add_argument("--cpu-heads", type=int, default=1)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -70,6 +74,35 @@ def attention_flops(w, idx_cpu) -> float:
         corr = 2.0 * d * d * L if w.k < T else 0.0
         total += exact + tail + corr
     return total
+
+
+def exact_phase_entry(reps: int = 3):
+    """The exact phase alone: the same attention kernel on the keep = 100% control
+    of the long-video shape (every kv-block exact, no tail, no correction), so
+    every MFMA is stage-1 work. FLOPs 4 d sum_i n_i L per head."""
+    import torch
+    from block_sparse_attention_pisa_amd import paro
+    from workloads import WORKLOADS, make_inputs
+    w = WORKLOADS["video_long_118800_dense"]
+    q, k, v = make_inputs(w)
+    qd, kd, vd = (x.to("cuda:0") for x in (q, k, v))
+    del q, k, v
+    stats = paro.precompute(kd, vd)
+    idx = paro.route(qd, stats[0], stats[3], w.k, w.lam)
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+    paro.attention(qd, kd, vd, *stats[:3], idx, w.k, out=out)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        paro.attention(qd, kd, vd, *stats[:3], idx, w.k, out=out)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    flops = 4.0 * w.B * w.H * w.L * w.L * w.d
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "keep_k": w.k, "T": w.T, "ms": round(ms, 3), "achieved": round(tf, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
 def traffic_entry():
@@ -223,6 +256,10 @@ def main():
         },
         "input_generation_s": round(t_gen, 1),
     }
+    if not a.no_exact_phase:
+        del qd, kd, vd, stats, idx, out
+        torch.cuda.empty_cache()
+        res["exact_phase"] = exact_phase_entry()
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, a.cpu_qblocks, a.cpu_heads)
     print(json.dumps(res), flush=True)
