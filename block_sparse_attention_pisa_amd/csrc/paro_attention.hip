@@ -43,6 +43,7 @@ namespace paro {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kQB = 4;                    // query blocks per workgroup
 constexpr int kWaves = 2 * kQB;           // two 32-row waves per query block
 constexpr int kAttnThreads = 64 * kWaves;
@@ -50,13 +51,13 @@ constexpr int kAttnThreads = 64 * kWaves;
 template <int D>
 struct Geo {
   static constexpr int CG = D / 8;                         // 16-byte chunks in a K row
-  static constexpr int KS = D + 8;                         // K tile row stride (elements)
+  static constexpr int KS = D + 24;                        // K tile row stride: D dims, 16 reference dims, pad
   static constexpr int VS = 64 + 8;                        // V^T tile row stride
   static constexpr int HS = D + 8;                         // Hbar^T row stride
   static constexpr int KTILE = 64 * KS;
   static constexpr int VTILE = D * VS;
   static constexpr int BUF = KTILE + VTILE;                // one staging buffer (elements)
-  static constexpr int NK = D / 16;                        // k-steps of S^T = K Q^T
+  static constexpr int NK = D / 16;                        // k-steps of S^T = K Q^T over the D dims
   static constexpr int NU = D / 32;                        // 32-dim output tiles
   static constexpr int KPT = 64 * CG / kAttnThreads;       // exact-tile K chunks staged per thread
   static constexpr int KCT = (32 * CG + kAttnThreads - 1) / kAttnThreads;  // centroid K chunks per thread
@@ -211,23 +212,25 @@ __device__ __forceinline__ void store_centroids(const Stage<D>& st, uint16_t* bu
 // ------------------------------------------------------------ compute
 template <int D>
 struct Acc {
-  bf16x8 qb[Geo<D>::NK];   // B operand Q^T: query lane % 32 of the wave's rows, dims 16 s + 8 g .. + 8
+  bf16x8 qb[Geo<D>::NK];   // B operand (scale log2(e) Q)^T in bf16: query lane % 32, dims 16 s + 8 g .. + 8
+  bf16x8 qx;               // B operand of the reference k-step: -m of the lane's query (half 0 lanes, element 0)
   f32x16 o[Geo<D>::NU];    // O^T: dims 32 u + 8 (i / 4) + 4 g + i % 4, query lane % 32
-  float m;                 // reference max (log2 units), -inf until the first tile with a valid key
-  float nm;                // -m
+  float m;                 // softmax reference (log2 units); the logits S^T come out as logit - m
   float dsum;              // this lane's part of D
   float csum;              // this lane's part of c
   bool over;               // some logit exceeded m + 64 (log2 units)
 };
 
-// S^T of 32 keys (kt: the lane's permuted K row and 8-dim half).
+// S^T of 32 keys (kt: the lane's permuted K row and 8-dim half), in log2
+// units relative to the reference: scale log2(e) q.k - m.
 template <int D>
 __device__ __forceinline__ f32x16 qk_half(const uint16_t* kt, const Acc<D>& a) {
   f32x16 s = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < Geo<D>::NK; ++ks)
     s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kt + 16 * ks), a.qb[ks], s);
-  return s;
+  // reference k-step: K columns D.. hold (1, 0, ..), Q^T rows D.. hold (-m, 0, ..)
+  return mfma32x32x16(*reinterpret_cast<const bf16x8*>(kt + 16 * Geo<D>::NK), a.qx, s);
 }
 
 // O^T += V^T P^T for 32 keys (vt: the lane's V^T row base plus the key offset).
@@ -251,29 +254,31 @@ __device__ __forceinline__ bool key_bit(uint32_t km, int i) {
   return __builtin_amdgcn_inverse_ballot_w64(lo | hi);
 }
 
-// Maximum logit (log2 units) of this lane's query over the 32 keys.
-__device__ __forceinline__ float half_max(const f32x16& s, float cl2) {
-  float v = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v = fmaxf(v, s[i]);
-  return fmaxf(v, __shfl_xor(v, 32)) * cl2;
-}
-// The same with the keys of the wave-uniform mask km left out.
-__device__ __forceinline__ float half_max_masked(const f32x16& s, float cl2, uint32_t km) {
+// Maximum of S^T for this lane's query over the 32 keys, leaving out the
+// keys of the wave-uniform mask km.
+__device__ __forceinline__ float half_max_masked(const f32x16& s, uint32_t km) {
   float v = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) v = fmaxf(v, key_bit(km, i) ? -INFINITY : s[i]);
-  return fmaxf(v, __shfl_xor(v, 32)) * cl2;
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+// Sets the softmax reference m (log2 units) of this lane's query.
+template <int D>
+__device__ __forceinline__ void set_reference(Acc<D>& a, float m) {
+  a.m = m;
+  const uint32_t w0 = (threadIdx.x & 32) ? 0u : static_cast<uint32_t>(f32_to_bf16(-m));
+  a.qx = __builtin_bit_cast(bf16x8, make_uint4(w0, 0u, 0u, 0u));
 }
 
-// Softmax weights of one 32-key sub-tile against the fixed reference max
-// (no data-dependent branches); returns this lane's sum of the bf16-rounded
-// weights, which is also what the numerator sees.
+// Softmax weights exp2(S^T) of one 32-key sub-tile (the reference is already
+// subtracted by the MFMA; kShift adds shift first), with no data-dependent
+// branches; returns this lane's sum of the bf16-rounded weights, which is
+// also what the numerator sees.
 // kMask: keys whose bit is set in the wave-uniform mask km get weight 0.
 // kLast: pl receives the (bf16-rounded) weight of the key flagged in kl.
 // A weight of 2^64 or more (logits far above the reference) sets a.over.
-template <int D, bool kMask, bool kLast>
-__device__ __forceinline__ float softmax_half(f32x16& s, Acc<D>& a, float cl2, uint32_t km, uint32_t kl,
+template <int D, bool kMask, bool kLast, bool kShift = false>
+__device__ __forceinline__ float softmax_half(f32x16& s, Acc<D>& a, float shift, uint32_t km, uint32_t kl,
                                               bf16x8 (&pb)[2], float& pl) {
   if (kMask) {
 #pragma unroll
@@ -281,7 +286,7 @@ __device__ __forceinline__ float softmax_half(f32x16& s, Acc<D>& a, float cl2, u
   }
   float pv[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], cl2, a.nm));
+  for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(kShift ? s[i] + shift : s[i]);
   uint32_t w[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) w[c] = pack_bf16x2(pv[2 * c], pv[2 * c + 1]);
@@ -317,26 +322,27 @@ constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
 // ahead. kMask: the uniform 64-bit key mask km zeroes keys (partial block).
 // Returns this lane's sum of the weights.
 template <int D, bool kMask>
-__device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int voff, Acc<D>& a, float cl2,
-                                            uint64_t km) {
+__device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int voff, Acc<D>& a, uint64_t km) {
   constexpr int NK = Geo<D>::NK, NU = Geo<D>::NU, KS = Geo<D>::KS, VS = Geo<D>::VS;
   constexpr int NV = 2 * NU;
-  constexpr int kValu = kMask ? 68 : 52;  // VALU instructions of one softmax half (approximate)
+  constexpr int kValu = kMask ? 52 : 36;  // VALU instructions of one softmax half (approximate)
   const uint16_t* kp = bc + koff;
   const uint16_t* vp = bc + voff;
-  bf16x8 k0[NK], k1[NK], v0[NV], v1[NV];
+  constexpr int NKX = NK + 1;  // the D dims plus the reference k-step
+  bf16x8 k0[NKX], k1[NKX], v0[NV], v1[NV];
+  auto qop = [&](int ks) { return ks < NK ? a.qb[ks] : a.qx; };
   // region 1: K operands of half 0
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) k0[ks] = *reinterpret_cast<const bf16x8*>(kp + 16 * ks);
+  for (int ks = 0; ks < NKX; ++ks) k0[ks] = *reinterpret_cast<const bf16x8*>(kp + 16 * ks);
   __builtin_amdgcn_sched_barrier(0);
   // region 2: S^T half 0 | K operands of half 1
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) k1[ks] = *reinterpret_cast<const bf16x8*>(kp + 32 * KS + 16 * ks);
+  for (int ks = 0; ks < NKX; ++ks) k1[ks] = *reinterpret_cast<const bf16x8*>(kp + 32 * KS + 16 * ks);
   f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) s0 = mfma32x32x16(k0[ks], a.qb[ks], s0);
+  for (int ks = 0; ks < NKX; ++ks) s0 = mfma32x32x16(k0[ks], qop(ks), s0);
 #pragma unroll
-  for (int i = 0; i < NK; ++i) {
+  for (int i = 0; i < NKX; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
     __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
   }
@@ -347,15 +353,15 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
 #pragma unroll
     for (int h = 0; h < 2; ++h) v0[2 * u + h] = *reinterpret_cast<const bf16x8*>(vp + 32 * u * VS + 16 * h);
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) s1 = mfma32x32x16(k1[ks], a.qb[ks], s1);
+  for (int ks = 0; ks < NKX; ++ks) s1 = mfma32x32x16(k1[ks], qop(ks), s1);
   float pl = 0.f;
   bf16x8 p0[2], p1[2];
-  float ps = softmax_half<D, kMask, false>(s0, a, cl2, static_cast<uint32_t>(km), 0u, p0, pl);
+  float ps = softmax_half<D, kMask, false>(s0, a, 0.f, static_cast<uint32_t>(km), 0u, p0, pl);
 #pragma unroll
-  for (int i = 0; i < NK; ++i) {
+  for (int i = 0; i < NKX; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgValu, (kValu + NK - 1) / NK, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, (NV + NK - 1) / NK, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, (kValu + NKX - 1) / NKX, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, (NV + NKX - 1) / NKX, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
   // region 4: P V half 0 | softmax of half 1 | V operands of half 1
@@ -367,7 +373,7 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
   for (int u = 0; u < NU; ++u)
 #pragma unroll
     for (int h = 0; h < 2; ++h) a.o[u] = mfma32x32x16(v0[2 * u + h], p0[h], a.o[u]);
-  ps += softmax_half<D, kMask, false>(s1, a, cl2, static_cast<uint32_t>(km >> 32), 0u, p1, pl);
+  ps += softmax_half<D, kMask, false>(s1, a, 0.f, static_cast<uint32_t>(km >> 32), 0u, p1, pl);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
@@ -424,10 +430,20 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
 #pragma unroll
     for (int ks = 0; ks < Geo<D>::NK; ++ks) {
       const uint4 v = (qvalid && row < L) ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
-      a.qb[ks] = __builtin_bit_cast(bf16x8, v);
+      const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+      uint32_t y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        y[e] = pack_bf16x2(bf16_to_f32(static_cast<uint16_t>(x[e])) * cl2, bf16_to_f32(static_cast<uint16_t>(x[e] >> 16)) * cl2);
+      a.qb[ks] = __builtin_bit_cast(bf16x8, make_uint4(y[0], y[1], y[2], y[3]));
     }
-    a.m = -INFINITY;
-    a.nm = 0.f;
+    set_reference(a, 0.f);
+  }
+  // reference columns of the K tiles (both buffers): key row . (1, 0, .., 0)
+  for (int e = tid; e < 2 * 64; e += kAttnThreads) {
+    uint16_t* kr = buf + (e / 64) * BUF + (e % 64) * KS + D;
+    *reinterpret_cast<uint4*>(kr) = make_uint4(0x3F80u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(kr + 8) = make_uint4(0u, 0u, 0u, 0u);
   }
   StageOffs<D> of;
   of.init();
@@ -538,20 +554,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
             const uint64_t km = step > nfull ? past_nlast : 0ull;
             const f32x16 s0 = qk_half<D>(bc + koff, a);
             const f32x16 s1 = qk_half<D>(bc + koff + 32 * KS, a);
-            mx = fmaxf(mx, fmaxf(half_max_masked(s0, cl2, static_cast<uint32_t>(km)),
-                                 half_max_masked(s1, cl2, static_cast<uint32_t>(km >> 32))));
+            mx = fmaxf(mx, fmaxf(half_max_masked(s0, static_cast<uint32_t>(km)),
+                                 half_max_masked(s1, static_cast<uint32_t>(km >> 32))));
           }
         } else if (active) {
           const int c = step == 0 ? 0 : step - nu;
           const f32x16 s0 = qk_half<D>(bc + koff, a);
           const int left = T - 32 * c;
-          mx = fmaxf(mx, half_max_masked(s0, cl2, left < 32 ? ~0u << left : 0u));
+          mx = fmaxf(mx, half_max_masked(s0, left < 32 ? ~0u << left : 0u));
         }
         advance(step);
       }
       if (active) {
-        a.m = mx;
-        a.nm = -mx;
+        set_reference(a, a.m + mx);  // mx is relative to the current reference
 #pragma unroll
         for (int u = 0; u < Geo<D>::NU; ++u) a.o[u] = f32x16{};
         a.dsum = 0.f;
@@ -565,18 +580,20 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     {
       if (active) {
         f32x16 s0 = qk_half<D>(buf + koff, a);
+        float shift = 0.f;
         if (pass == 0) {
-          // reference: the largest centroid logit of the chunk; a centroid
-          // logit is the mean of its block's key logits, so the reference
-          // never exceeds the largest logit that carries weight
-          const float v = half_max_masked(s0, cl2, past_T0);
-          a.m = v;
-          a.nm = -v;
+          // reference: the largest centroid logit of the chunk (computed with
+          // the reference 0); a centroid logit is the mean of its block's key
+          // logits, so the reference never exceeds the largest logit that
+          // carries weight
+          const float v = half_max_masked(s0, past_T0);
+          set_reference(a, v);
+          shift = -v;
         }
         if (nch > 0) {
           bf16x8 p0[2];
-          const float ps = softmax_half<D, true, true>(s0, a, cl2, chunk_mask(0), nch == 1 ? 1u << (T - 1) : 0u,
-                                                       p0, pl);
+          const float ps = softmax_half<D, true, true, true>(s0, a, shift, chunk_mask(0),
+                                                             nch == 1 ? 1u << (T - 1) : 0u, p0, pl);
           pv_half<D>(buf + voff, p0, a);
           a.dsum += 64.f * ps + (static_cast<float>(nlast) - 64.f) * pl;
           a.csum += ps;
@@ -587,12 +604,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     // ---- exact tiles: full blocks, then the partial last block
     for (int step = 1; step <= nfull; ++step) {
       const uint16_t* bc = buf + (step & 1) * BUF;
-      if (mine_tile(step)) a.dsum += exact_tile<D, false>(bc, koff, voff, a, cl2, 0ull);
+      if (mine_tile(step)) a.dsum += exact_tile<D, false>(bc, koff, voff, a, 0ull);
       advance(step);
     }
     for (int step = nfull + 1; step <= nu; ++step) {
       const uint16_t* bc = buf + (step & 1) * BUF;
-      if (mine_tile(step)) a.dsum += exact_tile<D, true>(bc, koff, voff, a, cl2, past_nlast);
+      if (mine_tile(step)) a.dsum += exact_tile<D, true>(bc, koff, voff, a, past_nlast);
       advance(step);
     }
     // ---- centroid chunks 1..nch-2, then the last chunk (block T - 1 with its
@@ -602,7 +619,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       if (active) {
         f32x16 s0 = qk_half<D>(bc + koff, a);
         bf16x8 p0[2];
-        const float ps = softmax_half<D, true, false>(s0, a, cl2, chunk_mask(step - nu), 0u, p0, pl);
+        const float ps = softmax_half<D, true, false>(s0, a, 0.f, chunk_mask(step - nu), 0u, p0, pl);
         pv_half<D>(bc + voff, p0, a);
         a.dsum += 64.f * ps;
         a.csum += ps;
@@ -615,7 +632,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       if (active) {
         f32x16 s0 = qk_half<D>(bc + koff, a);
         bf16x8 p0[2];
-        const float ps = softmax_half<D, true, true>(s0, a, cl2, chunk_mask(c), 1u << (T - 1 - 32 * c), p0, pl);
+        const float ps = softmax_half<D, true, true>(s0, a, 0.f, chunk_mask(c), 1u << (T - 1 - 32 * c), p0, pl);
         pv_half<D>(bc + voff, p0, a);
         a.dsum += 64.f * ps + (static_cast<float>(nlast) - 64.f) * pl;
         a.csum += ps;
@@ -671,7 +688,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
 #pragma unroll
         for (int ks = 0; ks < Geo<D>::NK; ++ks)
           r = mfma32x32x16(*reinterpret_cast<const bf16x8*>(hrow + 32 * u * HS + 16 * ks), a.qb[ks], r);
-        o += (scale * csum) * r;
+        o += (kLn2 * csum) * r;  // r = Hbar^T (scale log2(e) q): scale c Hbar^T q = ln2 c r
       }
       if (row < L) {
 #pragma unroll
