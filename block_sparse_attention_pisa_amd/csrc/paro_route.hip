@@ -3,16 +3,24 @@
 // routing"): score_ij = scale * qbar_i . kbar_j + lambda * M_j, and S_i is the
 // set of the keep_k best-scoring kv-blocks of query block i.
 //
-// One workgroup (4 waves) handles R consecutive query blocks of one
-// (batch, head):
-//   1. qbar_i in fp64 from the valid query rows (Q streamed once);
-//   2. all T scores of the R rows in fp64 (exact products of fp64 qbar and
-//      fp32 kbar), kept in LDS;
-//   3. per row, one wave finds the keep_k-th largest score by an MSB-first
-//      radix select over order-preserving 64-bit keys (8 passes of 8 bits,
-//      LDS histogram), then writes the winners in ascending j with a
-//      ballot / mbcnt compaction. Exact ties go to the lower j, so the result
-//      is a deterministic integer function of the scores.
+// One workgroup (kWaves waves) handles R <= 16 consecutive query blocks of
+// one (batch, head):
+//   1. qbar_i: each wave sums the valid query rows of its blocks in fp64
+//      (one pass over Q, cross-lane reduction by shuffles) and stores qbar in
+//      fp32;
+//   2. the dot products qbar_i . kbar_j of all R rows and T centroids on fp32
+//      MFMA 16x16x4 (R rows are the 16 rows of the MFMA tile), kept in LDS as
+//      fp32. Their error (~1e-7) is far below the 1e-5 score gaps that decide
+//      routing;
+//   3. per row, one wave forms the fp64 scores scale * dot + lambda * M_j,
+//      maps them onto order-preserving 64-bit keys held in registers, and
+//      finds the keep_k-th largest key bit by bit, from the highest bit where
+//      the row's keys differ down, counting matches with wave ballots (no LDS
+//      traffic, no atomics); it stops as soon as the keys that agree with the
+//      prefix found so far are exactly the ones still needed. The winners are
+//      written in ascending j with a ballot / mbcnt compaction. Exact ties go
+//      to the lower j, so the result is a deterministic integer function of
+//      the scores.
 #include <algorithm>
 
 #include "paro_common.h"
@@ -20,35 +28,63 @@
 namespace paro {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMaxRows = 8;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxRows = 16;   // query blocks per workgroup = rows of the 16x16 MFMA tile
+constexpr int kMaxKeyRegs = 32;  // keys per lane kept in registers: rows of T <= 2048 never re-read LDS
 constexpr size_t kLdsBudget = 152 * 1024;
 
 // Order-preserving map of a double onto uint64 (larger score -> larger key);
-// -0.0 is folded onto +0.0 first so equal scores give equal keys.
+// -0.0 is folded onto +0.0 first so equal scores give equal keys. Finite
+// scores never map to 0.
 __device__ __forceinline__ uint64_t score_key(double s) {
   s = s + 0.0;
   const uint64_t u = __builtin_bit_cast(uint64_t, s);
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
-  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+__device__ __forceinline__ double shfl_xor_f64(double v, int m) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(u), m);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(u >> 32), m);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-template <typename E, int D>
-__global__ __launch_bounds__(kThreads) void k_route(const E* __restrict__ Q, const float* __restrict__ kbar,
+__device__ __forceinline__ int lanes_below(uint64_t bal) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
+}
+
+__device__ __forceinline__ int count_lanes(bool p) { return __builtin_popcountll(__ballot(p)); }
+
+// acc[e] += element e of a 16-byte piece of a row (8 bf16 or 4 fp32 values)
+template <typename E>
+__device__ __forceinline__ void add_piece(double* acc, uint4 raw);
+template <>
+__device__ __forceinline__ void add_piece<uint16_t>(double* acc, uint4 raw) {
+  const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    acc[2 * h] += __uint_as_float(u[h] << 16);
+    acc[2 * h + 1] += __uint_as_float(u[h] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void add_piece<float>(double* acc, uint4 raw) {
+  acc[0] += __uint_as_float(raw.x);
+  acc[1] += __uint_as_float(raw.y);
+  acc[2] += __uint_as_float(raw.z);
+  acc[3] += __uint_as_float(raw.w);
+}
+
+template <typename E, int D, int NI>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_route(const E* __restrict__ Q, const float* __restrict__ kbar,
                                                     const double* __restrict__ M, int32_t* __restrict__ idx,
                                                     int L, int T, int R, int keep_k, double scale,
                                                     double lambda) {
   extern __shared__ __align__(16) unsigned char smem[];
-  double* qbar = reinterpret_cast<double*>(smem);                      // [D][R]
-  uint32_t* hist = reinterpret_cast<uint32_t*>(qbar + D * kMaxRows);    // [4][256]
-  double* score = reinterpret_cast<double*>(hist + 4 * 256);            // [R][T]
-  double* qred = score;  // qbar partials [2 * rows per sweep][D], used before any score exists
+  float* qs = reinterpret_cast<float*>(smem);    // qbar [R][D]; dead once the MFMA operands are loaded
+  float* dots = reinterpret_cast<float*>(smem);  // [R][T], written after qs is dead
 
   const int bh = blockIdx.y;
   const int i0 = blockIdx.x * R;
@@ -58,214 +94,215 @@ __global__ __launch_bounds__(kThreads) void k_route(const E* __restrict__ Q, con
   const float* kb = kbar + static_cast<size_t>(bh) * T * D;
   const double* Mh = M + static_cast<size_t>(bh) * T;
 
-  // 1. qbar (fp64 sums of the valid rows). Thread t reads 16-byte pieces of
-  //    rows t / G, t / G + 256 / G, ... at dim group t % G (G pieces per row);
-  //    the loads of two query blocks are in flight together.
-  constexpr int EPL = 16 / sizeof(E);  // elements per 16-byte piece
-  constexpr int G = D / EPL;           // pieces per row
-  constexpr int RS = kThreads / G;     // rows covered per sweep
-  constexpr int SW = kBlock / RS;      // sweeps per block
-  const int dg = t % G, ro = t / G;
-  for (int r0 = 0; r0 < nrows; r0 += 2) {
-    uint4 raw[2][SW];
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int r = r0 + rr;
-      const int row0 = (i0 + r) * kBlock, nvalid = r < nrows ? min(kBlock, L - row0) : 0;
-#pragma unroll
-      for (int sw = 0; sw < SW; ++sw) {
-        const int tok = ro + RS * sw;
-        raw[rr][sw] = tok < nvalid
-                          ? *reinterpret_cast<const uint4*>(Qh + static_cast<size_t>(row0 + tok) * D + EPL * dg)
-                          : make_uint4(0, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
+  // 1. qbar. Lane l reads the 16-byte piece dg = l % G of rows rg, rg + RG,
+  //    ... (rg = l / G) of the block, sums them in fp64, and the RG lanes of
+  //    one piece are then reduced by shuffles.
+  {
+    constexpr int EPL = 16 / sizeof(E);  // elements per 16-byte piece
+    constexpr int G = D / EPL;           // pieces per row
+    constexpr int RG = 64 / G;           // rows read together by one load instruction
+    constexpr int NL = kBlock / RG;      // loads per lane per block
+    constexpr int CH = NL < 8 ? NL : 8;  // loads kept in flight together
+    const int dg = l % G, rg = l / G;
+    for (int r = w; r < nrows; r += kWaves) {
+      const int row0 = (i0 + r) * kBlock, nvalid = min(kBlock, L - row0);
+      const E* base = Qh + static_cast<size_t>(row0) * D + EPL * dg;
       double acc[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[e] = 0.0;
-#pragma unroll
-      for (int sw = 0; sw < SW; ++sw) {
-        const E* x = reinterpret_cast<const E*>(&raw[rr][sw]);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += load_elem<E>(x + e);
-      }
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) qred[(rr * RS + ro) * D + EPL * dg + e] = acc[e];
-    }
-    __syncthreads();
-    for (int e = t; e < 2 * D; e += kThreads) {
-      const int rr = e / D, a = e % D, r = r0 + rr;
-      if (r < nrows) {
-        const int row0 = (i0 + r) * kBlock, nvalid = min(kBlock, L - row0);
-        double sum = 0.0;
-        for (int p = 0; p < RS; ++p) sum += qred[(rr * RS + p) * D + a];
-        qbar[a * kMaxRows + r] = sum / nvalid;
-      }
-    }
-    __syncthreads();
-  }
-
-  // 2. scores: each thread handles centroids j and j + 256 together, with
-  //    8 loads of 16 bytes per centroid in flight; qbar is read as LDS broadcasts.
-  for (int ja = t; ja < T; ja += 2 * kThreads) {
-    const int jb = ja + kThreads;
-    const bool okb = jb < T;
-    double acc_a[kMaxRows], acc_b[kMaxRows];
-#pragma unroll
-    for (int r = 0; r < kMaxRows; ++r) {
-      acc_a[r] = 0.0;
-      acc_b[r] = 0.0;
-    }
-    const float4* rowa = reinterpret_cast<const float4*>(kb + static_cast<size_t>(ja) * D);
-    const float4* rowb = reinterpret_cast<const float4*>(kb + static_cast<size_t>(okb ? jb : ja) * D);
 #pragma unroll 1
-    for (int a0 = 0; a0 < D / 4; a0 += 8) {
-      float4 ka[8], kc[8];
+      for (int s0 = 0; s0 < NL; s0 += CH) {
+        uint4 raw[CH];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        ka[u] = rowa[a0 + u];
-        kc[u] = rowb[a0 + u];
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep the 16 loads in flight together
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float xa[4] = {ka[u].x, ka[u].y, ka[u].z, ka[u].w};
-        const float xb[4] = {kc[u].x, kc[u].y, kc[u].z, kc[u].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const double* qa = qbar + (4 * (a0 + u) + e) * kMaxRows;
-#pragma unroll
-          for (int r = 0; r < kMaxRows; ++r) {
-            acc_a[r] += qa[r] * static_cast<double>(xa[e]);
-            acc_b[r] += qa[r] * static_cast<double>(xb[e]);
-          }
+        for (int s = 0; s < CH; ++s) {
+          const int tok = rg + RG * (s0 + s);
+          raw[s] = tok < nvalid ? *reinterpret_cast<const uint4*>(base + static_cast<size_t>(tok) * D)
+                                : make_uint4(0, 0, 0, 0);
         }
+#pragma unroll
+        for (int s = 0; s < CH; ++s) add_piece<E>(acc, raw[s]);
+      }
+#pragma unroll
+      for (int o = G; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += shfl_xor_f64(acc[e], o);
+      if (rg == 0) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qs[r * D + EPL * dg + e] = static_cast<float>(acc[e] / nvalid);
       }
     }
-    const double lma = lambda * Mh[ja];
-    const double lmb = okb ? lambda * Mh[jb] : 0.0;
+  }
+  __syncthreads();
+
+  // 2. dots. Lane l = 16 g + n16 supplies A = qbar[n16][.] and B =
+  //    kbar[16 c + n16][.]; k-step 4 q + u of a lane of group g uses dim
+  //    16 q + 4 g + u, so every lane reads whole float4s and the four groups
+  //    of one row read 64 contiguous bytes per load. The C layout gives lane l
+  //    the dots of rows 4 g .. 4 g + 3 with centroid 16 c + n16. Rows
+  //    n16 >= nrows are zero. Wave w takes centroid blocks c = w, w + kWaves, ...
+  {
+    constexpr int NQ = D / 16;
+    const int g = l / 16, n16 = l % 16;
+    float qa[4 * NQ];
 #pragma unroll
-    for (int r = 0; r < kMaxRows; ++r) {
-      if (r < nrows) {
-        score[static_cast<size_t>(r) * T + ja] = scale * acc_a[r] + lma;
-        if (okb) score[static_cast<size_t>(r) * T + jb] = scale * acc_b[r] + lmb;
+    for (int q = 0; q < NQ; ++q) {
+      const float4 x = n16 < nrows ? *reinterpret_cast<const float4*>(qs + n16 * D + 16 * q + 4 * g)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      qa[4 * q] = x.x;
+      qa[4 * q + 1] = x.y;
+      qa[4 * q + 2] = x.z;
+      qa[4 * q + 3] = x.w;
+    }
+    __syncthreads();  // qs is overwritten by the dots from here on
+    const int nblk = ceil_div(T, 16);
+    for (int c = w; c < nblk; c += kWaves) {
+      const int n = 16 * c + n16;
+      const float4* kr = reinterpret_cast<const float4*>(kb + static_cast<size_t>(min(n, T - 1)) * D) + g;
+      float kv[4 * NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const float4 x = kr[4 * q];
+        kv[4 * q] = x.x;
+        kv[4 * q + 1] = x.y;
+        kv[4 * q + 2] = x.z;
+        kv[4 * q + 3] = x.w;
+      }
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4 * NQ; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[ks], kv[ks], acc, 0, 0, 0);
+      if (n < T) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g + i;
+          if (r < nrows) dots[r * T + n] = acc[i];
+        }
       }
     }
   }
   __syncthreads();
 
   // 3. selection, one wave per row
-  uint32_t* h = hist + 256 * w;
-  for (int r = w; r < nrows; r += 4) {
-    const double* sc = score + static_cast<size_t>(r) * T;
+  // Lane l keeps the keys of j = l + 64 i, i < NI, in registers (NI * 64 >= T
+  // unless T > 64 * kMaxKeyRegs); keys from tail0 on are re-formed from LDS
+  // whenever they are needed. Padding keys (j >= T) are 0, which no finite
+  // score maps to and no prefix test below matches.
+  constexpr int tail0 = 64 * NI;
+  for (int r = w; r < nrows; r += kWaves) {
+    const float* dr = dots + r * T;
     int32_t* out = idx + (static_cast<size_t>(bh) * T + i0 + r) * keep_k;
-    // Radix select over the digits below the common prefix of the row's keys:
-    // keys are order-preserving images of the scores, so the first digits of
-    // a row usually agree and would all hit one histogram bin.
-    uint64_t kmin = ~0ull, kmax = 0ull;
-    for (int j = l; j < T; j += 64) {
-      const uint64_t key = score_key(sc[j]);
-      kmin = key < kmin ? key : kmin;
-      kmax = key > kmax ? key : kmax;
+    if (keep_k >= T) {
+      for (int j = l; j < T; j += 64) out[j] = j;
+      continue;
     }
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint64_t a0 = shfl_xor_u64(kmin, o), a1 = shfl_xor_u64(kmax, o);
-      kmin = a0 < kmin ? a0 : kmin;
-      kmax = a1 > kmax ? a1 : kmax;
-    }
-    int top = kmin == kmax ? -8 : (63 - __builtin_clzll(kmin ^ kmax)) / 8 * 8;  // digit holding the top differing bit
-    uint64_t mask = top + 8 >= 64 ? 0ull : ~((1ull << (top + 8)) - 1);
-    uint64_t prefix = kmax & mask;
-    int remaining = keep_k;  // how many keys equal to prefix (on the mask bits) are still needed
-    if (keep_k < T) {
-      for (int shift = top; shift >= 0; shift -= 8) {
-        for (int b = l; b < 256; b += 64) h[b] = 0;
-        __builtin_amdgcn_wave_barrier();
-        for (int j = l; j < T; j += 64) {
-          const uint64_t key = score_key(sc[j]);
-          if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
-        }
-        __builtin_amdgcn_wave_barrier();
-        // lane l owns digits 4l..4l+3
-        uint32_t c[4];
-        for (int e = 0; e < 4; ++e) c[e] = h[4 * l + e];
-        const uint32_t mine = c[0] + c[1] + c[2] + c[3];
-        // exclusive suffix sum over lanes: digits held by lanes above l
-        uint32_t incl = mine;
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t v = __shfl_down(incl, o);
-          if (l + o < 64) incl += v;
-        }
-        const uint32_t above = incl - mine;
-        int found = -1;
-        uint32_t cum = above, binc = 0;
-        int newrem = 0;
-        for (int e = 3; e >= 0; --e) {
-          if (found < 0 && cum < static_cast<uint32_t>(remaining) && cum + c[e] >= static_cast<uint32_t>(remaining)) {
-            found = 4 * l + e;
-            newrem = remaining - static_cast<int>(cum);
-            binc = c[e];
-          }
-          cum += c[e];
-        }
-        const uint64_t bal = ballot64(found >= 0);
-        const int src = __builtin_ctzll(bal);
-        const int digit = __shfl(found, src);
-        remaining = __shfl(newrem, src);
-        const int bin_count = __shfl(static_cast<int>(binc), src);
-        prefix |= static_cast<uint64_t>(digit) << shift;
-        mask |= 255ull << shift;
-        if (remaining == bin_count) break;  // the whole bin is taken: no finer digit needed
-      }
-    }
-    // Take every key whose masked bits exceed prefix, and the first
-    // `remaining` (in ascending j) whose masked bits equal it.
-    int written = 0, eq_seen = 0;
-    for (int base = 0; base < T; base += 64) {
-      const int j = base + l;
-      bool gt = false, eq = false;
+    auto score_at = [&](int j) { return scale * static_cast<double>(dr[j]) + lambda * Mh[j]; };
+    uint64_t key[NI];
+    double smin = __builtin_huge_val(), smax = -__builtin_huge_val();
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int j = 64 * i + l;
+      key[i] = 0;
       if (j < T) {
-        if (keep_k >= T) {
-          gt = true;
-        } else {
-          const uint64_t key = score_key(sc[j]) & mask;
-          gt = key > prefix;
-          eq = key == prefix;
-        }
+        const double s = score_at(j);
+        key[i] = score_key(s);
+        smin = fmin(smin, s);
+        smax = fmax(smax, s);
       }
-      const uint64_t beq = ballot64(eq);
-      const int eq_rank = eq_seen + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(beq >> 32),
-                                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(beq), 0));
-      const bool sel = gt || (eq && eq_rank < remaining);
-      const uint64_t bsel = ballot64(sel);
-      const int pos = written + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bsel >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bsel), 0));
+    }
+    for (int j = tail0 + l; j < T; j += 64) {
+      const double s = score_at(j);
+      smin = fmin(smin, s);
+      smax = fmax(smax, s);
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      smin = fmin(smin, shfl_xor_f64(smin, o));
+      smax = fmax(smax, shfl_xor_f64(smax, o));
+    }
+    const uint64_t kmin = score_key(smin), kmax = score_key(smax);
+    // Invariants: every key whose bits under `mask` exceed `prefix` is taken
+    // (keep_k - rem of them); `match` keys equal prefix under mask and rem of
+    // them are still needed, so match >= rem.
+    uint64_t mask = ~0ull, prefix = kmax;
+    int rem = keep_k;
+    if (kmin != kmax) {
+      const int top = 63 - __builtin_clzll(kmin ^ kmax);  // highest bit where the row's keys differ
+      mask = top == 63 ? 0ull : ~0ull << (top + 1);
+      prefix = kmax & mask;
+      int match = T;
+      for (int b = top; b >= 0 && match != rem; --b) {
+        const uint64_t m2 = mask | (1ull << b), want = prefix | (1ull << b);
+        int c1 = 0;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) c1 += count_lanes((key[i] & m2) == want);
+        for (int base = tail0; base < T; base += 64) {
+          const int j = base + l;
+          c1 += count_lanes(j < T && (score_key(score_at(j)) & m2) == want);
+        }
+        if (rem <= c1) {
+          prefix = want;
+          match = c1;
+        } else {
+          rem -= c1;
+          match -= c1;
+        }
+        mask = m2;
+      }
+    }
+    // Take every key above prefix under mask and the first rem (in ascending
+    // j) equal to it: exactly keep_k indices.
+    int written = 0, eq_seen = 0;
+    auto emit = [&](int j, uint64_t k, bool valid) {
+      const uint64_t km = k & mask;
+      const bool eq = valid && km == prefix;
+      const uint64_t beq = __ballot(eq);
+      const bool sel = (valid && km > prefix) || (eq && eq_seen + lanes_below(beq) < rem);
+      const uint64_t bsel = __ballot(sel);
+      const int pos = written + lanes_below(bsel);
       if (sel && pos < keep_k) out[pos] = j;
       written += __builtin_popcountll(bsel);
       eq_seen += __builtin_popcountll(beq);
+    };
+#pragma unroll
+    for (int i = 0; i < NI; ++i) emit(64 * i + l, key[i], 64 * i + l < T);
+    for (int base = tail0; base < T; base += 64) {
+      const int j = base + l;
+      emit(j, j < T ? score_key(score_at(j)) : 0ull, j < T);
     }
   }
 }
 
 size_t route_lds_bytes(int T, int d, int R) {
-  const size_t scores = static_cast<size_t>(R) * T, partials = 2 * (kThreads / (d * 2 / 16)) * static_cast<size_t>(d);
-  return sizeof(double) * (static_cast<size_t>(d) * kMaxRows + std::max(scores, partials)) + 4 * 256 * sizeof(uint32_t);
+  return sizeof(float) * static_cast<size_t>(R) * static_cast<size_t>(std::max(T, d));
 }
 
-template <typename E, int D>
-hipError_t launch_typed(const paro_problem& p, const E* Q, const float* kbar, const double* M, int keep_k,
-                        double lambda, int32_t* idx, hipStream_t s) {
+template <typename E, int D, int NI>
+hipError_t launch_ni(const paro_problem& p, const E* Q, const float* kbar, const double* M, int keep_k,
+                     double lambda, int32_t* idx, hipStream_t s) {
   const int T = ceil_div(p.L, kBlock);
   const int R = route_rows_per_group(T, D);
   const size_t lds = route_lds_bytes(T, D, R);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_route<E, D>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_route<E, D, NI>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_route<E, D>), dim3(ceil_div(T, R), p.B * p.H), dim3(kThreads), lds, s, Q, kbar, M, idx,
-                     p.L, T, R, keep_k, p.scale, lambda);
+  hipLaunchKernelGGL((k_route<E, D, NI>), dim3(ceil_div(T, R), p.B * p.H), dim3(kThreads), lds, s, Q, kbar, M,
+                     idx, p.L, T, R, keep_k, p.scale, lambda);
   return hipGetLastError();
+}
+
+// Register chunks per lane: ceil(T / 64) rounded up to a multiple of 4.
+template <typename E, int D>
+hipError_t launch_typed(const paro_problem& p, const E* Q, const float* kbar, const double* M, int keep_k,
+                        double lambda, int32_t* idx, hipStream_t s) {
+  switch (std::min((ceil_div(ceil_div(p.L, kBlock), 64) + 3) / 4, kMaxKeyRegs / 4)) {
+    case 1: return launch_ni<E, D, 4>(p, Q, kbar, M, keep_k, lambda, idx, s);
+    case 2: return launch_ni<E, D, 8>(p, Q, kbar, M, keep_k, lambda, idx, s);
+    case 3: return launch_ni<E, D, 12>(p, Q, kbar, M, keep_k, lambda, idx, s);
+    case 4: return launch_ni<E, D, 16>(p, Q, kbar, M, keep_k, lambda, idx, s);
+    case 5: return launch_ni<E, D, 20>(p, Q, kbar, M, keep_k, lambda, idx, s);
+    case 6: return launch_ni<E, D, 24>(p, Q, kbar, M, keep_k, lambda, idx, s);
+    case 7: return launch_ni<E, D, 28>(p, Q, kbar, M, keep_k, lambda, idx, s);
+    default: return launch_ni<E, D, 32>(p, Q, kbar, M, keep_k, lambda, idx, s);
+  }
 }
 
 }  // namespace

@@ -111,7 +111,9 @@ size_t paro_precompute_workspace_bytes(const paro_problem* p);
  * in : Q [B, H, L, d] (dtype); kbar, M from paro_precompute; 0 <= keep_k <= T;
  *      lambda finite.
  * out: idx [B, H, T, keep_k] int32 (nothing is written when keep_k == 0).
- * Scores are formed in fp64 from fp32 kbar and fp64 qbar and M.
+ * qbar is summed in fp64 and rounded to fp32; the dot products qbar . kbar
+ * are fp32 (error ~1e-7); scale * dot + lambda * M and the selection are
+ * fp64.
  */
 int paro_route(const paro_problem* p, const void* Q, const float* kbar, const double* M,
                int32_t keep_k, double lambda, int32_t* idx, void* stream);

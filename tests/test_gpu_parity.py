@@ -144,6 +144,24 @@ def test_route_exact_ties_and_equal_scores(keep):
         assert (idx.cpu().numpy()[0, 0] == ir).all()
 
 
+@pytest.mark.parametrize("keep", [300, 2060])
+def test_route_rows_longer_than_register_keys(keep):
+    """T = 2100 > 2048 kv blocks: the keys past the first 2048 of a row are
+    re-formed each time they are counted. Random keys check the threshold
+    search across that boundary; constant keys (every score equal) check that
+    the first keep blocks in ascending j win across it."""
+    B, H, T, d = 1, 1, 2100, 64
+    L = 64 * T - 30
+    q, k, v = random_uniform_inputs(B, H, L, d, dtype=torch.bfloat16, seed=keep, scale=0.8)
+    lam, scale = 0.1, 1 / np.sqrt(d)
+    for kk, vv in ((k, v), (torch.ones_like(k), torch.ones_like(v))):
+        (qd, kd, vd), stats, idx = run_gpu(q, kk, vv, keep, lam)
+        qn, kn, vn = (x[0, 0].double().numpy() for x in (q, kk, vv))
+        st = pisa.block_stats(kn, vn, 64)
+        ir, sc = pisa.route(qn, st["kbar"], st["M"], keep, lam, scale, 64)
+        check_route(idx.cpu().numpy()[0, 0], ir, sc)
+
+
 def test_logit_jump_rerun_keeps_every_row_exact():
     """A kv block whose logits sit ~88 nats above the first tile's forces the
     kernel's rerun path for the query blocks that list it; the other blocks of
