@@ -225,6 +225,9 @@ def main():
     traffic = traffic_entry()
     kv_bytes = 2.0 * w.B * w.H * w.L * w.d * (2 if w.dtype == "bf16" else 4)
     pre_ms = sum(pre) / len(pre)
+    # routing reads Q once plus kbar (fp32) and M (fp64), and writes idx (int32)
+    route_bytes = kv_bytes / 2 + w.B * w.H * w.T * (4.0 * w.d + 8.0 + 4.0 * w.k)
+    route_ms = sum(rou) / len(rou)
 
     res = {
         "metric": "dense-equiv TFLOP/s + ms/call, 32k-119k-token DiT attention, 12.5% density",
@@ -240,10 +243,12 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded Fourier-feature Q/K, N(0,1) V; no trained weights)",
         "config": {**w.describe(), "parallelism": "none (1 GPU)"},
-        "phases_ms": {"precompute": round(pre_ms, 4), "route": round(sum(rou) / len(rou), 4),
+        "phases_ms": {"precompute": round(pre_ms, 4), "route": round(route_ms, 4),
                       "attention": round(attn_ms, 4)},
         "precompute_hbm": {"algorithmic_GBs": round(kv_bytes / (pre_ms * 1e-3) / 1e9, 1),
                            "frac_of_peak": round(kv_bytes / (pre_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "route_hbm": {"algorithmic_GBs": round(route_bytes / (route_ms * 1e-3) / 1e9, 1),
+                      "frac_of_peak": round(route_bytes / (route_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "roofline": {
             "kernel": "k_attn_bf16 (paro_attention)",
             "bound": "mfma",
