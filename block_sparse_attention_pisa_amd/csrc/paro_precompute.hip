@@ -18,7 +18,7 @@
 //   3. k_block_spectral: one workgroup of two waves per block; re-reads K_j
 //                        and V_j, rebuilds A = H_j - Hbar in registers on
 //                        MFMA and finds its largest singular value by
-//                        restarted Lanczos on A^T A (fp32 vectors, fp64
+//                        restarted Lanczos on A^T A (fp32 vectors and
 //                        tridiagonal eigenproblem); the final ||A x|| / ||x||
 //                        is accumulated in fp64. H_j never reaches memory.
 // No float atomics anywhere: results are bitwise reproducible.

@@ -88,8 +88,8 @@ typedef struct paro_problem {
  *      Hbar [B, H, d, d] fp32   mean over all T blocks of H_j; row = key dim,
  *                               column = value dim
  *      M    [B, H, T]    fp64   largest singular value of H_j - Hbar
- *                               (restarted Lanczos on A^T A in fp32 with
- *                               fp64 scalars; final ||A x|| / ||x|| in fp64)
+ *                               (restarted Lanczos on A^T A in fp32;
+ *                               final ||A x|| / ||x|| in fp64)
  * workspace: device scratch of at least paro_precompute_workspace_bytes(p)
  *            bytes (per-chunk partial sums of H_j); contents on entry are
  *            ignored and undefined on return.
