@@ -94,6 +94,42 @@ def test_edge_shapes(case, dtype):
         check_attention(o[b, h], oref, dtype)
 
 
+@pytest.mark.parametrize("case", [
+    dict(B=1, H=2, L=64 * 300 + 11, d=64, keep=30, lam=0.1),     # d = 64 over many tiles, ragged tail
+    dict(B=2, H=1, L=64 * 600 - 5, d=128, keep=599, lam=0.1),    # keep = T - 1: one tail block per row
+    dict(B=1, H=1, L=64 * 200, d=128, keep=25, lam=0.0),         # lambda = 0: routing by q-bar . k-bar alone
+    dict(B=1, H=1, L=64 * 200, d=128, keep=25, lam=5.0),         # large lambda: routing by M_j mostly
+])
+def test_medium_shapes(case):
+    """Stats and routing of every row, attention on sampled query blocks, at
+    sizes between the edge cases and the DiT workloads."""
+    B, H, L, d, keep, lam = (case[x] for x in ("B", "H", "L", "d", "keep", "lam"))
+    q, k, v = random_uniform_inputs(B, H, L, d, dtype=torch.bfloat16, seed=L + keep, scale=0.8)
+    scale = 1 / np.sqrt(d)
+    (qd, kd, vd), stats, idx = run_gpu(q, k, v, keep, lam)
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    idx_h = idx.cpu().numpy()
+    idx_or = torch.empty_like(idx.cpu())
+    refs = {}
+    for b in range(B):
+        for h in range(H):
+            st = pisa.block_stats(kn[b, h], vn[b, h], 64)
+            ir, sc = pisa.route(qn[b, h], st["kbar"], st["M"], keep, lam, scale, 64)
+            check_stats(stats, st, b, h)
+            ex = check_route(idx_h[b, h], ir, sc)
+            log(f"[parity] medium {case} b{b}h{h}: excused routing rows {ex}")
+            idx_or[b, h] = torch.from_numpy(ir.astype(np.int32))
+            refs[(b, h)] = (st, ir)
+    o = paro.attention(qd, kd, vd, *stats[:3], idx_or.cuda(), keep).float().cpu().numpy()
+    rng_ = pisa.block_ranges(L, 64)
+    for (b, h), (st, ir) in refs.items():
+        qbs = sample_qblocks(len(rng_), 8)
+        oref = pisa.attention(qn[b, h], kn[b, h], vn[b, h], st, ir, scale, 64, qblocks=qbs)
+        og = np.concatenate([o[b, h, rng_[i][0]:rng_[i][1]] for i in qbs])
+        orr = np.concatenate([oref[i] for i in qbs])
+        check_attention(og, orr, "bf16")
+
+
 def test_rows_past_L_are_not_written():
     """The output is written only for the L valid rows (bytes after it stay untouched)."""
     B, H, L, d = 1, 1, 64 * 3 - 10, 128
