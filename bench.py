@@ -49,7 +49,7 @@ def parse():
     return ap.parse_args()
 
 
-def attention_flops(w, idx_cpu) -> float:
+def attention_flops(w, idx_cpu, with_exact: bool = False):
     """Algorithmic FLOPs of one attention launch.
 
     Exact part 4 d sum_i n_i sum_{j in S_i} n_j (QK^T and PV), zeroth-order
@@ -64,6 +64,7 @@ def attention_flops(w, idx_cpu) -> float:
     idx = idx_cpu.reshape(-1, T, w.k) if w.k else None
     heads = w.B * w.H
     total = 0.0
+    exact_total = 0.0
     for h in range(heads):
         if w.k:
             sel_tokens = n[idx[h]].sum(axis=1)           # sum_{j in S_i} n_j per row i
@@ -73,7 +74,8 @@ def attention_flops(w, idx_cpu) -> float:
         tail = 4.0 * d * float((n * (T - w.k)).sum())
         corr = 2.0 * d * d * L if w.k < T else 0.0
         total += exact + tail + corr
-    return total
+        exact_total += exact
+    return (total, exact_total) if with_exact else total
 
 
 def exact_phase_entry(reps: int = 3):
@@ -219,7 +221,32 @@ def main():
     value = dense_flops / (ms_step * 1e-3) / 1e12
 
     idx_cpu = idx.cpu().numpy()
-    attn_flops = attention_flops(w, idx_cpu)
+    attn_flops, exact_flops = attention_flops(w, idx_cpu, with_exact=True)
+
+    # the exact phase on this workload: the same kernel with U_i dropped
+    # (keep-or-drop mode), exact FLOPs over its time
+    ex_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, w.k, out=out, drop_tail=True)
+    ex_ev[0].record(stream)
+    for _ in range(3):
+        paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, w.k, out=out, drop_tail=True)
+    ex_ev[1].record(stream)
+    torch.cuda.synchronize()
+    ex_ms = ex_ev[0].elapsed_time(ex_ev[1]) / 3
+    ex_tf = exact_flops / (ex_ms * 1e-3) / 1e12
+
+    # cold steps: L2 and MALL flushed by a 512 MB write before each step
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(3):
+        flush.fill_(i & 255)
+        cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        cev[0].record(stream)
+        step()
+        cev[1].record(stream)
+        torch.cuda.synchronize()
+        cold.append(cev[0].elapsed_time(cev[1]))
+    del flush
     attn_ms = sum(att) / len(att)
     achieved = attn_flops / (attn_ms * 1e-3) / 1e12
     traffic = traffic_entry()
@@ -259,6 +286,11 @@ def main():
             "traffic": traffic,
             "algorithmic_flops_per_launch": attn_flops,
         },
+        "exact_phase_tail_dropped": {"workload": w.name + " (tail dropped)", "ms": round(ex_ms, 3),
+                             "algorithmic_flops": exact_flops, "achieved": round(ex_tf, 2),
+                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(ex_tf / PEAK_BF16_TFLOPS, 4)},
+        "cold_ms_per_step": round(sorted(cold)[1], 4),
         "input_generation_s": round(t_gen, 1),
     }
     if not a.no_exact_phase:

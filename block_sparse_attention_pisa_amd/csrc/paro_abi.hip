@@ -57,7 +57,7 @@ const char* paro_status_string(int status) {
     case PARO_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case PARO_ERR_WORKSPACE: return "workspace smaller than paro_precompute_workspace_bytes()";
     case PARO_ERR_HIP: return "a kernel launch reported a HIP error";
-    case PARO_ERR_ARG: return "scale must be finite and > 0, lambda finite";
+    case PARO_ERR_ARG: return "scale must be finite and > 0, lambda finite, mode known";
     default: return "unknown status";
   }
 }
@@ -90,17 +90,24 @@ int paro_route(const paro_problem* p, const void* Q, const float* kbar, const do
   return from_hip(paro::launch_route(*p, Q, kbar, M, keep_k, lambda, idx, static_cast<hipStream_t>(stream)));
 }
 
-int paro_attention(const paro_problem* p, const void* Q, const void* K, const void* V, const float* kbar,
-                   const float* vsum, const float* Hbar, const int32_t* idx, int32_t keep_k, void* O,
-                   void* stream) {
+int paro_attention_mode(const paro_problem* p, const void* Q, const void* K, const void* V, const float* kbar,
+                        const float* vsum, const float* Hbar, const int32_t* idx, int32_t keep_k, int32_t mode,
+                        void* O, void* stream) {
   int rc = check_problem(p);
   if (rc != PARO_OK) return rc;
   const int T = num_blocks(p);
   if (keep_k < 0 || keep_k > T) return PARO_ERR_SHAPE;
+  if (mode != PARO_TAIL_PISA && mode != PARO_TAIL_DROP) return PARO_ERR_ARG;
   if ((rc = check_ptrs({Q, K, V, kbar, vsum, Hbar, O})) != PARO_OK) return rc;
   if (keep_k > 0 && (rc = check_ptrs({idx})) != PARO_OK) return rc;
-  return from_hip(paro::launch_attention(*p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O,
+  return from_hip(paro::launch_attention(*p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode == PARO_TAIL_PISA,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int paro_attention(const paro_problem* p, const void* Q, const void* K, const void* V, const float* kbar,
+                   const float* vsum, const float* Hbar, const int32_t* idx, int32_t keep_k, void* O,
+                   void* stream) {
+  return paro_attention_mode(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, PARO_TAIL_PISA, O, stream);
 }
 
 }  // extern "C"

@@ -393,7 +393,8 @@ template <int D>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const float* __restrict__ kbar, const float* __restrict__ vsum, const float* __restrict__ Hbar,
-    const int32_t* __restrict__ idx, uint16_t* __restrict__ O, int L, int T, int keep_k, float scale, int nwg) {
+    const int32_t* __restrict__ idx, uint16_t* __restrict__ O, int L, int T, int keep_k, float scale, int nwg,
+    bool tail) {
   constexpr int BUF = Geo<D>::BUF, KS = Geo<D>::KS, VS = Geo<D>::VS, HS = Geo<D>::HS;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* buf = reinterpret_cast<uint16_t*>(smem);  // 2 staging buffers
@@ -485,7 +486,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   const uint32_t* mymask = masks + qi * nw;
   const float* kb = kbar + static_cast<size_t>(bh) * T * D;
   const float* vs = vsum + static_cast<size_t>(bh) * T * D;
-  const int nch = keep_k < T ? ceil_div(T, 32) : 0;
+  // stage 2 chunks (none when U_i is empty or the tail is dropped; step 0
+  // still stages centroid chunk 0 for the softmax reference)
+  const int nch = (tail && keep_k < T) ? ceil_div(T, 32) : 0;
 
   bool active = qvalid;
 #pragma unroll
@@ -711,7 +714,7 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
                                                           const float* __restrict__ vsum,
                                                           const float* __restrict__ Hbar,
                                                           const int32_t* __restrict__ idx, float* __restrict__ O,
-                                                          int L, int T, int keep_k, float scale) {
+                                                          int L, int T, int keep_k, float scale, bool tail) {
   constexpr int DP = D / 4;  // dims per thread
   extern __shared__ __align__(16) unsigned char smem[];
   float(*kt)[D] = reinterpret_cast<float(*)[D]>(smem);
@@ -758,7 +761,7 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
     __syncthreads();
     for (int tk = 0; tk < nv; ++tk) key_step(kt[tk], vt[tk], 1.f, false);
   }
-  if (keep_k < T) {
+  if (tail && keep_k < T) {
     __syncthreads();
     for (int wd = tid; wd < nw; wd += kF32Threads) selmask[wd] = 0u;
     __syncthreads();
@@ -792,7 +795,7 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
 
 template <int D>
 hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
-                       const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O,
+                       const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, bool tail,
                        hipStream_t s) {
   const int T = ceil_div(p.L, 64);
   const int nw = ceil_div(T, 32);
@@ -806,13 +809,13 @@ hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, cons
   hipLaunchKernelGGL(k_attn_bf16<D>, dim3(nwg), dim3(kAttnThreads), lds_al, s,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), kbar, vsum, Hbar, idx, static_cast<uint16_t*>(O), p.L, T,
-                     keep_k, static_cast<float>(p.scale), nwg);
+                     keep_k, static_cast<float>(p.scale), nwg, tail);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_f32(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
-                      const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O,
+                      const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, bool tail,
                       hipStream_t s) {
   const int T = ceil_div(p.L, 64);
   const size_t lds = 2 * sizeof(float) * 64 * D + sizeof(uint32_t) * ceil_div(T, 32);
@@ -821,20 +824,20 @@ hipError_t launch_f32(const paro_problem& p, const void* Q, const void* K, const
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_f32<D>, dim3(T, p.B * p.H), dim3(kF32Threads), lds, s, static_cast<const float*>(Q),
                      static_cast<const float*>(K), static_cast<const float*>(V), kbar, vsum, Hbar, idx,
-                     static_cast<float*>(O), p.L, T, keep_k, static_cast<float>(p.scale));
+                     static_cast<float*>(O), p.L, T, keep_k, static_cast<float>(p.scale), tail);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attention(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
-                            const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O,
+                            const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, bool tail,
                             hipStream_t s) {
   if (p.dtype == PARO_DTYPE_BF16)
-    return p.d == 128 ? launch_bf16<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, s)
-                      : launch_bf16<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, s);
-  return p.d == 128 ? launch_f32<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, s)
-                    : launch_f32<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, s);
+    return p.d == 128 ? launch_bf16<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, tail, s)
+                      : launch_bf16<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, tail, s);
+  return p.d == 128 ? launch_f32<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, tail, s)
+                    : launch_f32<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, tail, s);
 }
 
 }  // namespace paro

@@ -27,6 +27,7 @@ STATUS = {
 
 EXPORTED = (
     "paro_precompute", "paro_precompute_workspace_bytes", "paro_route", "paro_attention",
+    "paro_attention_mode",
     "paro_num_blocks", "paro_status_string", "paro_version",
 )
 
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.paro_route.restype = ctypes.c_int
         L.paro_attention.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
         L.paro_attention.restype = ctypes.c_int
+        L.paro_attention_mode.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp]
+        L.paro_attention_mode.restype = ctypes.c_int
         L.paro_num_blocks.argtypes = [i32, i32]
         L.paro_num_blocks.restype = i32
         L.paro_status_string.argtypes = [ctypes.c_int]
@@ -162,17 +165,23 @@ def route(q: torch.Tensor, kbar: torch.Tensor, M: torch.Tensor, keep_k: int, lam
     return idx
 
 
+TAIL_PISA, TAIL_DROP = 0, 1
+
+
 def attention(q, k, v, kbar, vsum, Hbar, idx, keep_k: int, scale: float | None = None,
-              out: torch.Tensor | None = None) -> torch.Tensor:
-    """Piecewise attention output [B, H, L, d] in the dtype of q."""
+              out: torch.Tensor | None = None, drop_tail: bool = False) -> torch.Tensor:
+    """Piecewise attention output [B, H, L, d] in the dtype of q.
+
+    drop_tail=True drops U_i instead of approximating it (keep-or-drop
+    sparse attention, the exact phase alone)."""
     p = problem(q, scale)
     o = torch.empty_like(q) if out is None else out
     ptr = _dev(idx, "idx", torch.int32) if keep_k > 0 else None
-    _check(lib().paro_attention(
+    _check(lib().paro_attention_mode(
         ctypes.byref(p), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
         _dev(kbar, "kbar", torch.float32), _dev(vsum, "vsum", torch.float32),
-        _dev(Hbar, "Hbar", torch.float32), ptr, int(keep_k), _dev(o, "o", q.dtype), _stream()),
-        "paro_attention")
+        _dev(Hbar, "Hbar", torch.float32), ptr, int(keep_k), TAIL_DROP if drop_tail else TAIL_PISA,
+        _dev(o, "o", q.dtype), _stream()), "paro_attention_mode")
     return o
 
 

@@ -61,7 +61,10 @@ extern "C" {
 #define PARO_ERR_ALIGN (-4)     /* a pointer is not 16-byte aligned */
 #define PARO_ERR_WORKSPACE (-5) /* workspace smaller than paro_precompute_workspace_bytes() */
 #define PARO_ERR_HIP (-6)       /* a kernel launch reported a HIP error */
-#define PARO_ERR_ARG (-7)       /* scale not finite and > 0, or lambda not finite */
+#define PARO_ERR_ARG (-7)       /* scale not finite and > 0, lambda not finite, or unknown mode */
+
+#define PARO_TAIL_PISA 0  /* paro_attention_mode: zeroth-order tail and first-order correction */
+#define PARO_TAIL_DROP 1  /* paro_attention_mode: tail dropped (keep-or-drop sparse attention) */
 
 #define PARO_DTYPE_BF16 0
 #define PARO_DTYPE_FP32 1
@@ -138,6 +141,22 @@ int paro_route(const paro_problem* p, const void* Q, const float* kbar, const do
 int paro_attention(const paro_problem* p, const void* Q, const void* K, const void* V,
                    const float* kbar, const float* vsum, const float* Hbar,
                    const int32_t* idx, int32_t keep_k, void* O, void* stream);
+
+/*
+ * paro_attention_mode - paro_attention with the treatment of the tail U_i
+ * chosen by `mode`:
+ *   PARO_TAIL_PISA: the method (same as paro_attention);
+ *   PARO_TAIL_DROP: U_i is dropped (no stage 2, no stage 3): softmax
+ *     attention renormalised over the blocks of S_i, i.e. the keep-or-drop
+ *     sparse attention that section 1 (problem definition) describes as the
+ *     approach the method improves on, and the exact phase of the method on
+ *     its own.
+ * Same arguments and contract as paro_attention; an unknown mode returns
+ * PARO_ERR_ARG.
+ */
+int paro_attention_mode(const paro_problem* p, const void* Q, const void* K, const void* V,
+                        const float* kbar, const float* vsum, const float* Hbar,
+                        const int32_t* idx, int32_t keep_k, int32_t mode, void* O, void* stream);
 
 /* T = ceil(L / block), or -1 when L < 1 or block < 1. */
 int32_t paro_num_blocks(int32_t L, int32_t block);

@@ -130,6 +130,34 @@ def test_medium_shapes(case):
         check_attention(og, orr, "bf16")
 
 
+@pytest.mark.parametrize("case", ["image_4608", "ragged_d64", "tiny_fp32"])
+def test_drop_tail_mode_is_keep_or_drop_attention(case):
+    """PARO_TAIL_DROP: stages 2 and 3 off, softmax renormalised over S_i (the
+    oracle's tail=False mode), fed the oracle's routing."""
+    if case == "ragged_d64":
+        B, H, L, d, keep = 1, 2, 64 * 9 - 17, 64, 3
+        q, k, v = random_uniform_inputs(B, H, L, d, dtype=torch.bfloat16, seed=91, scale=0.8)
+        dtype, scale = "bf16", 1 / np.sqrt(d)
+    else:
+        w = WORKLOADS[case]
+        q, k, v = make_inputs(w)
+        B, H, L, keep, dtype, scale = w.B, w.H, w.L, w.k, w.dtype, w.scale
+    (qd, kd, vd), stats, _ = run_gpu(q, k, v, keep, 0.1)
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    idx_or = torch.empty(B, H, -(-L // 64), keep, dtype=torch.int32)
+    refs = {}
+    for b in range(B):
+        for h in range(H):
+            st = pisa.block_stats(kn[b, h], vn[b, h], 64)
+            ir, _ = pisa.route(qn[b, h], st["kbar"], st["M"], keep, 0.1, scale, 64)
+            idx_or[b, h] = torch.from_numpy(ir.astype(np.int32))
+            refs[(b, h)] = (st, ir)
+    o = paro.attention(qd, kd, vd, *stats[:3], idx_or.cuda(), keep, drop_tail=True).float().cpu().numpy()
+    for (b, h), (st, ir) in refs.items():
+        oref = pisa.attention(qn[b, h], kn[b, h], vn[b, h], st, ir, scale, 64, tail=False)
+        check_attention(o[b, h], oref, dtype)
+
+
 def test_rows_past_L_are_not_written():
     """The output is written only for the L valid rows (bytes after it stay untouched)."""
     B, H, L, d = 1, 1, 64 * 3 - 10, 128
