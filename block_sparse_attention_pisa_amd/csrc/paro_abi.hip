@@ -97,10 +97,10 @@ int paro_attention_mode(const paro_problem* p, const void* Q, const void* K, con
   if (rc != PARO_OK) return rc;
   const int T = num_blocks(p);
   if (keep_k < 0 || keep_k > T) return PARO_ERR_SHAPE;
-  if (mode != PARO_TAIL_PISA && mode != PARO_TAIL_DROP) return PARO_ERR_ARG;
+  if (mode != PARO_TAIL_PISA && mode != PARO_TAIL_DROP && mode != PARO_TAIL_ZEROTH) return PARO_ERR_ARG;
   if ((rc = check_ptrs({Q, K, V, kbar, vsum, Hbar, O})) != PARO_OK) return rc;
   if (keep_k > 0 && (rc = check_ptrs({idx})) != PARO_OK) return rc;
-  return from_hip(paro::launch_attention(*p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode == PARO_TAIL_PISA,
+  return from_hip(paro::launch_attention(*p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode,
                                          static_cast<hipStream_t>(stream)));
 }
 

@@ -47,6 +47,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kQB = 4;                    // query blocks per workgroup
 constexpr int kWaves = 2 * kQB;           // two 32-row waves per query block
 constexpr int kAttnThreads = 64 * kWaves;
+// tail modes (the PARO_TAIL_* codes of the ABI; 2 = zeroth order only: tail on, correction off)
+constexpr int kModePisa = 0, kModeDrop = 1;
 
 template <int D>
 struct Geo {
@@ -394,7 +396,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const float* __restrict__ kbar, const float* __restrict__ vsum, const float* __restrict__ Hbar,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ O, int L, int T, int keep_k, float scale, int nwg,
-    bool tail) {
+    int mode) {
+  const bool tail = mode != kModeDrop, corr = mode == kModePisa;
   constexpr int BUF = Geo<D>::BUF, KS = Geo<D>::KS, VS = Geo<D>::VS, HS = Geo<D>::HS;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* buf = reinterpret_cast<uint16_t*>(smem);  // 2 staging buffers
@@ -658,7 +661,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   // ---- stage 3: global first-order correction, then N / D
   const float csum = a.csum + __shfl_xor(a.csum, 32);
   const float dsum = a.dsum + __shfl_xor(a.dsum, 32);
-  if (nch > 0) {
+  if (nch > 0 && corr) {
     // Hbar^T in bf16: ht[v][k] = Hbar[k][v], rows padded to HS
     const float* Hh = Hbar + static_cast<size_t>(bh) * D * D;
     for (int item = tid; item < (D / 4) * Geo<D>::CG; item += kAttnThreads) {
@@ -686,7 +689,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
 #pragma unroll
     for (int u = 0; u < Geo<D>::NU; ++u) {
       f32x16 o = a.o[u];
-      if (nch > 0) {
+      if (nch > 0 && corr) {
         f32x16 r = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < Geo<D>::NK; ++ks)
@@ -714,7 +717,8 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
                                                           const float* __restrict__ vsum,
                                                           const float* __restrict__ Hbar,
                                                           const int32_t* __restrict__ idx, float* __restrict__ O,
-                                                          int L, int T, int keep_k, float scale, bool tail) {
+                                                          int L, int T, int keep_k, float scale, int mode) {
+  const bool tail = mode != kModeDrop, corr = mode == kModePisa;
   constexpr int DP = D / 4;  // dims per thread
   extern __shared__ __align__(16) unsigned char smem[];
   float(*kt)[D] = reinterpret_cast<float(*)[D]>(smem);
@@ -735,7 +739,7 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
   float m = -INFINITY, dsum = 0.f, csum = 0.f;
   const int nlast = L - 64 * (T - 1);
 
-  auto key_step = [&](const float* kk, const float* vv, float weight, bool tail) {
+  auto key_step = [&](const float* kk, const float* vv, float weight, bool in_tail) {
     float x = 0.f;
     for (int e = 0; e < DP; ++e) x += q[e] * kk[part * DP + e];
     x += __shfl_xor(x, 1);
@@ -745,7 +749,7 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
     const float p = expf(x - mnew);
     m = mnew;
     dsum = dsum * alpha + p * weight;
-    if (tail) csum = csum * alpha + p;
+    if (in_tail) csum = csum * alpha + p;
     for (int e = 0; e < DP; ++e) o[e] = o[e] * alpha + p * vv[part * DP + e];
   };
 
@@ -789,13 +793,13 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
       for (int e = 0; e < DP; ++e) rr[e] += qk * Hh[k * D + part * DP + e];
     }
     float* op = O + head + static_cast<size_t>(row) * D + part * DP;
-    for (int e = 0; e < DP; ++e) op[e] = (o[e] + csum * rr[e]) / dsum;
+    for (int e = 0; e < DP; ++e) op[e] = (o[e] + (corr ? csum * rr[e] : 0.f)) / dsum;
   }
 }
 
 template <int D>
 hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
-                       const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, bool tail,
+                       const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, int mode,
                        hipStream_t s) {
   const int T = ceil_div(p.L, 64);
   const int nw = ceil_div(T, 32);
@@ -809,13 +813,13 @@ hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, cons
   hipLaunchKernelGGL(k_attn_bf16<D>, dim3(nwg), dim3(kAttnThreads), lds_al, s,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), kbar, vsum, Hbar, idx, static_cast<uint16_t*>(O), p.L, T,
-                     keep_k, static_cast<float>(p.scale), nwg, tail);
+                     keep_k, static_cast<float>(p.scale), nwg, mode);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_f32(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
-                      const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, bool tail,
+                      const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, int mode,
                       hipStream_t s) {
   const int T = ceil_div(p.L, 64);
   const size_t lds = 2 * sizeof(float) * 64 * D + sizeof(uint32_t) * ceil_div(T, 32);
@@ -824,20 +828,20 @@ hipError_t launch_f32(const paro_problem& p, const void* Q, const void* K, const
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_f32<D>, dim3(T, p.B * p.H), dim3(kF32Threads), lds, s, static_cast<const float*>(Q),
                      static_cast<const float*>(K), static_cast<const float*>(V), kbar, vsum, Hbar, idx,
-                     static_cast<float*>(O), p.L, T, keep_k, static_cast<float>(p.scale), tail);
+                     static_cast<float*>(O), p.L, T, keep_k, static_cast<float>(p.scale), mode);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attention(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
-                            const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, bool tail,
+                            const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, int mode,
                             hipStream_t s) {
   if (p.dtype == PARO_DTYPE_BF16)
-    return p.d == 128 ? launch_bf16<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, tail, s)
-                      : launch_bf16<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, tail, s);
-  return p.d == 128 ? launch_f32<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, tail, s)
-                    : launch_f32<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, tail, s);
+    return p.d == 128 ? launch_bf16<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, s)
+                      : launch_bf16<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, s);
+  return p.d == 128 ? launch_f32<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, s)
+                    : launch_f32<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, s);
 }
 
 }  // namespace paro

@@ -165,22 +165,25 @@ def route(q: torch.Tensor, kbar: torch.Tensor, M: torch.Tensor, keep_k: int, lam
     return idx
 
 
-TAIL_PISA, TAIL_DROP = 0, 1
+TAIL_PISA, TAIL_DROP, TAIL_ZEROTH = 0, 1, 2
 
 
 def attention(q, k, v, kbar, vsum, Hbar, idx, keep_k: int, scale: float | None = None,
-              out: torch.Tensor | None = None, drop_tail: bool = False) -> torch.Tensor:
+              out: torch.Tensor | None = None, drop_tail: bool = False,
+              first_order: bool = True) -> torch.Tensor:
     """Piecewise attention output [B, H, L, d] in the dtype of q.
 
     drop_tail=True drops U_i instead of approximating it (keep-or-drop
-    sparse attention, the exact phase alone)."""
+    sparse attention, the exact phase alone); first_order=False keeps the
+    zeroth-order tail but leaves out the first-order correction."""
     p = problem(q, scale)
     o = torch.empty_like(q) if out is None else out
     ptr = _dev(idx, "idx", torch.int32) if keep_k > 0 else None
     _check(lib().paro_attention_mode(
         ctypes.byref(p), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
         _dev(kbar, "kbar", torch.float32), _dev(vsum, "vsum", torch.float32),
-        _dev(Hbar, "Hbar", torch.float32), ptr, int(keep_k), TAIL_DROP if drop_tail else TAIL_PISA,
+        _dev(Hbar, "Hbar", torch.float32), ptr, int(keep_k),
+        TAIL_DROP if drop_tail else (TAIL_PISA if first_order else TAIL_ZEROTH),
         _dev(o, "o", q.dtype), _stream()), "paro_attention_mode")
     return o
 

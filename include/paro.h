@@ -65,6 +65,7 @@ extern "C" {
 
 #define PARO_TAIL_PISA 0  /* paro_attention_mode: zeroth-order tail and first-order correction */
 #define PARO_TAIL_DROP 1  /* paro_attention_mode: tail dropped (keep-or-drop sparse attention) */
+#define PARO_TAIL_ZEROTH 2 /* paro_attention_mode: zeroth-order tail only, no first-order correction */
 
 #define PARO_DTYPE_BF16 0
 #define PARO_DTYPE_FP32 1
@@ -151,6 +152,10 @@ int paro_attention(const paro_problem* p, const void* Q, const void* K, const vo
  *     sparse attention that section 1 (problem definition) describes as the
  *     approach the method improves on, and the exact phase of the method on
  *     its own.
+ *   PARO_TAIL_ZEROTH: stages 1 and 2 only (the zeroth-order tail terms
+ *     without the first-order correction of stage 3), the ablation that
+ *     isolates what the correction adds (section 2, the third term of the
+ *     numerator).
  * Same arguments and contract as paro_attention; an unknown mode returns
  * PARO_ERR_ARG.
  */

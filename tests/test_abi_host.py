@@ -94,7 +94,7 @@ def test_pointer_and_argument_validation():
     assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, FAKE, None) == -1
     assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T + 1, FAKE, None) == -2
     assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE + 2, None) == -4
-    assert L.paro_attention_mode(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, FAKE, None) == -7
+    assert L.paro_attention_mode(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 3, FAKE, None) == -7
     assert L.paro_attention_mode(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, -1, FAKE, None) == -7
     assert L.paro_attention_mode(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T + 1, 1, FAKE, None) == -2
 

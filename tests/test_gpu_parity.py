@@ -158,6 +158,31 @@ def test_drop_tail_mode_is_keep_or_drop_attention(case):
         check_attention(o[b, h], oref, dtype)
 
 
+@pytest.mark.parametrize("case", ["image_4608", "tiny_fp32"])
+def test_zeroth_order_mode(case):
+    """PARO_TAIL_ZEROTH: stages 1 and 2 without the first-order correction
+    (the oracle's first_order="none" mode); it must differ from the method
+    by the correction term."""
+    w = WORKLOADS[case]
+    q, k, v = make_inputs(w)
+    (qd, kd, vd), stats, _ = run_gpu(q, k, v, w.k, w.lam)
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    idx_or = torch.empty(w.B, w.H, w.T, w.k, dtype=torch.int32)
+    refs = {}
+    for b in range(w.B):
+        for h in range(w.H):
+            st = pisa.block_stats(kn[b, h], vn[b, h], 64)
+            ir, _ = pisa.route(qn[b, h], st["kbar"], st["M"], w.k, w.lam, w.scale, 64)
+            idx_or[b, h] = torch.from_numpy(ir.astype(np.int32))
+            refs[(b, h)] = (st, ir)
+    o0 = paro.attention(qd, kd, vd, *stats[:3], idx_or.cuda(), w.k, first_order=False).float().cpu().numpy()
+    o1 = paro.attention(qd, kd, vd, *stats[:3], idx_or.cuda(), w.k).float().cpu().numpy()
+    for (b, h), (st, ir) in refs.items():
+        oref = pisa.attention(qn[b, h], kn[b, h], vn[b, h], st, ir, w.scale, 64, first_order="none")
+        check_attention(o0[b, h], oref, w.dtype)
+    assert np.abs(o1 - o0).max() > 0.0
+
+
 def test_rows_past_L_are_not_written():
     """The output is written only for the L valid rows (bytes after it stay untouched)."""
     B, H, L, d = 1, 1, 64 * 3 - 10, 128
