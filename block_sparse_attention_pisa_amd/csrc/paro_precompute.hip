@@ -731,7 +731,10 @@ template <typename E, int D>
 int stats_chunks(const paro_problem& p, int* G) {
   const int T = ceil_div(p.L, kBlock);
   const int bh = p.B * p.H;
-  int nchunk = max(1, min(T, ceil_div(1024, bh)));
+  // about 1024 workgroups in all, rounded down: two full rounds of the 512
+  // that fit at once (256 CUs x 2), rather than two and a sliver whose
+  // workgroups each walk a whole chunk alone
+  int nchunk = max(1, min(T, 1024 / bh));
   *G = ceil_div(T, nchunk);
   return ceil_div(T, *G);
 }
