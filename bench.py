@@ -92,12 +92,14 @@ def exact_phase_entry(reps: int = 3):
     stats = paro.precompute(kd, vd)
     idx = paro.route(qd, stats[0], stats[3], w.k, w.lam)
     out = torch.empty_like(qd)
+    attn_ws = torch.empty(max(16, paro.attention_workspace_bytes(paro.problem(qd))), dtype=torch.uint8,
+                          device=qd.device)
     stream = torch.cuda.current_stream()
-    paro.attention(qd, kd, vd, *stats[:3], idx, w.k, out=out)
+    paro.attention(qd, kd, vd, *stats[:3], idx, w.k, out=out, workspace=attn_ws)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
     for _ in range(reps):
-        paro.attention(qd, kd, vd, *stats[:3], idx, w.k, out=out)
+        paro.attention(qd, kd, vd, *stats[:3], idx, w.k, out=out, workspace=attn_ws)
     ev[1].record(stream)
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[1]) / reps
@@ -188,6 +190,8 @@ def main():
     stats = paro.alloc_stats(kd)
     idx = torch.empty(w.B, w.H, w.T, w.k, dtype=torch.int32, device=dev)
     out = torch.empty_like(qd)
+    attn_ws = torch.empty(max(16, paro.attention_workspace_bytes(paro.problem(qd))), dtype=torch.uint8,
+                          device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -199,7 +203,7 @@ def main():
         paro.route(qd, stats[0], stats[3], w.k, w.lam, out=idx)
         if ev:
             ev[2].record(stream)
-        paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, w.k, out=out)
+        paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, w.k, out=out, workspace=attn_ws)
         if ev:
             ev[3].record(stream)
 
@@ -226,10 +230,12 @@ def main():
     # the exact phase on this workload: the same kernel with U_i dropped
     # (keep-or-drop mode), exact FLOPs over its time
     ex_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, w.k, out=out, drop_tail=True)
+    paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, w.k, out=out, drop_tail=True,
+                   workspace=attn_ws)
     ex_ev[0].record(stream)
     for _ in range(3):
-        paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, w.k, out=out, drop_tail=True)
+        paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, w.k, out=out, drop_tail=True,
+                   workspace=attn_ws)
     ex_ev[1].record(stream)
     torch.cuda.synchronize()
     ex_ms = ex_ev[0].elapsed_time(ex_ev[1]) / 3

@@ -55,7 +55,7 @@ const char* paro_status_string(int status) {
     case PARO_ERR_SHAPE: return "unsupported shape (B, H, L, d, block, keep_k or number of blocks)";
     case PARO_ERR_DTYPE: return "unknown dtype code";
     case PARO_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case PARO_ERR_WORKSPACE: return "workspace smaller than paro_precompute_workspace_bytes()";
+    case PARO_ERR_WORKSPACE: return "workspace smaller than the call's *_workspace_bytes()";
     case PARO_ERR_HIP: return "a kernel launch reported a HIP error";
     case PARO_ERR_ARG: return "scale must be finite and > 0, lambda finite, mode known";
     default: return "unknown status";
@@ -90,9 +90,14 @@ int paro_route(const paro_problem* p, const void* Q, const float* kbar, const do
   return from_hip(paro::launch_route(*p, Q, kbar, M, keep_k, lambda, idx, static_cast<hipStream_t>(stream)));
 }
 
+size_t paro_attention_workspace_bytes(const paro_problem* p) {
+  if (check_problem(p) != PARO_OK) return 0;
+  return paro::attention_workspace_bytes(*p);
+}
+
 int paro_attention_mode(const paro_problem* p, const void* Q, const void* K, const void* V, const float* kbar,
                         const float* vsum, const float* Hbar, const int32_t* idx, int32_t keep_k, int32_t mode,
-                        void* O, void* stream) {
+                        void* O, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_problem(p);
   if (rc != PARO_OK) return rc;
   const int T = num_blocks(p);
@@ -100,14 +105,18 @@ int paro_attention_mode(const paro_problem* p, const void* Q, const void* K, con
   if (mode != PARO_TAIL_PISA && mode != PARO_TAIL_DROP && mode != PARO_TAIL_ZEROTH) return PARO_ERR_ARG;
   if ((rc = check_ptrs({Q, K, V, kbar, vsum, Hbar, O})) != PARO_OK) return rc;
   if (keep_k > 0 && (rc = check_ptrs({idx})) != PARO_OK) return rc;
-  return from_hip(paro::launch_attention(*p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode,
+  const size_t need = paro::attention_workspace_bytes(*p);
+  if (workspace_bytes < need) return PARO_ERR_WORKSPACE;
+  if (need > 0 && (rc = check_ptrs({workspace})) != PARO_OK) return rc;
+  return from_hip(paro::launch_attention(*p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, workspace,
                                          static_cast<hipStream_t>(stream)));
 }
 
 int paro_attention(const paro_problem* p, const void* Q, const void* K, const void* V, const float* kbar,
                    const float* vsum, const float* Hbar, const int32_t* idx, int32_t keep_k, void* O,
-                   void* stream) {
-  return paro_attention_mode(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, PARO_TAIL_PISA, O, stream);
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return paro_attention_mode(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, PARO_TAIL_PISA, O, workspace,
+                             workspace_bytes, stream);
 }
 
 }  // extern "C"

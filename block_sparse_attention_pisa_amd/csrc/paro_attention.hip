@@ -27,9 +27,11 @@
 //    beyond real attention logits) marks the wave, and after the pass the
 //    marked waves recompute their rows with m set to the exact maximum
 //    recorded during the first pass.
-//  * Stage 2 streams all T centroids in chunks of 32 through the same code
-//    (kbar as keys, vsum as values, converted to bf16 while staging), with the
-//    blocks of S_i and j >= T masked; the weights add n_j p to D and p to c.
+//  * Stage 2 streams all T centroids in chunks of 64 through the same staging
+//    and the same pipelined tile code as the exact tiles (kbar as keys, vsum
+//    as values, rounded to bf16 by a small kernel into a caller workspace),
+//    with the blocks of S_i and j >= T masked; the weights add n_j p to D and
+//    p to c.
 //  * Stage 3 forms r^T = Hbar^T q^T on MFMA (Hbar transposed into LDS in
 //    bf16) and adds (scale c) r before the division.
 //
@@ -61,10 +63,9 @@ struct Geo {
   static constexpr int BUF = KTILE + VTILE;                // one staging buffer (elements)
   static constexpr int NK = D / 16;                        // k-steps of S^T = K Q^T over the D dims
   static constexpr int NU = D / 32;                        // 32-dim output tiles
-  static constexpr int KPT = 64 * CG / kAttnThreads;       // exact-tile K chunks staged per thread
-  static constexpr int KCT = (32 * CG + kAttnThreads - 1) / kAttnThreads;  // centroid K chunks per thread
-  static constexpr int NR = (KPT > 2 * KCT ? KPT : 2 * KCT) + 2;          // staging registers (16 B)
-  static constexpr int VI = NR - 2;                                       // first V register
+  static constexpr int KPT = 64 * CG / kAttnThreads;       // K chunks staged per thread and tile
+  static constexpr int NR = KPT + 2;                       // staging registers (16 B)
+  static constexpr int VI = KPT;                           // first V register
   static_assert(D * HS <= 2 * BUF, "Hbar^T must fit in the staging buffers");
   static_assert(32 * CG == kAttnThreads || 32 * CG * 2 == kAttnThreads, "V items per thread");
 };
@@ -99,9 +100,7 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 
 // One step's data in flight, NR registers of 16 bytes per thread:
-//  exact tile (bf16): r[0..KPT) = K chunks; r[VI..VI+2) = 2 keys x 8 dims of V;
-//  centroid chunk (fp32, 32 centroids): r[0..2 KCT) = kbar chunks as float4
-//  pairs; r[VI..VI+2) = 1 centroid x 8 dims of vsum.
+// r[0..KPT) = K chunks; r[VI..VI+2) = 2 keys x 8 dims of V.
 // V items put consecutive lanes on consecutive keys, so each LDS write
 // instruction fills whole V^T rows.
 template <int D>
@@ -114,8 +113,6 @@ template <int D>
 struct StageOffs {
   uint32_t k[Geo<D>::KPT];   // K chunk i: row q / CG, chunk q % CG (q = tid + threads * i)
   uint32_t v;                // V rows 2 kp, 2 kp + 1 (this one and + D * 2), dims 8 dg
-  uint32_t ck[Geo<D>::KCT];  // kbar chunk i (fp32 rows, 32 bytes)
-  uint32_t cv;               // vsum row kc, dims 8 dg (32 bytes)
   __device__ __forceinline__ void init() {
     constexpr int CG = Geo<D>::CG;
     const int tid = threadIdx.x;
@@ -127,23 +124,19 @@ struct StageOffs {
     const int item = tid % (32 * CG);
     const int kp = item & 31, dg = item >> 5;
     v = static_cast<uint32_t>(2 * kp * D * 2 + 16 * dg);
-#pragma unroll
-    for (int i = 0; i < Geo<D>::KCT; ++i) {
-      const int q = min(tid + kAttnThreads * i, 32 * CG - 1);
-      ck[i] = static_cast<uint32_t>((q / CG) * D * 4 + 32 * (q % CG));
-    }
-    cv = static_cast<uint32_t>(kp * D * 4 + 32 * dg);
   }
 };
 
-// Exact tile of kv-block j (uniform): K rows and V rows of the block.
+// 64 rows of keys (from kr) and values (from vr), both bf16 [rows][D] with
+// `bytes` valid bytes from the base on (uniform): an exact tile (the K and V
+// rows of kv-block j) or a centroid chunk (kbar and vsum rows of 64
+// centroids, rounded to bf16 beforehand).
 template <int D>
-__device__ __forceinline__ void load_exact(const uint16_t* __restrict__ Kh, const uint16_t* __restrict__ Vh, int j,
-                                           int L, const StageOffs<D>& of, Stage<D>& st) {
+__device__ __forceinline__ void load_rows(const uint16_t* kr, const uint16_t* vr, uint32_t bytes,
+                                          const StageOffs<D>& of, Stage<D>& st) {
   constexpr int KPT = Geo<D>::KPT, VI = Geo<D>::VI;
-  const uint32_t bytes = static_cast<uint32_t>(L - 64 * j) * D * 2;
-  const auto rk = make_rsrc(Kh + static_cast<size_t>(64 * j) * D, bytes);
-  const auto rv = make_rsrc(Vh + static_cast<size_t>(64 * j) * D, bytes);
+  const auto rk = make_rsrc(kr, bytes);
+  const auto rv = make_rsrc(vr, bytes);
 #pragma unroll
   for (int i = 0; i < KPT; ++i) st.r[i] = bload(rk, of.k[i]);
   st.r[VI] = bload(rv, of.v);
@@ -172,43 +165,16 @@ __device__ __forceinline__ void store_exact(const Stage<D>& st, uint16_t* buf) {
       *reinterpret_cast<uint32_t*>(vt + (8 * dg + e) * VS + 2 * kp) = pair16(a[e >> 1], b[e >> 1], e & 1);
   }
 }
-// Tail chunk of 32 centroids [j0, j0 + 32) (j0 uniform): kbar rows -> K tile
-// rows 0..31, vsum rows -> keys 0..31 of the V^T tile (fp32 converted to bf16
-// on store).
-template <int D>
-__device__ __forceinline__ void load_centroids(const float* __restrict__ kb, const float* __restrict__ vs, int j0,
-                                               int T, const StageOffs<D>& of, Stage<D>& st) {
-  constexpr int KCT = Geo<D>::KCT, VI = Geo<D>::VI;
-  const uint32_t bytes = static_cast<uint32_t>(T - j0) * D * 4;
-  const auto rk = make_rsrc(kb + static_cast<size_t>(j0) * D, bytes);
-  const auto rv = make_rsrc(vs + static_cast<size_t>(j0) * D, bytes);
-#pragma unroll
-  for (int i = 0; i < KCT; ++i) {
-    st.r[2 * i] = bload(rk, of.ck[i]);
-    st.r[2 * i + 1] = bload(rk, of.ck[i] + 16);
-  }
-  st.r[VI] = bload(rv, of.cv);
-  st.r[VI + 1] = bload(rv, of.cv + 16);
-}
-template <int D>
-__device__ __forceinline__ void store_centroids(const Stage<D>& st, uint16_t* buf) {
-  constexpr int CG = Geo<D>::CG, KCT = Geo<D>::KCT, KS = Geo<D>::KS, VS = Geo<D>::VS, VI = Geo<D>::VI;
-  uint16_t* vt = buf + Geo<D>::KTILE;
-#pragma unroll
-  for (int i = 0; i < KCT; ++i) {
-    const int q = threadIdx.x + kAttnThreads * i;
-    if (q < 32 * CG)
-      *reinterpret_cast<uint4*>(buf + (q / CG) * KS + 8 * (q % CG)) =
-          to_bf16x8(as_f4(st.r[2 * i]), as_f4(st.r[2 * i + 1]));
-  }
-  if (threadIdx.x < 32 * CG) {
-    const int item = threadIdx.x;
-    const int kc = item & 31, dg = item >> 5;
-    const float4 x = as_f4(st.r[VI]), y = as_f4(st.r[VI + 1]);
-    const float a0[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vt[(8 * dg + e) * VS + kc] = f32_to_bf16(a0[e]);
-  }
+// kbar and vsum (fp32 [BH][T][D]) rounded to bf16 for the matrix cores.
+__global__ __launch_bounds__(256) void k_centroids_bf16(const float* __restrict__ kbar, const float* __restrict__ vsum,
+                                                        uint16_t* __restrict__ kb16, uint16_t* __restrict__ vs16,
+                                                        size_t n8) {
+  const size_t e = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= n8) return;
+  const float4* k4 = reinterpret_cast<const float4*>(kbar) + 2 * e;
+  const float4* v4 = reinterpret_cast<const float4*>(vsum) + 2 * e;
+  reinterpret_cast<uint4*>(kb16)[e] = to_bf16x8(k4[0], k4[1]);
+  reinterpret_cast<uint4*>(vs16)[e] = to_bf16x8(v4[0], v4[1]);
 }
 
 // ------------------------------------------------------------ compute
@@ -321,10 +287,12 @@ constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
 // the wave: the K operands of half 1 load during the MFMAs of half 0, the
 // softmax of half 0 runs between the MFMAs of half 1, the softmax of half 1
 // between the P V MFMAs of half 0, and every V operand is read one phase
-// ahead. kMask: the uniform 64-bit key mask km zeroes keys (partial block).
-// Returns this lane's sum of the weights.
-template <int D, bool kMask>
-__device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int voff, Acc<D>& a, uint64_t km) {
+// ahead. kMask: the uniform 64-bit key mask km zeroes keys (partial block,
+// centroids outside the tail). kLast: pl receives the weight of the key
+// flagged in kl. Returns this lane's sum of the weights.
+template <int D, bool kMask, bool kLast = false>
+__device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int voff, Acc<D>& a, uint64_t km,
+                                            uint64_t kl, float& pl) {
   constexpr int NK = Geo<D>::NK, NU = Geo<D>::NU, KS = Geo<D>::KS, VS = Geo<D>::VS;
   constexpr int NV = 2 * NU;
   constexpr int kValu = kMask ? 52 : 36;  // VALU instructions of one softmax half (approximate)
@@ -356,9 +324,9 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
     for (int h = 0; h < 2; ++h) v0[2 * u + h] = *reinterpret_cast<const bf16x8*>(vp + 32 * u * VS + 16 * h);
 #pragma unroll
   for (int ks = 0; ks < NKX; ++ks) s1 = mfma32x32x16(k1[ks], qop(ks), s1);
-  float pl = 0.f;
+  float pl0 = 0.f, pl1 = 0.f;
   bf16x8 p0[2], p1[2];
-  float ps = softmax_half<D, kMask, false>(s0, a, 0.f, static_cast<uint32_t>(km), 0u, p0, pl);
+  float ps = softmax_half<D, kMask, kLast>(s0, a, 0.f, static_cast<uint32_t>(km), static_cast<uint32_t>(kl), p0, pl0);
 #pragma unroll
   for (int i = 0; i < NKX; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
@@ -375,7 +343,9 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
   for (int u = 0; u < NU; ++u)
 #pragma unroll
     for (int h = 0; h < 2; ++h) a.o[u] = mfma32x32x16(v0[2 * u + h], p0[h], a.o[u]);
-  ps += softmax_half<D, kMask, false>(s1, a, 0.f, static_cast<uint32_t>(km >> 32), 0u, p1, pl);
+  ps += softmax_half<D, kMask, kLast>(s1, a, 0.f, static_cast<uint32_t>(km >> 32), static_cast<uint32_t>(kl >> 32), p1,
+                                      pl1);
+  if (kLast) pl = pl0 + pl1;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
@@ -394,7 +364,7 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const float* __restrict__ kbar, const float* __restrict__ vsum, const float* __restrict__ Hbar,
+    const uint16_t* __restrict__ kb16, const uint16_t* __restrict__ vs16, const float* __restrict__ Hbar,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ O, int L, int T, int keep_k, float scale, int nwg,
     int mode) {
   const bool tail = mode != kModeDrop, corr = mode == kModePisa;
@@ -487,11 +457,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   lds_barrier();
   const int nu = sh[0];
   const uint32_t* mymask = masks + qi * nw;
-  const float* kb = kbar + static_cast<size_t>(bh) * T * D;
-  const float* vs = vsum + static_cast<size_t>(bh) * T * D;
+  const uint16_t* kb = kb16 + static_cast<size_t>(bh) * T * D;
+  const uint16_t* vs = vs16 + static_cast<size_t>(bh) * T * D;
   // stage 2 chunks (none when U_i is empty or the tail is dropped; step 0
   // still stages centroid chunk 0 for the softmax reference)
-  const int nch = (tail && keep_k < T) ? ceil_div(T, 32) : 0;
+  const int nch = (tail && keep_k < T) ? ceil_div(T, 64) : 0;
 
   bool active = qvalid;
 #pragma unroll
@@ -501,23 +471,21 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
 
   // One stream of staged steps: step 0 = centroid chunk 0 (it also sets the
   // softmax reference), steps 1..nu = the exact tiles of the union, then
-  // centroid chunks 1..nch-1. Chunk c covers blocks [32 c, 32 c + 32).
+  // centroid chunks 1..nch-1. Chunk c covers blocks [64 c, 64 c + 64).
   const int nsteps = 1 + nu + (nch > 1 ? nch - 1 : 0);
   Stage<D> st;
   auto fetch = [&](int step) {
     if (step >= 1 && step <= nu) {
       const int j = __builtin_amdgcn_readfirstlane(ulist[step - 1]);
-      load_exact<D>(Kh, Vh, j, L, of, st);
+      const size_t base = static_cast<size_t>(64 * j) * D;
+      load_rows<D>(Kh + base, Vh + base, static_cast<uint32_t>(min(64, L - 64 * j) * D * 2), of, st);
     } else {
-      load_centroids<D>(kb, vs, step == 0 ? 0 : 32 * (step - nu), T, of, st);
+      const int c = step == 0 ? 0 : step - nu;
+      const size_t base = static_cast<size_t>(64 * c) * D;
+      load_rows<D>(kb + base, vs + base, static_cast<uint32_t>(min(64, T - 64 * c) * D * 2), of, st);
     }
   };
-  auto put = [&](int step, uint16_t* b) {
-    if (step >= 1 && step <= nu)
-      store_exact<D>(st, b);
-    else
-      store_centroids<D>(st, b);
-  };
+  auto put = [&](int step, uint16_t* b) { store_exact<D>(st, b); };
   auto advance = [&](int step) {
     if (step + 1 < nsteps) put(step + 1, buf + ((step + 1) & 1) * BUF);
     if (step + 2 < nsteps) fetch(step + 2);
@@ -534,14 +502,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     return active && ((mymask[j >> 5] >> (j & 31)) & 1u);
   };
   // keys of centroid chunk c left out of the tail: the blocks of S_i (this
-  // wave's membership word c) and blocks >= T
-  auto chunk_mask = [&](int c) {
-    uint32_t km = __builtin_amdgcn_readfirstlane(mymask[c]);
-    const int left = T - 32 * c;
-    if (left < 32) km |= ~0u << left;
-    return km;
+  // wave's membership words 2 c, 2 c + 1) and blocks >= T
+  auto past_T = [&](int c) {
+    const int left = T - 64 * c;
+    return left < 64 ? ~0ull << left : 0ull;
   };
-  const uint32_t past_T0 = T < 32 ? ~0u << T : 0u;  // keys of chunk 0 at blocks >= T
+  auto chunk_mask = [&](int c) {
+    // (readfirstlane yields a signed int: widen through uint32_t, not sign-extended)
+    uint64_t km = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(mymask[2 * c]));
+    if (2 * c + 1 < nw)
+      km |= static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(mymask[2 * c + 1]))) << 32;
+    return km | past_T(c);
+  };
   const uint64_t past_nlast = ~0ull << nlast;        // keys past the end of the last block
   // exact tiles 1..nfull are full blocks; a partial last block is always last
   const int nfull = (nu > 0 && ulist[nu - 1] == T - 1 && nlast < 64) ? nu - 1 : nu;
@@ -564,10 +536,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
                                  half_max_masked(s1, static_cast<uint32_t>(km >> 32))));
           }
         } else if (active) {
-          const int c = step == 0 ? 0 : step - nu;
+          const uint64_t km = past_T(step == 0 ? 0 : step - nu);
           const f32x16 s0 = qk_half<D>(bc + koff, a);
-          const int left = T - 32 * c;
-          mx = fmaxf(mx, half_max_masked(s0, left < 32 ? ~0u << left : 0u));
+          const f32x16 s1 = qk_half<D>(bc + koff + 32 * KS, a);
+          mx = fmaxf(mx, fmaxf(half_max_masked(s0, static_cast<uint32_t>(km)),
+                               half_max_masked(s1, static_cast<uint32_t>(km >> 32))));
         }
         advance(step);
       }
@@ -586,22 +559,31 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     {
       if (active) {
         f32x16 s0 = qk_half<D>(buf + koff, a);
+        f32x16 s1 = qk_half<D>(buf + koff + 32 * KS, a);
         float shift = 0.f;
         if (pass == 0) {
           // reference: the largest centroid logit of the chunk (computed with
           // the reference 0); a centroid logit is the mean of its block's key
           // logits, so the reference never exceeds the largest logit that
           // carries weight
-          const float v = half_max_masked(s0, past_T0);
+          const uint64_t km = past_T(0);
+          const float v = fmaxf(half_max_masked(s0, static_cast<uint32_t>(km)),
+                                half_max_masked(s1, static_cast<uint32_t>(km >> 32)));
           set_reference(a, v);
           shift = -v;
         }
         if (nch > 0) {
-          bf16x8 p0[2];
-          const float ps = softmax_half<D, true, true, true>(s0, a, shift, chunk_mask(0),
-                                                             nch == 1 ? 1u << (T - 1) : 0u, p0, pl);
+          const uint64_t km = chunk_mask(0);
+          const uint64_t kl = nch == 1 ? 1ull << (T - 1) : 0ull;
+          bf16x8 p0[2], p1[2];
+          float pl0 = 0.f, pl1 = 0.f;
+          float ps = softmax_half<D, true, true, true>(s0, a, shift, static_cast<uint32_t>(km),
+                                                       static_cast<uint32_t>(kl), p0, pl0);
+          ps += softmax_half<D, true, true, true>(s1, a, shift, static_cast<uint32_t>(km >> 32),
+                                                  static_cast<uint32_t>(kl >> 32), p1, pl1);
           pv_half<D>(buf + voff, p0, a);
-          a.dsum += 64.f * ps + (static_cast<float>(nlast) - 64.f) * pl;
+          pv_half<D>(buf + voff + 32, p1, a);
+          a.dsum += 64.f * ps + (static_cast<float>(nlast) - 64.f) * (pl0 + pl1);
           a.csum += ps;
         }
       }
@@ -610,12 +592,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     // ---- exact tiles: full blocks, then the partial last block
     for (int step = 1; step <= nfull; ++step) {
       const uint16_t* bc = buf + (step & 1) * BUF;
-      if (mine_tile(step)) a.dsum += exact_tile<D, false>(bc, koff, voff, a, 0ull);
+      if (mine_tile(step)) a.dsum += exact_tile<D, false>(bc, koff, voff, a, 0ull, 0ull, pl);
       advance(step);
     }
     for (int step = nfull + 1; step <= nu; ++step) {
       const uint16_t* bc = buf + (step & 1) * BUF;
-      if (mine_tile(step)) a.dsum += exact_tile<D, true>(bc, koff, voff, a, past_nlast);
+      if (mine_tile(step)) a.dsum += exact_tile<D, true>(bc, koff, voff, a, past_nlast, 0ull, pl);
       advance(step);
     }
     // ---- centroid chunks 1..nch-2, then the last chunk (block T - 1 with its
@@ -623,10 +605,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     for (int step = nu + 1; step < nsteps - 1; ++step) {
       const uint16_t* bc = buf + (step & 1) * BUF;
       if (active) {
-        f32x16 s0 = qk_half<D>(bc + koff, a);
-        bf16x8 p0[2];
-        const float ps = softmax_half<D, true, false>(s0, a, 0.f, chunk_mask(step - nu), 0u, p0, pl);
-        pv_half<D>(bc + voff, p0, a);
+        const float ps = exact_tile<D, true>(bc, koff, voff, a, chunk_mask(step - nu), 0ull, pl);
         a.dsum += 64.f * ps;
         a.csum += ps;
       }
@@ -636,10 +615,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       const int step = nsteps - 1, c = nch - 1;
       const uint16_t* bc = buf + (step & 1) * BUF;
       if (active) {
-        f32x16 s0 = qk_half<D>(bc + koff, a);
-        bf16x8 p0[2];
-        const float ps = softmax_half<D, true, true>(s0, a, 0.f, chunk_mask(c), 1u << (T - 1 - 32 * c), p0, pl);
-        pv_half<D>(bc + voff, p0, a);
+        const float ps = exact_tile<D, true, true>(bc, koff, voff, a, chunk_mask(c), 1ull << (T - 1 - 64 * c), pl);
         a.dsum += 64.f * ps + (static_cast<float>(nlast) - 64.f) * pl;
         a.csum += ps;
       }
@@ -800,8 +776,14 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
 template <int D>
 hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
                        const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, int mode,
-                       hipStream_t s) {
+                       void* ws, hipStream_t s) {
   const int T = ceil_div(p.L, 64);
+  // kbar and vsum in bf16: ws = [kb16 | vs16], each [B H][T][D]
+  const size_t n = static_cast<size_t>(p.B) * p.H * T * D;
+  uint16_t* kb16 = static_cast<uint16_t*>(ws);
+  uint16_t* vs16 = kb16 + n;
+  hipLaunchKernelGGL(k_centroids_bf16, dim3(static_cast<unsigned>((n / 8 + 255) / 256)), dim3(256), 0, s, kbar, vsum,
+                     kb16, vs16, n / 8);
   const int nw = ceil_div(T, 32);
   const size_t lds = sizeof(uint16_t) * 2 * Geo<D>::BUF + sizeof(uint32_t) * kQB * nw + 12 * sizeof(int) +
                      sizeof(uint16_t) * T;
@@ -812,7 +794,7 @@ hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, cons
   const int nwg = ceil_div(T, kQB) * p.B * p.H;
   hipLaunchKernelGGL(k_attn_bf16<D>, dim3(nwg), dim3(kAttnThreads), lds_al, s,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
-                     static_cast<const uint16_t*>(V), kbar, vsum, Hbar, idx, static_cast<uint16_t*>(O), p.L, T,
+                     static_cast<const uint16_t*>(V), kb16, vs16, Hbar, idx, static_cast<uint16_t*>(O), p.L, T,
                      keep_k, static_cast<float>(p.scale), nwg, mode);
   return hipGetLastError();
 }
@@ -834,12 +816,17 @@ hipError_t launch_f32(const paro_problem& p, const void* Q, const void* K, const
 
 }  // namespace
 
+size_t attention_workspace_bytes(const paro_problem& p) {
+  if (p.dtype != PARO_DTYPE_BF16) return 0;
+  return 2 * static_cast<size_t>(p.B) * p.H * ceil_div(p.L, 64) * p.d * sizeof(uint16_t);
+}
+
 hipError_t launch_attention(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
                             const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, int mode,
-                            hipStream_t s) {
+                            void* ws, hipStream_t s) {
   if (p.dtype == PARO_DTYPE_BF16)
-    return p.d == 128 ? launch_bf16<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, s)
-                      : launch_bf16<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, s);
+    return p.d == 128 ? launch_bf16<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s)
+                      : launch_bf16<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s);
   return p.d == 128 ? launch_f32<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, s)
                     : launch_f32<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, s);
 }

@@ -109,6 +109,7 @@ hipError_t launch_route(const paro_problem& p, const void* Q, const float* kbar,
                         int keep_k, double lambda, int32_t* idx, hipStream_t s);
 hipError_t launch_attention(const paro_problem& p, const void* Q, const void* K, const void* V,
                             const float* kbar, const float* vsum, const float* Hbar, const int32_t* idx,
-                            int keep_k, void* O, int mode, hipStream_t s);
+                            int keep_k, void* O, int mode, void* ws, hipStream_t s);
+size_t attention_workspace_bytes(const paro_problem& p);
 int route_rows_per_group(int T, int d);
 }  // namespace paro

@@ -27,7 +27,7 @@ STATUS = {
 
 EXPORTED = (
     "paro_precompute", "paro_precompute_workspace_bytes", "paro_route", "paro_attention",
-    "paro_attention_mode",
+    "paro_attention_mode", "paro_attention_workspace_bytes",
     "paro_num_blocks", "paro_status_string", "paro_version",
 )
 
@@ -67,10 +67,12 @@ def lib() -> ctypes.CDLL:
         L.paro_precompute_workspace_bytes.restype = sz
         L.paro_route.argtypes = [pp, vp, vp, vp, i32, dbl, vp, vp]
         L.paro_route.restype = ctypes.c_int
-        L.paro_attention.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+        L.paro_attention.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
         L.paro_attention.restype = ctypes.c_int
-        L.paro_attention_mode.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp]
+        L.paro_attention_mode.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
         L.paro_attention_mode.restype = ctypes.c_int
+        L.paro_attention_workspace_bytes.argtypes = [pp]
+        L.paro_attention_workspace_bytes.restype = sz
         L.paro_num_blocks.argtypes = [i32, i32]
         L.paro_num_blocks.restype = i32
         L.paro_status_string.argtypes = [ctypes.c_int]
@@ -168,23 +170,34 @@ def route(q: torch.Tensor, kbar: torch.Tensor, M: torch.Tensor, keep_k: int, lam
 TAIL_PISA, TAIL_DROP, TAIL_ZEROTH = 0, 1, 2
 
 
+def attention_workspace_bytes(p: ParoProblem) -> int:
+    return int(lib().paro_attention_workspace_bytes(ctypes.byref(p)))
+
+
 def attention(q, k, v, kbar, vsum, Hbar, idx, keep_k: int, scale: float | None = None,
               out: torch.Tensor | None = None, drop_tail: bool = False,
-              first_order: bool = True) -> torch.Tensor:
+              first_order: bool = True, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Piecewise attention output [B, H, L, d] in the dtype of q.
 
     drop_tail=True drops U_i instead of approximating it (keep-or-drop
     sparse attention, the exact phase alone); first_order=False keeps the
-    zeroth-order tail but leaves out the first-order correction."""
+    zeroth-order tail but leaves out the first-order correction. workspace:
+    a device byte buffer of at least attention_workspace_bytes (allocated
+    here when not given)."""
     p = problem(q, scale)
     o = torch.empty_like(q) if out is None else out
     ptr = _dev(idx, "idx", torch.int32) if keep_k > 0 else None
+    nws = attention_workspace_bytes(p)
+    if nws > 0 and workspace is None:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    wptr = _dev(workspace, "workspace") if nws > 0 else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().paro_attention_mode(
         ctypes.byref(p), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
         _dev(kbar, "kbar", torch.float32), _dev(vsum, "vsum", torch.float32),
         _dev(Hbar, "Hbar", torch.float32), ptr, int(keep_k),
         TAIL_DROP if drop_tail else (TAIL_PISA if first_order else TAIL_ZEROTH),
-        _dev(o, "o", q.dtype), _stream()), "paro_attention_mode")
+        _dev(o, "o", q.dtype), wptr, wbytes, _stream()), "paro_attention_mode")
     return o
 
 

@@ -59,7 +59,7 @@ extern "C" {
 #define PARO_ERR_SHAPE (-2)     /* unsupported B, H, L, d, block, keep_k or T */
 #define PARO_ERR_DTYPE (-3)     /* unknown dtype code */
 #define PARO_ERR_ALIGN (-4)     /* a pointer is not 16-byte aligned */
-#define PARO_ERR_WORKSPACE (-5) /* workspace smaller than paro_precompute_workspace_bytes() */
+#define PARO_ERR_WORKSPACE (-5) /* workspace smaller than the call's *_workspace_bytes() */
 #define PARO_ERR_HIP (-6)       /* a kernel launch reported a HIP error */
 #define PARO_ERR_ARG (-7)       /* scale not finite and > 0, lambda not finite, or unknown mode */
 
@@ -134,6 +134,10 @@ int paro_route(const paro_problem* p, const void* Q, const float* kbar, const do
  *      indices in [0, T) in ascending order (as paro_route writes them);
  *      0 <= keep_k <= T.
  * out: O [B, H, L, d] (dtype; rows >= L of the last block are not written).
+ * workspace: device scratch of at least paro_attention_workspace_bytes(p)
+ *            bytes (bf16 copies of kbar and vsum for the matrix cores; 0
+ *            bytes, so NULL is allowed, for fp32 problems); contents on entry
+ *            are ignored and undefined on return.
  * bf16 problems use bf16 MFMA products with fp32 accumulation (tail
  * centroids, value sums and Hbar rounded to bf16 for the matrix cores);
  * fp32 problems use fp32 arithmetic throughout. An idx row that breaks the
@@ -141,7 +145,12 @@ int paro_route(const paro_problem* p, const void* Q, const float* kbar, const do
  */
 int paro_attention(const paro_problem* p, const void* Q, const void* K, const void* V,
                    const float* kbar, const float* vsum, const float* Hbar,
-                   const int32_t* idx, int32_t keep_k, void* O, void* stream);
+                   const int32_t* idx, int32_t keep_k, void* O, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace paro_attention and paro_attention_mode need for
+ * this problem (0 on bad shape, and 0 for fp32 problems). */
+size_t paro_attention_workspace_bytes(const paro_problem* p);
 
 /*
  * paro_attention_mode - paro_attention with the treatment of the tail U_i
@@ -161,7 +170,8 @@ int paro_attention(const paro_problem* p, const void* Q, const void* K, const vo
  */
 int paro_attention_mode(const paro_problem* p, const void* Q, const void* K, const void* V,
                         const float* kbar, const float* vsum, const float* Hbar,
-                        const int32_t* idx, int32_t keep_k, int32_t mode, void* O, void* stream);
+                        const int32_t* idx, int32_t keep_k, int32_t mode, void* O,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* T = ceil(L / block), or -1 when L < 1 or block < 1. */
 int32_t paro_num_blocks(int32_t L, int32_t block);

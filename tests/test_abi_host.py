@@ -73,7 +73,7 @@ def test_problem_validation(kw, code):
     ws = 1 << 30
     assert L.paro_precompute(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == code
     assert L.paro_route(ctypes.byref(p), FAKE, FAKE, FAKE, 2, 0.1, FAKE, None) == code
-    assert L.paro_attention(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, None) == code
+    assert L.paro_attention(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, ws, None) == code
 
 
 def test_pointer_and_argument_validation():
@@ -91,12 +91,17 @@ def test_pointer_and_argument_validation():
     assert L.paro_route(pp, FAKE, FAKE, FAKE, 2, float("inf"), FAKE, None) == -7
     assert L.paro_route(pp, FAKE, FAKE, FAKE, 2, 0.1, None, None) == -1
     assert L.paro_route(pp, FAKE, FAKE + 4, FAKE, 2, 0.1, FAKE, None) == -4
-    assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, FAKE, None) == -1
-    assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T + 1, FAKE, None) == -2
-    assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE + 2, None) == -4
-    assert L.paro_attention_mode(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 3, FAKE, None) == -7
-    assert L.paro_attention_mode(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, -1, FAKE, None) == -7
-    assert L.paro_attention_mode(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T + 1, 1, FAKE, None) == -2
+    wa = L.paro_attention_workspace_bytes(pp)
+    assert wa == 2 * 1 * 2 * T * 128 * 2   # bf16 copies of kbar and vsum
+    assert L.paro_attention_workspace_bytes(ctypes.byref(_p(dtype=1))) == 0
+    assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, FAKE, FAKE, wa, None) == -1
+    assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T + 1, FAKE, FAKE, wa, None) == -2
+    assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE + 2, FAKE, wa, None) == -4
+    assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, wa - 1, None) == -5
+    assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, None, wa, None) == -1
+    assert L.paro_attention_mode(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 3, FAKE, FAKE, wa, None) == -7
+    assert L.paro_attention_mode(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, -1, FAKE, FAKE, wa, None) == -7
+    assert L.paro_attention_mode(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T + 1, 1, FAKE, FAKE, wa, None) == -2
 
 
 def test_binding_refuses_host_tensors():
