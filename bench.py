@@ -11,6 +11,9 @@ the kv-blocks exact). Prints one JSON line:
              correction) over its mean launch time measured with HIP events
   exact_phase   the same attention kernel on the all-exact (keep = 100%)
                 control of the long-video shape, against the bf16 MFMA peak
+  reorder       the geometric token reordering (paro_reorder) of one
+                [B, H, L, d] tensor into the tiled order and back, against
+                the HBM peak (one read and one write of every row)
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -120,6 +123,30 @@ def traffic_entry():
         return rec["hbm_bytes_per_launch"]
     except Exception:
         return None
+
+
+def reorder_entry(w, x, out, reps: int = 5):
+    """paro_reorder of x [B, H, L, d] into the tiled order of the workload's
+    latent grid (gather) and back (scatter); algorithmic bytes = one read and
+    one write of the tensor."""
+    import torch
+    from block_sparse_attention_pisa_amd import paro
+    tile = (1, 8, 8) if w.grid[0] == 1 else (2, 4, 8)
+    stream = torch.cuda.current_stream()
+    nbytes = 2.0 * x.numel() * x.element_size()
+    res = {"tile_txy": list(tile), "bytes_per_call": nbytes}
+    for name, inv in (("gather", False), ("scatter", True)):
+        paro.reorder(x, w.grid, tile, inverse=inv, out=out)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            paro.reorder(x, w.grid, tile, inverse=inv, out=out)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "GBs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    return res
 
 
 def cpu_baseline(w, q, k, v, nq: int, nheads: int):
@@ -240,6 +267,7 @@ def main():
     torch.cuda.synchronize()
     ex_ms = ex_ev[0].elapsed_time(ex_ev[1]) / 3
     ex_tf = exact_flops / (ex_ms * 1e-3) / 1e12
+    reorder = reorder_entry(w, qd, out)
 
     # cold steps: L2 and MALL flushed by a 512 MB write before each step
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -296,6 +324,7 @@ def main():
                              "algorithmic_flops": exact_flops, "achieved": round(ex_tf, 2),
                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(ex_tf / PEAK_BF16_TFLOPS, 4)},
+        "reorder": reorder,
         "cold_ms_per_step": round(sorted(cold)[1], 4),
         "input_generation_s": round(t_gen, 1),
     }

@@ -1,6 +1,7 @@
 // C ABI of libparo: host-side argument validation, then the kernel launchers.
 // Validation touches no HIP API, so every error path runs without a device
 // and nothing is launched when an argument is rejected.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
@@ -37,9 +38,40 @@ int num_blocks(const paro_problem* p) { return (p->L + p->block - 1) / p->block;
 
 int from_hip(hipError_t e) { return e == hipSuccess ? PARO_OK : PARO_ERR_HIP; }
 
+// Checks a token grid against L and returns it with the tile extents clamped
+// to the grid extents (the same order, and products that stay within L).
+int check_grid(const paro_grid* g, int32_t L, paro_grid* out) {
+  if (!g) return PARO_ERR_NULL;
+  if (g->t < 1 || g->y < 1 || g->x < 1 || g->tile_t < 1 || g->tile_y < 1 || g->tile_x < 1) return PARO_ERR_SHAPE;
+  if (static_cast<int64_t>(g->t) * g->y * g->x > L) return PARO_ERR_SHAPE;
+  *out = *g;
+  out->tile_t = std::min(g->tile_t, g->t);
+  out->tile_y = std::min(g->tile_y, g->y);
+  out->tile_x = std::min(g->tile_x, g->x);
+  return PARO_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int paro_reorder(const paro_problem* p, const paro_grid* g, int32_t direction, const void* X, void* Y,
+                 void* stream) {
+  int rc = check_problem(p);
+  if (rc != PARO_OK) return rc;
+  paro_grid gc;
+  if ((rc = check_grid(g, p->L, &gc)) != PARO_OK) return rc;
+  if (direction != PARO_REORDER_GATHER && direction != PARO_REORDER_SCATTER) return PARO_ERR_ARG;
+  if ((rc = check_ptrs({X, Y})) != PARO_OK) return rc;
+  if (X == Y) return PARO_ERR_ARG;
+  return from_hip(paro::launch_reorder(*p, gc, direction, X, Y, static_cast<hipStream_t>(stream)));
+}
+
+int32_t paro_reorder_source(const paro_grid* g, int32_t L, int32_t i) {
+  paro_grid gc;
+  if (L < 1 || check_grid(g, L, &gc) != PARO_OK || i < 0 || i >= L) return -1;
+  return paro::reorder_source(gc, gc.t * gc.y * gc.x, i);
+}
 
 int32_t paro_num_blocks(int32_t L, int32_t block) {
   if (L < 1 || block < 1) return -1;
@@ -57,7 +89,7 @@ const char* paro_status_string(int status) {
     case PARO_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case PARO_ERR_WORKSPACE: return "workspace smaller than the call's *_workspace_bytes()";
     case PARO_ERR_HIP: return "a kernel launch reported a HIP error";
-    case PARO_ERR_ARG: return "scale must be finite and > 0, lambda finite, mode known";
+    case PARO_ERR_ARG: return "scale must be finite and > 0, lambda finite, mode or direction known, X != Y";
     default: return "unknown status";
   }
 }

@@ -111,5 +111,9 @@ hipError_t launch_attention(const paro_problem& p, const void* Q, const void* K,
                             const float* kbar, const float* vsum, const float* Hbar, const int32_t* idx,
                             int keep_k, void* O, int mode, void* ws, hipStream_t s);
 size_t attention_workspace_bytes(const paro_problem& p);
+// g must have its tile extents clamped to the grid extents.
+hipError_t launch_reorder(const paro_problem& p, const paro_grid& g, int direction, const void* X, void* Y,
+                          hipStream_t s);
+__host__ __device__ int reorder_source(const paro_grid& g, int N, int i);
 int route_rows_per_group(int T, int d);
 }  // namespace paro

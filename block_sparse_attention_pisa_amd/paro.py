@@ -27,9 +27,11 @@ STATUS = {
 
 EXPORTED = (
     "paro_precompute", "paro_precompute_workspace_bytes", "paro_route", "paro_attention",
-    "paro_attention_mode", "paro_attention_workspace_bytes",
-    "paro_num_blocks", "paro_status_string", "paro_version",
+    "paro_attention_mode", "paro_attention_workspace_bytes", "paro_reorder",
+    "paro_reorder_source", "paro_num_blocks", "paro_status_string", "paro_version",
 )
+REORDER_GATHER = 0
+REORDER_SCATTER = 1
 
 
 class ParoProblem(ctypes.Structure):
@@ -37,6 +39,13 @@ class ParoProblem(ctypes.Structure):
         ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
         ("d", ctypes.c_int32), ("block", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("scale", ctypes.c_double),
+    ]
+
+
+class ParoGrid(ctypes.Structure):
+    _fields_ = [
+        ("t", ctypes.c_int32), ("y", ctypes.c_int32), ("x", ctypes.c_int32),
+        ("tile_t", ctypes.c_int32), ("tile_y", ctypes.c_int32), ("tile_x", ctypes.c_int32),
     ]
 
 
@@ -73,6 +82,11 @@ def lib() -> ctypes.CDLL:
         L.paro_attention_mode.restype = ctypes.c_int
         L.paro_attention_workspace_bytes.argtypes = [pp]
         L.paro_attention_workspace_bytes.restype = sz
+        gp = ctypes.POINTER(ParoGrid)
+        L.paro_reorder.argtypes = [pp, gp, i32, vp, vp, vp]
+        L.paro_reorder.restype = ctypes.c_int
+        L.paro_reorder_source.argtypes = [gp, i32, i32]
+        L.paro_reorder_source.restype = i32
         L.paro_num_blocks.argtypes = [i32, i32]
         L.paro_num_blocks.restype = i32
         L.paro_status_string.argtypes = [ctypes.c_int]
@@ -206,12 +220,48 @@ def keep_to_k(keep: float, T: int) -> int:
     return min(T, max(0, -(-round(keep * 1000) * T // 1000)))
 
 
+def grid_spec(grid, tile) -> ParoGrid:
+    """paro_grid for a (t, y, x) latent grid cut into (tile_t, tile_y, tile_x) boxes."""
+    (t, y, x), (tt, ty, tx) = grid, tile
+    return ParoGrid(int(t), int(y), int(x), int(tt), int(ty), int(tx))
+
+
+def reorder(x: torch.Tensor, grid, tile, inverse: bool = False,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """Token rows of x [B, H, L, d] in the tiled order of the (t, y, x) grid
+    (inverse=False), or back to raster order (inverse=True). The first
+    t*y*x tokens are the grid in raster order; later tokens keep their places."""
+    p = problem(x)
+    g = grid_spec(grid, tile)
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    _check(lib().paro_reorder(ctypes.byref(p), ctypes.byref(g),
+                              REORDER_SCATTER if inverse else REORDER_GATHER,
+                              _dev(x, "x"), _dev(y, "out"), _stream()), "paro_reorder")
+    return y
+
+
+def reorder_source(grid, tile, L: int, i: int) -> int:
+    """Raster index of the token at tiled position i (host-side, no GPU), -1 on bad input."""
+    return int(lib().paro_reorder_source(ctypes.byref(grid_spec(grid, tile)), int(L), int(i)))
+
+
 def pisa_attention(q, k, v, keep_k: int | None = None, keep: float | None = None, lam: float = 0.1,
-                   scale: float | None = None) -> torch.Tensor:
-    """Whole path: precompute, route and fused attention on the current stream."""
+                   scale: float | None = None, grid=None, tile=None) -> torch.Tensor:
+    """Whole path: precompute, route and fused attention on the current stream.
+
+    With grid and tile, the tokens are first moved into the tiled order of
+    the latent grid (geometric reordering before blocking) and the output is
+    moved back to the raster order of the inputs."""
+    if (grid is None) != (tile is None):
+        raise ValueError("grid and tile go together")
+    if grid is not None:
+        q, k, v = (reorder(t, grid, tile) for t in (q, k, v))
     T = -(-q.shape[2] // BLOCK)
     if keep_k is None:
         keep_k = keep_to_k(0.125 if keep is None else keep, T)
     kbar, vsum, Hbar, M = precompute(k, v, scale=scale)
     idx = route(q, kbar, M, keep_k, lam, scale=scale)
-    return attention(q, k, v, kbar, vsum, Hbar, idx, keep_k, scale=scale)
+    o = attention(q, k, v, kbar, vsum, Hbar, idx, keep_k, scale=scale)
+    return o if grid is None else reorder(o, grid, tile, inverse=True)

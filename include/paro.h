@@ -61,7 +61,7 @@ extern "C" {
 #define PARO_ERR_ALIGN (-4)     /* a pointer is not 16-byte aligned */
 #define PARO_ERR_WORKSPACE (-5) /* workspace smaller than the call's *_workspace_bytes() */
 #define PARO_ERR_HIP (-6)       /* a kernel launch reported a HIP error */
-#define PARO_ERR_ARG (-7)       /* scale not finite and > 0, lambda not finite, or unknown mode */
+#define PARO_ERR_ARG (-7)       /* scale not finite and > 0, lambda not finite, unknown mode or direction, X == Y */
 
 #define PARO_TAIL_PISA 0  /* paro_attention_mode: zeroth-order tail and first-order correction */
 #define PARO_TAIL_DROP 1  /* paro_attention_mode: tail dropped (keep-or-drop sparse attention) */
@@ -172,6 +172,48 @@ int paro_attention_mode(const paro_problem* p, const void* Q, const void* K, con
                         const float* kbar, const float* vsum, const float* Hbar,
                         const int32_t* idx, int32_t keep_k, int32_t mode, void* O,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Geometric token reordering before blocking ("PAROAttention: Pattern-Aware
+ * ReOrdering for Efficient Sparse and Quantized Attention in Visual
+ * Generation Models", abstract: visual tokens are reordered so that their
+ * locally aggregating attention becomes block-wise before sparsification;
+ * "Adaptive Vector Quantized Attention" review, supplementary analysis: the
+ * token order measurably changes the quality of a blockwise approximation).
+ * The pages fix no concrete permutation; the order used here is the tiled
+ * raster order:
+ *   - the first t*y*x of the L tokens form a (t, y, x) latent grid in raster
+ *     order (x fastest); tokens after it (text tokens) keep their places;
+ *   - the grid is cut into boxes of tile_t x tile_y x tile_x tokens (boxes at
+ *     the far edges are cut short), the boxes are listed in raster order and
+ *     the tokens of each box in raster order.
+ * With tile = 2 x 4 x 8 or 4 x 4 x 4 every full box is exactly one block of
+ * 64 tokens, a compact piece of the latent instead of a slice of one row.
+ */
+typedef struct paro_grid {
+  int32_t t, y, x;                /* latent grid extents, each >= 1, t*y*x <= L */
+  int32_t tile_t, tile_y, tile_x; /* box extents, each >= 1 (larger than the grid = whole extent) */
+} paro_grid;
+
+#define PARO_REORDER_GATHER 0  /* Y[b,h,i,:] = X[b,h,src(i),:]: raster order -> tiled order */
+#define PARO_REORDER_SCATTER 1 /* Y[b,h,src(i),:] = X[b,h,i,:]: tiled order -> raster order */
+
+/*
+ * paro_reorder - moves the token rows of X [B, H, L, d] (dtype of p) into
+ * Y [B, H, L, d] in the tiled order of g (direction PARO_REORDER_GATHER) or
+ * back (PARO_REORDER_SCATTER), where src(i) is the raster index of the
+ * token at tiled position i. Rows are copied bit for bit. X and Y must not
+ * overlap (X == Y returns PARO_ERR_ARG; a partial overlap is not detected).
+ * A grid that does not fit L, or a non-positive extent, returns
+ * PARO_ERR_SHAPE; an unknown direction PARO_ERR_ARG. p->scale is ignored.
+ */
+int paro_reorder(const paro_problem* p, const paro_grid* g, int32_t direction, const void* X, void* Y,
+                 void* stream);
+
+/* src(i) of paro_reorder, computed on the host: the raster index of the token
+ * at tiled position i for L tokens, or -1 when g does not fit L or i is not
+ * in [0, L). */
+int32_t paro_reorder_source(const paro_grid* g, int32_t L, int32_t i);
 
 /* T = ceil(L / block), or -1 when L < 1 or block < 1. */
 int32_t paro_num_blocks(int32_t L, int32_t block);

@@ -109,3 +109,45 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros(1, 1, 64, 64)
     with pytest.raises(ValueError):
         paro.precompute(q, q)
+
+
+def _g(t, y, x, tt, ty, tx):
+    return paro.ParoGrid(t, y, x, tt, ty, tx)
+
+
+@pytest.mark.parametrize("grid,tile,extra", [
+    ((3, 7, 11), (2, 3, 4), 0), ((5, 9, 13), (4, 4, 4), 17), ((1, 33, 20), (1, 8, 8), 64),
+    ((21, 10, 16), (2, 4, 8), 3), ((4, 4, 4), (9, 9, 9), 0), ((2, 5, 3), (1, 1, 1), 5),
+    ((21, 45, 80), (2, 4, 8), 0), ((1, 64, 64), (1, 8, 8), 512), ((7, 1, 1), (3, 1, 1), 2),
+])
+def test_reorder_source_matches_oracle_order(grid, tile, extra):
+    """The library's arithmetic position -> source map (the one the reorder
+    kernel evaluates) equals the oracle's box-by-box enumeration."""
+    from oracle import reorder
+    N = grid[0] * grid[1] * grid[2]
+    L = N + extra
+    ref = reorder.tiled_order(grid, tile, L=L)
+    lib = paro.lib()
+    g = _g(*grid, *tile)
+    got = [lib.paro_reorder_source(ctypes.byref(g), L, i) for i in range(L)]
+    assert got == ref.tolist()
+
+
+def test_reorder_validation():
+    L = paro.lib()
+    p = _p(L=1000)
+    pp = ctypes.byref(p)
+    ok = _g(2, 10, 50, 2, 4, 8)
+    assert L.paro_reorder_source(ctypes.byref(ok), 1000, 999) == 999
+    assert L.paro_reorder_source(ctypes.byref(ok), 1000, 1000) == -1
+    assert L.paro_reorder_source(ctypes.byref(_g(2, 10, 51, 2, 4, 8)), 1000, 0) == -1
+    assert L.paro_reorder_source(None, 1000, 0) == -1
+    assert L.paro_reorder(pp, None, 0, FAKE, FAKE + 16, None) == -1
+    assert L.paro_reorder(pp, ctypes.byref(_g(2, 10, 51, 2, 4, 8)), 0, FAKE, FAKE + 16, None) == -2
+    assert L.paro_reorder(pp, ctypes.byref(_g(0, 10, 50, 2, 4, 8)), 0, FAKE, FAKE + 16, None) == -2
+    assert L.paro_reorder(pp, ctypes.byref(_g(2, 10, 50, 2, 0, 8)), 0, FAKE, FAKE + 16, None) == -2
+    assert L.paro_reorder(pp, ctypes.byref(ok), 2, FAKE, FAKE + 16, None) == -7
+    assert L.paro_reorder(pp, ctypes.byref(ok), 0, FAKE, FAKE, None) == -7
+    assert L.paro_reorder(pp, ctypes.byref(ok), 1, None, FAKE, None) == -1
+    assert L.paro_reorder(pp, ctypes.byref(ok), 1, FAKE, FAKE + 4, None) == -4
+    assert L.paro_reorder(ctypes.byref(_p(d=96)), ctypes.byref(ok), 0, FAKE, FAKE + 16, None) == -2
