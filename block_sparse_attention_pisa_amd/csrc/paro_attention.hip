@@ -373,7 +373,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   uint16_t* buf = reinterpret_cast<uint16_t*>(smem);  // 2 staging buffers
   const int nw = ceil_div(T, 32);
   uint32_t* masks = reinterpret_cast<uint32_t*>(smem + sizeof(uint16_t) * 2 * BUF);  // [kQB][nw]
-  int* sh = reinterpret_cast<int*>(masks + kQB * nw);                               // nu, rerun flags
+  uint32_t* ubits = masks + kQB * nw;  // [kQB][nw]: bit e = union tile e belongs to S_i of q-block qi
+  int* sh = reinterpret_cast<int*>(ubits + kQB * nw);                               // nu, rerun flags
   uint16_t* ulist = reinterpret_cast<uint16_t*>(sh + 12);                           // [T]
 
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so hand
@@ -456,7 +457,22 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   }
   lds_barrier();
   const int nu = sh[0];
+  // which union tiles each q-block computes, as bitmaps over the union
+  for (int e0 = 64 * w; e0 < nu; e0 += 64 * kWaves) {
+    const int e = e0 + l;
+    const int j = e < nu ? ulist[e] : 0;
+#pragma unroll
+    for (int q = 0; q < kQB; ++q) {
+      const uint64_t b = __ballot(e < nu && ((masks[q * nw + (j >> 5)] >> (j & 31)) & 1u));
+      if (l == 0) {
+        ubits[q * nw + (e0 >> 5)] = static_cast<uint32_t>(b);
+        if ((e0 >> 5) + 1 < nw) ubits[q * nw + (e0 >> 5) + 1] = static_cast<uint32_t>(b >> 32);
+      }
+    }
+  }
+  lds_barrier();
   const uint32_t* mymask = masks + qi * nw;
+  const uint32_t* mybits = ubits + qi * nw;
   const uint16_t* kb = kb16 + static_cast<size_t>(bh) * T * D;
   const uint16_t* vs = vs16 + static_cast<size_t>(bh) * T * D;
   // stage 2 chunks (none when U_i is empty or the tail is dropped; step 0
@@ -497,9 +513,20 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     lds_barrier();
     if (nsteps > 1) fetch(1);
   };
+  // whether this wave computes union tile `step`: one 64-bit word of its
+  // bitmap per 64 tiles, held in scalar registers
+  int mblk = -1;
+  uint64_t mword = 0;
   auto mine_tile = [&](int step) {
-    const int j = ulist[step - 1];
-    return active && ((mymask[j >> 5] >> (j & 31)) & 1u);
+    const int e = step - 1;
+    if ((e >> 6) != mblk) {
+      mblk = e >> 6;
+      const int i0 = 2 * mblk;
+      const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(mybits[i0]));
+      const uint32_t hi = i0 + 1 < nw ? static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(mybits[i0 + 1])) : 0u;
+      mword = (static_cast<uint64_t>(hi) << 32) | lo;
+    }
+    return active && ((mword >> (e & 63)) & 1ull);
   };
   // keys of centroid chunk c left out of the tail: the blocks of S_i (this
   // wave's membership words 2 c, 2 c + 1) and blocks >= T
@@ -785,7 +812,7 @@ hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, cons
   hipLaunchKernelGGL(k_centroids_bf16, dim3(static_cast<unsigned>((n / 8 + 255) / 256)), dim3(256), 0, s, kbar, vsum,
                      kb16, vs16, n / 8);
   const int nw = ceil_div(T, 32);
-  const size_t lds = sizeof(uint16_t) * 2 * Geo<D>::BUF + sizeof(uint32_t) * kQB * nw + 12 * sizeof(int) +
+  const size_t lds = sizeof(uint16_t) * 2 * Geo<D>::BUF + 2 * sizeof(uint32_t) * kQB * nw + 12 * sizeof(int) +
                      sizeof(uint16_t) * T;
   const size_t lds_al = (lds + 15) / 16 * 16;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_bf16<D>),
