@@ -55,7 +55,7 @@ constexpr int kModePisa = 0, kModeDrop = 1;
 template <int D>
 struct Geo {
   static constexpr int CG = D / 8;                         // 16-byte chunks in a K row
-  static constexpr int KS = D + 24;                        // K tile row stride: D dims, 16 reference dims, pad
+  static constexpr int KS = D + 24;                        // K tile row stride: D dims and padding
   static constexpr int VS = 64 + 8;                        // V^T tile row stride
   static constexpr int HS = D + 8;                         // Hbar^T row stride
   static constexpr int KTILE = 64 * KS;
@@ -182,6 +182,7 @@ template <int D>
 struct Acc {
   bf16x8 qb[Geo<D>::NK];   // B operand (scale log2(e) Q)^T in bf16: query lane % 32, dims 16 s + 8 g .. + 8
   bf16x8 qx;               // B operand of the reference k-step: -m of the lane's query (half 0 lanes, element 0)
+  bf16x8 kref;             // A operand of the reference k-step: 1 for every key (half 0 lanes, element 0)
   f32x16 o[Geo<D>::NU];    // O^T: dims 32 u + 8 (i / 4) + 4 g + i % 4, query lane % 32
   float m;                 // softmax reference (log2 units); the logits S^T come out as logit - m
   float dsum;              // this lane's part of D
@@ -197,8 +198,8 @@ __device__ __forceinline__ f32x16 qk_half(const uint16_t* kt, const Acc<D>& a) {
 #pragma unroll
   for (int ks = 0; ks < Geo<D>::NK; ++ks)
     s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kt + 16 * ks), a.qb[ks], s);
-  // reference k-step: K columns D.. hold (1, 0, ..), Q^T rows D.. hold (-m, 0, ..)
-  return mfma32x32x16(*reinterpret_cast<const bf16x8*>(kt + 16 * Geo<D>::NK), a.qx, s);
+  // reference k-step: a K column of ones against Q^T rows (-m, 0, ..)
+  return mfma32x32x16(a.kref, a.qx, s);
 }
 
 // O^T += V^T P^T for 32 keys (vt: the lane's V^T row base plus the key offset).
@@ -299,18 +300,19 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
   const uint16_t* kp = bc + koff;
   const uint16_t* vp = bc + voff;
   constexpr int NKX = NK + 1;  // the D dims plus the reference k-step
-  bf16x8 k0[NKX], k1[NKX], v0[NV], v1[NV];
+  bf16x8 k0[NK], k1[NK], v0[NV], v1[NV];
   auto qop = [&](int ks) { return ks < NK ? a.qb[ks] : a.qx; };
+  auto kop = [&](const bf16x8 (&k)[NK], int ks) { return ks < NK ? k[ks] : a.kref; };
   // region 1: K operands of half 0
 #pragma unroll
-  for (int ks = 0; ks < NKX; ++ks) k0[ks] = *reinterpret_cast<const bf16x8*>(kp + 16 * ks);
+  for (int ks = 0; ks < NK; ++ks) k0[ks] = *reinterpret_cast<const bf16x8*>(kp + 16 * ks);
   __builtin_amdgcn_sched_barrier(0);
   // region 2: S^T half 0 | K operands of half 1
 #pragma unroll
-  for (int ks = 0; ks < NKX; ++ks) k1[ks] = *reinterpret_cast<const bf16x8*>(kp + 32 * KS + 16 * ks);
+  for (int ks = 0; ks < NK; ++ks) k1[ks] = *reinterpret_cast<const bf16x8*>(kp + 32 * KS + 16 * ks);
   f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-  for (int ks = 0; ks < NKX; ++ks) s0 = mfma32x32x16(k0[ks], qop(ks), s0);
+  for (int ks = 0; ks < NKX; ++ks) s0 = mfma32x32x16(kop(k0, ks), qop(ks), s0);
 #pragma unroll
   for (int i = 0; i < NKX; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
@@ -323,7 +325,7 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
 #pragma unroll
     for (int h = 0; h < 2; ++h) v0[2 * u + h] = *reinterpret_cast<const bf16x8*>(vp + 32 * u * VS + 16 * h);
 #pragma unroll
-  for (int ks = 0; ks < NKX; ++ks) s1 = mfma32x32x16(k1[ks], qop(ks), s1);
+  for (int ks = 0; ks < NKX; ++ks) s1 = mfma32x32x16(kop(k1, ks), qop(ks), s1);
   float pl0 = 0.f, pl1 = 0.f;
   bf16x8 p0[2], p1[2];
   float ps = softmax_half<D, kMask, kLast>(s0, a, 0.f, static_cast<uint32_t>(km), static_cast<uint32_t>(kl), p0, pl0);
@@ -414,12 +416,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     }
     set_reference(a, 0.f);
   }
-  // reference columns of the K tiles (both buffers): key row . (1, 0, .., 0)
-  for (int e = tid; e < 2 * 64; e += kAttnThreads) {
-    uint16_t* kr = buf + (e / 64) * BUF + (e % 64) * KS + D;
-    *reinterpret_cast<uint4*>(kr) = make_uint4(0x3F80u, 0u, 0u, 0u);
-    *reinterpret_cast<uint4*>(kr + 8) = make_uint4(0u, 0u, 0u, 0u);
-  }
+  a.kref = __builtin_bit_cast(bf16x8, make_uint4(g == 0 ? 0x3F80u : 0u, 0u, 0u, 0u));
   StageOffs<D> of;
   of.init();
 
