@@ -55,6 +55,38 @@ int check_grid(const paro_grid* g, int32_t L, paro_grid* out) {
 
 extern "C" {
 
+size_t paro_attention_fp8_workspace_bytes(const paro_problem* p) {
+  if (check_problem(p) != PARO_OK) return 0;
+  return paro::attention_fp8_workspace_bytes(*p);
+}
+
+int paro_attention_fp8(const paro_problem* p, const void* Q, const void* K, const void* V, const float* kbar,
+                       const float* vsum, const float* Hbar, const int32_t* idx, int32_t keep_k, int32_t mode, void* O,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc != PARO_OK) return rc;
+  if (p->dtype != PARO_DTYPE_BF16) return PARO_ERR_DTYPE;
+  const int T = num_blocks(p);
+  if (keep_k < 0 || keep_k > T) return PARO_ERR_SHAPE;
+  if (mode != PARO_TAIL_PISA && mode != PARO_TAIL_DROP && mode != PARO_TAIL_ZEROTH) return PARO_ERR_ARG;
+  if ((rc = check_ptrs({Q, K, V, kbar, vsum, Hbar, O, workspace})) != PARO_OK) return rc;
+  if (keep_k > 0 && (rc = check_ptrs({idx})) != PARO_OK) return rc;
+  if (workspace_bytes < paro::attention_fp8_workspace_bytes(*p)) return PARO_ERR_WORKSPACE;
+  return from_hip(paro::launch_attention_fp8(*p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, workspace,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int paro_fp8_rows(const void* src, int32_t dtype, int64_t nrows, int32_t d, uint8_t* dst, uint8_t* scales,
+                  void* stream) {
+  if (dtype != PARO_DTYPE_BF16 && dtype != PARO_DTYPE_FP32) return PARO_ERR_DTYPE;
+  if (nrows < 1 || (d != 64 && d != 128) || nrows * d > INT64_C(1) << 40) return PARO_ERR_SHAPE;
+  int rc;
+  if ((rc = check_ptrs({src, dst})) != PARO_OK) return rc;
+  if (!scales) return PARO_ERR_NULL;
+  return from_hip(paro::launch_fp8_rows(src, dtype, static_cast<size_t>(nrows), d, dst, scales,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 int paro_reorder(const paro_problem* p, const paro_grid* g, int32_t direction, const void* X, void* Y,
                  void* stream) {
   int rc = check_problem(p);

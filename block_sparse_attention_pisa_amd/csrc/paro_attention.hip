@@ -52,22 +52,31 @@ constexpr int kAttnThreads = 64 * kWaves;
 // tail modes (the PARO_TAIL_* codes of the ABI; 2 = zeroth order only: tail on, correction off)
 constexpr int kModePisa = 0, kModeDrop = 1;
 
-template <int D>
+// Tile geometry. F8: K (and the centroid keys) are staged as fp8 e4m3 rows
+// of D bytes plus one power-of-two (E8M0) scale byte per row; V stays bf16.
+template <int D, bool F8 = false>
 struct Geo {
-  static constexpr int CG = D / 8;                         // 16-byte chunks in a K row
-  static constexpr int KS = D + 24;                        // K tile row stride: D dims and padding
+  static constexpr int CG = D / 8;                         // 16-byte chunks in a bf16 K row
+  static constexpr int KS = D + 24;                        // bf16 K tile row stride (elements): D dims and padding
+  static constexpr int KSB = D + 16;                       // fp8 K tile row stride (bytes): D dims and padding
   static constexpr int VS = 64 + 8;                        // V^T tile row stride
   static constexpr int HS = D + 8;                         // Hbar^T row stride
-  static constexpr int KTILE = 64 * KS;
+  // K tile (elements of 2 bytes); fp8: 64 rows, then the 64 row-scale bytes
+  static constexpr int KTILE = F8 ? (64 * KSB + 64) / 2 : 64 * KS;
   static constexpr int VTILE = D * VS;
   static constexpr int BUF = KTILE + VTILE;                // one staging buffer (elements)
-  static constexpr int NK = D / 16;                        // k-steps of S^T = K Q^T over the D dims
+  static constexpr int NK = D / 16;                        // bf16 k-steps of S^T = K Q^T over the D dims
+  static constexpr int NK8 = D / 64;                       // fp8 k-steps
   static constexpr int NU = D / 32;                        // 32-dim output tiles
-  static constexpr int KPT = 64 * CG / kAttnThreads;       // K chunks staged per thread and tile
-  static constexpr int NR = KPT + 2;                       // staging registers (16 B)
+  // K items (16 bytes) staged per thread and tile; fp8: 4 D items, threads < 4 D take one each
+  static constexpr int KPT = F8 ? 1 : 64 * CG / kAttnThreads;
   static constexpr int VI = KPT;                           // first V register
+  static constexpr int EI = KPT + 2;                       // fp8: the row-scale item (threads 0-3)
+  static constexpr int NR = KPT + 2 + (F8 ? 1 : 0);        // staging registers (16 B)
   static_assert(D * HS <= 2 * BUF, "Hbar^T must fit in the staging buffers");
   static_assert(32 * CG == kAttnThreads || 32 * CG * 2 == kAttnThreads, "V items per thread");
+  static_assert(!F8 || 4 * D <= kAttnThreads, "fp8 K items per thread");
+  static_assert(KTILE % 8 == 0, "V^T tile alignment");
 };
 
 // Key (tile row) that MFMA row m of S^T sub-tile t reads, chosen so that
@@ -103,23 +112,28 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // r[0..KPT) = K chunks; r[VI..VI+2) = 2 keys x 8 dims of V.
 // V items put consecutive lanes on consecutive keys, so each LDS write
 // instruction fills whole V^T rows.
-template <int D>
+template <int D, bool F8 = false>
 struct Stage {
-  uint4 r[Geo<D>::NR];
+  uint4 r[Geo<D, F8>::NR];
 };
 
 // Per-thread byte offsets of the staging loads inside a tile (constant).
-template <int D>
+template <int D, bool F8 = false>
 struct StageOffs {
-  uint32_t k[Geo<D>::KPT];   // K chunk i: row q / CG, chunk q % CG (q = tid + threads * i)
-  uint32_t v;                // V rows 2 kp, 2 kp + 1 (this one and + D * 2), dims 8 dg
+  uint32_t k[Geo<D, F8>::KPT];  // K chunk i: row q / CG, chunk q % CG (q = tid + threads * i);
+                                // fp8: row tid / (D / 16), chunk tid % (D / 16)
+  uint32_t v;                   // V rows 2 kp, 2 kp + 1 (this one and + D * 2), dims 8 dg
   __device__ __forceinline__ void init() {
     constexpr int CG = Geo<D>::CG;
     const int tid = threadIdx.x;
+    if (F8) {
+      k[0] = static_cast<uint32_t>((tid / (D / 16)) * D + 16 * (tid % (D / 16)));
+    } else {
 #pragma unroll
-    for (int i = 0; i < Geo<D>::KPT; ++i) {
-      const int q = tid + kAttnThreads * i;
-      k[i] = static_cast<uint32_t>((q / CG) * D * 2 + 16 * (q % CG));
+      for (int i = 0; i < Geo<D, F8>::KPT; ++i) {
+        const int q = tid + kAttnThreads * i;
+        k[i] = static_cast<uint32_t>((q / CG) * D * 2 + 16 * (q % CG));
+      }
     }
     const int item = tid % (32 * CG);
     const int kp = item & 31, dg = item >> 5;
@@ -131,14 +145,24 @@ struct StageOffs {
 // `bytes` valid bytes from the base on (uniform): an exact tile (the K and V
 // rows of kv-block j) or a centroid chunk (kbar and vsum rows of 64
 // centroids, rounded to bf16 beforehand).
-template <int D>
-__device__ __forceinline__ void load_rows(const uint16_t* kr, const uint16_t* vr, uint32_t bytes,
-                                          const StageOffs<D>& of, Stage<D>& st) {
-  constexpr int KPT = Geo<D>::KPT, VI = Geo<D>::VI;
-  const auto rk = make_rsrc(kr, bytes);
-  const auto rv = make_rsrc(vr, bytes);
+// fp8 (F8): kr holds rows of D bytes and ke one scale byte per row.
+template <int D, bool F8 = false>
+__device__ __forceinline__ void load_rows(const void* kr, const uint16_t* vr, const uint8_t* ke, int rows,
+                                          const StageOffs<D, F8>& of, Stage<D, F8>& st) {
+  constexpr int KPT = Geo<D, F8>::KPT, VI = Geo<D, F8>::VI;
+  const auto rk = make_rsrc(kr, static_cast<uint32_t>(rows * D * (F8 ? 1 : 2)));
+  const auto rv = make_rsrc(vr, static_cast<uint32_t>(rows * D * 2));
+  if (F8) {
+    if (threadIdx.x < 4 * D) st.r[0] = bload(rk, of.k[0]);
+    // the range check of a raw buffer load is per dword, so the scale bytes'
+    // range is rounded up to whole dwords (the bytes past the last row belong
+    // to masked keys; they lie inside the caller's workspace)
+    if (threadIdx.x < 4)
+      st.r[Geo<D, F8>::EI] = bload(make_rsrc(ke, static_cast<uint32_t>((rows + 3) & ~3)), 16 * threadIdx.x);
+  } else {
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) st.r[i] = bload(rk, of.k[i]);
+    for (int i = 0; i < KPT; ++i) st.r[i] = bload(rk, of.k[i]);
+  }
   st.r[VI] = bload(rv, of.v);
   st.r[VI + 1] = bload(rv, of.v + D * 2);
 }
@@ -146,14 +170,22 @@ __device__ __forceinline__ void load_rows(const uint16_t* kr, const uint16_t* vr
 __device__ __forceinline__ uint32_t pair16(uint32_t a, uint32_t b, bool high) {
   return __builtin_amdgcn_perm(b, a, high ? 0x07060302u : 0x05040100u);
 }
-template <int D>
-__device__ __forceinline__ void store_exact(const Stage<D>& st, uint16_t* buf) {
-  constexpr int CG = Geo<D>::CG, KPT = Geo<D>::KPT, KS = Geo<D>::KS, VS = Geo<D>::VS, VI = Geo<D>::VI;
-  uint16_t* vt = buf + Geo<D>::KTILE;
+template <int D, bool F8 = false>
+__device__ __forceinline__ void store_exact(const Stage<D, F8>& st, uint16_t* buf) {
+  constexpr int CG = Geo<D>::CG, KPT = Geo<D, F8>::KPT, KS = Geo<D>::KS, VS = Geo<D>::VS, VI = Geo<D, F8>::VI;
+  uint16_t* vt = buf + Geo<D, F8>::KTILE;
+  if (F8) {
+    constexpr int KSB = Geo<D>::KSB;
+    uint8_t* kb = reinterpret_cast<uint8_t*>(buf);
+    const int q = threadIdx.x;
+    if (q < 4 * D) *reinterpret_cast<uint4*>(kb + (q / (D / 16)) * KSB + 16 * (q % (D / 16))) = st.r[0];
+    if (q < 4) *reinterpret_cast<uint4*>(kb + 64 * KSB + 16 * q) = st.r[Geo<D, F8>::EI];
+  } else {
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int q = threadIdx.x + kAttnThreads * i;
-    *reinterpret_cast<uint4*>(buf + (q / CG) * KS + 8 * (q % CG)) = st.r[i];
+    for (int i = 0; i < KPT; ++i) {
+      const int q = threadIdx.x + kAttnThreads * i;
+      *reinterpret_cast<uint4*>(buf + (q / CG) * KS + 8 * (q % CG)) = st.r[i];
+    }
   }
   if (threadIdx.x < 32 * CG) {
     const int item = threadIdx.x;
@@ -165,22 +197,87 @@ __device__ __forceinline__ void store_exact(const Stage<D>& st, uint16_t* buf) {
       *reinterpret_cast<uint32_t*>(vt + (8 * dg + e) * VS + 2 * kp) = pair16(a[e >> 1], b[e >> 1], e & 1);
   }
 }
+// ------------------------------------------------------------ fp8
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// E8M0 code (exponent + 127) of the smallest power-of-two scale 2^e that
+// brings values of magnitude <= amax into the e4m3 range: amax 2^-e <= 448.
+__device__ __forceinline__ int e8m0_of(float amax) {
+  if (!(amax > 0.f)) return 127;
+  int p;
+  const float fr = frexpf(amax, &p);  // amax = fr 2^p, fr in [0.5, 1)
+  const int e = p - 9 + (fr * 512.f > 448.f ? 1 : 0);
+  return min(254, max(0, e + 127));
+}
+// Four floats (already scaled) -> four e4m3 bytes in one dword, first value
+// in the low byte (round to nearest even).
+__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
 // kbar and vsum (fp32 [BH][T][D]) rounded to bf16 for the matrix cores.
 __global__ __launch_bounds__(256) void k_centroids_bf16(const float* __restrict__ kbar, const float* __restrict__ vsum,
                                                         uint16_t* __restrict__ kb16, uint16_t* __restrict__ vs16,
                                                         size_t n8) {
   const size_t e = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   if (e >= n8) return;
-  const float4* k4 = reinterpret_cast<const float4*>(kbar) + 2 * e;
   const float4* v4 = reinterpret_cast<const float4*>(vsum) + 2 * e;
-  reinterpret_cast<uint4*>(kb16)[e] = to_bf16x8(k4[0], k4[1]);
   reinterpret_cast<uint4*>(vs16)[e] = to_bf16x8(v4[0], v4[1]);
+  if (kb16) {  // (the fp8 path keeps the centroid keys in e4m3 instead)
+    const float4* k4 = reinterpret_cast<const float4*>(kbar) + 2 * e;
+    reinterpret_cast<uint4*>(kb16)[e] = to_bf16x8(k4[0], k4[1]);
+  }
+}
+
+// Rows of D values (bf16 bits or fp32) -> e4m3 rows of D bytes, each row
+// scaled by the smallest power of two 2^e that brings it into the e4m3 range
+// (ex[row] = e + 127, the E8M0 code the fp8 MFMA applies). Consecutive lanes
+// share a row (16-byte loads), so the row maximum is a shuffle reduction.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_quant_rows(const E* __restrict__ src, size_t nrows, uint8_t* __restrict__ dst,
+                                                    uint8_t* __restrict__ ex) {
+  constexpr int EPT = 16 / static_cast<int>(sizeof(E));  // elements per thread
+  constexpr int TPR = D / EPT;                            // threads per row (divides 64)
+  const size_t t = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  const size_t r = t / TPR;
+  const int c = static_cast<int>(t % TPR);
+  const bool ok = r < nrows;
+  float x[EPT];
+  const uint4 v = ok ? *reinterpret_cast<const uint4*>(src + r * D + static_cast<size_t>(c) * EPT) : make_uint4(0, 0, 0, 0);
+  if constexpr (EPT == 8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32(static_cast<uint16_t>(half16(v, e)));
+  } else {
+    const float4 f = as_f4(v);
+    x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+  for (int o = 1; o < TPR; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  const int code = e8m0_of(amax);
+  const int sh = 127 - code;
+  if (!ok) return;
+  uint8_t* out = dst + r * D + static_cast<size_t>(c) * EPT;
+  if constexpr (EPT == 8) {
+    *reinterpret_cast<uint2*>(out) =
+        make_uint2(static_cast<uint32_t>(pack_fp8x4(ldexpf(x[0], sh), ldexpf(x[1], sh), ldexpf(x[2], sh), ldexpf(x[3], sh))),
+                   static_cast<uint32_t>(pack_fp8x4(ldexpf(x[4], sh), ldexpf(x[5], sh), ldexpf(x[6], sh), ldexpf(x[7], sh))));
+  } else {
+    *reinterpret_cast<uint32_t*>(out) =
+        static_cast<uint32_t>(pack_fp8x4(ldexpf(x[0], sh), ldexpf(x[1], sh), ldexpf(x[2], sh), ldexpf(x[3], sh)));
+  }
+  if (c == 0) ex[r] = static_cast<uint8_t>(code);
 }
 
 // ------------------------------------------------------------ compute
 template <int D>
 struct Acc {
   bf16x8 qb[Geo<D>::NK];   // B operand (scale log2(e) Q)^T in bf16: query lane % 32, dims 16 s + 8 g .. + 8
+  i32x8 q8[Geo<D>::NK8];   // fp8 path: B operand (scale log2(e) Q)^T 2^-qe in e4m3: dims 64 s + 32 g .. + 32
+  int qe;                  // fp8 path: E8M0 code of the lane's query scale
   bf16x8 qx;               // B operand of the reference k-step: -m of the lane's query (half 0 lanes, element 0)
   bf16x8 kref;             // A operand of the reference k-step: 1 for every key (half 0 lanes, element 0)
   f32x16 o[Geo<D>::NU];    // O^T: dims 32 u + 8 (i / 4) + 4 g + i % 4, query lane % 32
@@ -199,6 +296,23 @@ __device__ __forceinline__ f32x16 qk_half(const uint16_t* kt, const Acc<D>& a) {
   for (int ks = 0; ks < Geo<D>::NK; ++ks)
     s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kt + 16 * ks), a.qb[ks], s);
   // reference k-step: a K column of ones against Q^T rows (-m, 0, ..)
+  return mfma32x32x16(a.kref, a.qx, s);
+}
+
+// fp8 path: S^T of 32 keys (kt: the lane's permuted fp8 K row plus 32 g
+// bytes; sa: the E8M0 code of that row's scale). The two operands carry
+// their power-of-two scales into the MFMA, which applies them.
+template <int D>
+__device__ __forceinline__ f32x16 qk_half8(const uint8_t* kt, int sa, const Acc<D>& a) {
+  f32x16 s = f32x16{};
+#pragma unroll
+  for (int st = 0; st < Geo<D>::NK8; ++st) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(kt + 64 * st);
+    const uint4 hi = *reinterpret_cast<const uint4*>(kt + 64 * st + 16);
+    const i32x8 kk = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                      static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+    s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kk, a.q8[st], s, 0, 0, 0, sa, 0, a.qe);
+  }
   return mfma32x32x16(a.kref, a.qx, s);
 }
 
@@ -363,14 +477,114 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
   return ps;
 }
 
-template <int D>
+// exact_tile with S^T = K Q^T on the fp8 matrix cores (two 32x32x64 e4m3
+// MFMAs per 32 keys instead of eight bf16 ones); kb: the lane's fp8 K row
+// base (tile base + perm_key(0, ql) row + 32 g bytes), sc: the tile's
+// row-scale bytes. Softmax and P V are those of exact_tile.
+template <int D, bool kMask, bool kLast = false>
+__device__ __forceinline__ float exact_tile8(const uint8_t* kb, const uint8_t* sc, int ql, const uint16_t* bc,
+                                             int voff, Acc<D>& a, uint64_t km, uint64_t kl, float& pl) {
+  constexpr int NK8 = Geo<D>::NK8, NU = Geo<D>::NU, KSB = Geo<D>::KSB, VS = Geo<D>::VS;
+  constexpr int NV = 2 * NU;
+  constexpr int kValu = kMask ? 52 : 36;
+  constexpr int NKX = NK8 + 1;
+  const uint16_t* vp = bc + voff;
+  i32x8 k0[NK8], k1[NK8];
+  bf16x8 v0[NV], v1[NV];
+  auto ld = [&](const uint8_t* p) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(p);
+    const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
+    return i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                 static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+  };
+  // region 1: K operands of half 0, the row scales of both halves
+#pragma unroll
+  for (int st = 0; st < NK8; ++st) k0[st] = ld(kb + 64 * st);
+  const int sa0 = sc[perm_key(0, ql)], sa1 = sc[perm_key(1, ql)];
+  __builtin_amdgcn_sched_barrier(0);
+  // region 2: S^T half 0 | K operands of half 1
+#pragma unroll
+  for (int st = 0; st < NK8; ++st) k1[st] = ld(kb + 32 * KSB + 64 * st);
+  f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+  for (int st = 0; st < NK8; ++st)
+    s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k0[st], a.q8[st], s0, 0, 0, 0, sa0, 0, a.qe);
+  s0 = mfma32x32x16(a.kref, a.qx, s0);
+#pragma unroll
+  for (int i = 0; i < NKX; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // region 3: S^T half 1 | softmax of half 0 | V operands of half 0
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) v0[2 * u + h] = *reinterpret_cast<const bf16x8*>(vp + 32 * u * VS + 16 * h);
+#pragma unroll
+  for (int st = 0; st < NK8; ++st)
+    s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k1[st], a.q8[st], s1, 0, 0, 0, sa1, 0, a.qe);
+  s1 = mfma32x32x16(a.kref, a.qx, s1);
+  float pl0 = 0.f, pl1 = 0.f;
+  bf16x8 p0[2], p1[2];
+  float ps = softmax_half<D, kMask, kLast>(s0, a, 0.f, static_cast<uint32_t>(km), static_cast<uint32_t>(kl), p0, pl0);
+#pragma unroll
+  for (int i = 0; i < NKX; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, (kValu + NKX - 1) / NKX, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, (NV + NKX - 1) / NKX, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // region 4: P V half 0 | softmax of half 1 | V operands of half 1
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) v1[2 * u + h] = *reinterpret_cast<const bf16x8*>(vp + 32 + 32 * u * VS + 16 * h);
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) a.o[u] = mfma32x32x16(v0[2 * u + h], p0[h], a.o[u]);
+  ps += softmax_half<D, kMask, kLast>(s1, a, 0.f, static_cast<uint32_t>(km >> 32), static_cast<uint32_t>(kl >> 32), p1,
+                                      pl1);
+  if (kLast) pl = pl0 + pl1;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, (kValu + NV - 1) / NV, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // region 5: P V half 1
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) a.o[u] = mfma32x32x16(v1[2 * u + h], p1[h], a.o[u]);
+  return ps;
+}
+
+// One tile through the bf16 or the fp8 (F8) S^T path.
+template <int D, bool F8, bool kMask, bool kLast = false>
+__device__ __forceinline__ float run_tile(const uint16_t* bc, int koff, int koff8, int ql, int voff, Acc<D>& a,
+                                          uint64_t km, uint64_t kl, float& pl) {
+  if constexpr (F8) {
+    const uint8_t* b8 = reinterpret_cast<const uint8_t*>(bc);
+    return exact_tile8<D, kMask, kLast>(b8 + koff8, b8 + 64 * Geo<D>::KSB, ql, bc, voff, a, km, kl, pl);
+  } else {
+    return exact_tile<D, kMask, kLast>(bc, koff, voff, a, km, kl, pl);
+  }
+}
+
+// F8: the exact keys come from k8 (e4m3 rows) and ke (their E8M0 scales), the
+// centroid keys from kb8 and kbe; otherwise from K and kb16 (bf16).
+template <int D, bool F8>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ kb16, const uint16_t* __restrict__ vs16, const float* __restrict__ Hbar,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ O, int L, int T, int keep_k, float scale, int nwg,
-    int mode) {
+    int mode, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ ke, const uint8_t* __restrict__ kb8,
+    const uint8_t* __restrict__ kbe) {
   const bool tail = mode != kModeDrop, corr = mode == kModePisa;
-  constexpr int BUF = Geo<D>::BUF, KS = Geo<D>::KS, VS = Geo<D>::VS, HS = Geo<D>::HS;
+  constexpr int BUF = Geo<D, F8>::BUF, KS = Geo<D>::KS, KSB = Geo<D>::KSB, VS = Geo<D>::VS, HS = Geo<D>::HS;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* buf = reinterpret_cast<uint16_t*>(smem);  // 2 staging buffers
   const int nw = ceil_div(T, 32);
@@ -399,7 +613,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   const int nlast = L - 64 * (T - 1);
   // per-lane operand offsets inside a staging buffer
   const int koff = perm_key(0, ql) * KS + 8 * g;              // K rows of sub-tile 0 (+32 KS for 1)
-  const int voff = Geo<D>::KTILE + ql * VS + 8 * g;           // V^T rows 32 u + ql (+16 s + 32 t keys)
+  const int koff8 = perm_key(0, ql) * KSB + 32 * g;           // fp8: bytes, (+32 KSB for sub-tile 1)
+  const int voff = Geo<D, F8>::KTILE + ql * VS + 8 * g;       // V^T rows 32 u + ql (+16 s + 32 t keys)
 
   Acc<D> a;
   {
@@ -416,8 +631,53 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     }
     set_reference(a, 0.f);
   }
+  if constexpr (F8) {
+    // e4m3 copy of the lane's query dims 64 s + 32 g .. + 32, with one
+    // power-of-two scale per query (both lanes of the query agree on it)
+    constexpr int NK8 = Geo<D>::NK8;
+    float x[NK8][32];
+    float amax = 0.f;
+    const uint16_t* qp = Q + head + static_cast<size_t>(row) * D + 32 * g;
+#pragma unroll
+    for (int st = 0; st < NK8; ++st)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 v = (qvalid && row < L) ? *reinterpret_cast<const uint4*>(qp + 64 * st + 8 * c) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[st][8 * c + e] = bf16_to_f32(static_cast<uint16_t>(half16(v, e))) * cl2;
+          amax = fmaxf(amax, fabsf(x[st][8 * c + e]));
+        }
+      }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    a.qe = e8m0_of(amax);
+    const int ex = 127 - a.qe;
+#pragma unroll
+    for (int st = 0; st < NK8; ++st)
+#pragma unroll
+      for (int wd = 0; wd < 8; ++wd)
+        a.q8[st][wd] = pack_fp8x4(ldexpf(x[st][4 * wd], ex), ldexpf(x[st][4 * wd + 1], ex),
+                                  ldexpf(x[st][4 * wd + 2], ex), ldexpf(x[st][4 * wd + 3], ex));
+    // the bf16 operand of the correction holds the same rounded q' (an e4m3
+    // value times a power of two is exact in bf16), so every use of q' on
+    // this path sees one rounding
+    const uint16_t* qb16 = Q + head + static_cast<size_t>(row) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < Geo<D>::NK; ++ks) {
+      const uint4 v = (qvalid && row < L) ? *reinterpret_cast<const uint4*>(qb16 + 16 * ks) : make_uint4(0, 0, 0, 0);
+      float r[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y = bf16_to_f32(static_cast<uint16_t>(half16(v, e))) * cl2;
+        const int c8 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(y, ex), 0.f, 0, false);
+        r[e] = ldexpf(__builtin_amdgcn_cvt_f32_fp8(c8, 0), -ex);
+      }
+      a.qb[ks] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]),
+                                                      pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7])));
+    }
+  }
   a.kref = __builtin_bit_cast(bf16x8, make_uint4(g == 0 ? 0x3F80u : 0u, 0u, 0u, 0u));
-  StageOffs<D> of;
+  StageOffs<D, F8> of;
   of.init();
 
   // ---- membership masks of the 4 exact lists and their sorted union
@@ -486,19 +746,36 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   // softmax reference), steps 1..nu = the exact tiles of the union, then
   // centroid chunks 1..nch-1. Chunk c covers blocks [64 c, 64 c + 64).
   const int nsteps = 1 + nu + (nch > 1 ? nch - 1 : 0);
-  Stage<D> st;
+  Stage<D, F8> st;
   auto fetch = [&](int step) {
     if (step >= 1 && step <= nu) {
       const int j = __builtin_amdgcn_readfirstlane(ulist[step - 1]);
       const size_t base = static_cast<size_t>(64 * j) * D;
-      load_rows<D>(Kh + base, Vh + base, static_cast<uint32_t>(min(64, L - 64 * j) * D * 2), of, st);
+      if (F8)
+        load_rows<D, F8>(k8 + head + base, Vh + base, ke + static_cast<size_t>(bh) * L + 64 * j, min(64, L - 64 * j), of,
+                         st);
+      else
+        load_rows<D, F8>(Kh + base, Vh + base, nullptr, min(64, L - 64 * j), of, st);
     } else {
       const int c = step == 0 ? 0 : step - nu;
       const size_t base = static_cast<size_t>(64 * c) * D;
-      load_rows<D>(kb + base, vs + base, static_cast<uint32_t>(min(64, T - 64 * c) * D * 2), of, st);
+      if (F8)
+        load_rows<D, F8>(kb8 + static_cast<size_t>(bh) * T * D + base, vs + base,
+                         kbe + static_cast<size_t>(bh) * T + 64 * c, min(64, T - 64 * c), of, st);
+      else
+        load_rows<D, F8>(kb + base, vs + base, nullptr, min(64, T - 64 * c), of, st);
     }
   };
-  auto put = [&](int step, uint16_t* b) { store_exact<D>(st, b); };
+  auto put = [&](int step, uint16_t* b) { store_exact<D, F8>(st, b); };
+  // S^T of sub-tile t (keys 32 t ..) of a staged tile, either path
+  auto s_half = [&](const uint16_t* bc, int t) -> f32x16 {
+    if constexpr (F8) {
+      const uint8_t* b8 = reinterpret_cast<const uint8_t*>(bc);
+      return qk_half8<D>(b8 + koff8 + 32 * t * KSB, b8[64 * KSB + perm_key(t, ql)], a);
+    } else {
+      return qk_half<D>(bc + koff + 32 * t * KS, a);
+    }
+  };
   auto advance = [&](int step) {
     if (step + 1 < nsteps) put(step + 1, buf + ((step + 1) & 1) * BUF);
     if (step + 2 < nsteps) fetch(step + 2);
@@ -554,15 +831,15 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
         if (step >= 1 && step <= nu) {
           if (mine_tile(step)) {
             const uint64_t km = step > nfull ? past_nlast : 0ull;
-            const f32x16 s0 = qk_half<D>(bc + koff, a);
-            const f32x16 s1 = qk_half<D>(bc + koff + 32 * KS, a);
+            const f32x16 s0 = s_half(bc, 0);
+            const f32x16 s1 = s_half(bc, 1);
             mx = fmaxf(mx, fmaxf(half_max_masked(s0, static_cast<uint32_t>(km)),
                                  half_max_masked(s1, static_cast<uint32_t>(km >> 32))));
           }
         } else if (active) {
           const uint64_t km = past_T(step == 0 ? 0 : step - nu);
-          const f32x16 s0 = qk_half<D>(bc + koff, a);
-          const f32x16 s1 = qk_half<D>(bc + koff + 32 * KS, a);
+          const f32x16 s0 = s_half(bc, 0);
+          const f32x16 s1 = s_half(bc, 1);
           mx = fmaxf(mx, fmaxf(half_max_masked(s0, static_cast<uint32_t>(km)),
                                half_max_masked(s1, static_cast<uint32_t>(km >> 32))));
         }
@@ -582,8 +859,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     // ---- step 0: centroid chunk 0
     {
       if (active) {
-        f32x16 s0 = qk_half<D>(buf + koff, a);
-        f32x16 s1 = qk_half<D>(buf + koff + 32 * KS, a);
+        f32x16 s0 = s_half(buf, 0);
+        f32x16 s1 = s_half(buf, 1);
         float shift = 0.f;
         if (pass == 0) {
           // reference: the largest centroid logit of the chunk (computed with
@@ -616,12 +893,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     // ---- exact tiles: full blocks, then the partial last block
     for (int step = 1; step <= nfull; ++step) {
       const uint16_t* bc = buf + (step & 1) * BUF;
-      if (mine_tile(step)) a.dsum += exact_tile<D, false>(bc, koff, voff, a, 0ull, 0ull, pl);
+      if (mine_tile(step)) a.dsum += run_tile<D, F8, false>(bc, koff, koff8, ql, voff, a, 0ull, 0ull, pl);
       advance(step);
     }
     for (int step = nfull + 1; step <= nu; ++step) {
       const uint16_t* bc = buf + (step & 1) * BUF;
-      if (mine_tile(step)) a.dsum += exact_tile<D, true>(bc, koff, voff, a, past_nlast, 0ull, pl);
+      if (mine_tile(step)) a.dsum += run_tile<D, F8, true>(bc, koff, koff8, ql, voff, a, past_nlast, 0ull, pl);
       advance(step);
     }
     // ---- centroid chunks 1..nch-2, then the last chunk (block T - 1 with its
@@ -629,7 +906,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     for (int step = nu + 1; step < nsteps - 1; ++step) {
       const uint16_t* bc = buf + (step & 1) * BUF;
       if (active) {
-        const float ps = exact_tile<D, true>(bc, koff, voff, a, chunk_mask(step - nu), 0ull, pl);
+        const float ps = run_tile<D, F8, true>(bc, koff, koff8, ql, voff, a, chunk_mask(step - nu), 0ull, pl);
         a.dsum += 64.f * ps;
         a.csum += ps;
       }
@@ -639,7 +916,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       const int step = nsteps - 1, c = nch - 1;
       const uint16_t* bc = buf + (step & 1) * BUF;
       if (active) {
-        const float ps = exact_tile<D, true, true>(bc, koff, voff, a, chunk_mask(c), 1ull << (T - 1 - 64 * c), pl);
+        const float ps =
+            run_tile<D, F8, true, true>(bc, koff, koff8, ql, voff, a, chunk_mask(c), 1ull << (T - 1 - 64 * c), pl);
         a.dsum += 64.f * ps + (static_cast<float>(nlast) - 64.f) * pl;
         a.csum += ps;
       }
@@ -797,29 +1075,69 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
   }
 }
 
-template <int D>
+// Workspace of the bf16 problems (byte offsets, each region 256-byte aligned).
+// bf16 path: [kb16 | vs16], kbar and vsum in bf16, each [B H][T][D].
+// fp8 path: [k8 | ke | kb8 | kbe | vs16]: K in e4m3 [B H][L][D] and its row
+// scale codes [B H][L], kbar likewise ([B H][T][D], [B H][T]), vsum in bf16.
+struct WsLayout {
+  size_t k8, ke, kb8, kbe, vs16, kb16, total;
+};
+__host__ inline size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+__host__ inline WsLayout ws_layout(const paro_problem& p, bool fp8) {
+  const size_t bh = static_cast<size_t>(p.B) * p.H, T = ceil_div(p.L, 64), d = p.d;
+  WsLayout w{};
+  if (fp8) {
+    w.k8 = 0;
+    w.ke = up256(bh * p.L * d);
+    w.kb8 = w.ke + up256(bh * p.L);
+    w.kbe = w.kb8 + up256(bh * T * d);
+    w.vs16 = w.kbe + up256(bh * T);
+    w.total = w.vs16 + up256(bh * T * d * 2);
+  } else {
+    w.kb16 = 0;
+    w.vs16 = up256(bh * T * d * 2);
+    w.total = w.vs16 + up256(bh * T * d * 2);
+  }
+  return w;
+}
+
+template <int D, bool F8>
 hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
                        const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, int mode,
                        void* ws, hipStream_t s) {
   const int T = ceil_div(p.L, 64);
-  // kbar and vsum in bf16: ws = [kb16 | vs16], each [B H][T][D]
-  const size_t n = static_cast<size_t>(p.B) * p.H * T * D;
-  uint16_t* kb16 = static_cast<uint16_t*>(ws);
-  uint16_t* vs16 = kb16 + n;
+  const size_t bh = static_cast<size_t>(p.B) * p.H;
+  const size_t n = bh * T * D;
+  const WsLayout lay = ws_layout(p, F8);
+  unsigned char* wb = static_cast<unsigned char*>(ws);
+  uint16_t* kb16 = F8 ? nullptr : reinterpret_cast<uint16_t*>(wb + lay.kb16);
+  uint16_t* vs16 = reinterpret_cast<uint16_t*>(wb + lay.vs16);
+  uint8_t *k8 = nullptr, *ke = nullptr, *kb8 = nullptr, *kbe = nullptr;
   hipLaunchKernelGGL(k_centroids_bf16, dim3(static_cast<unsigned>((n / 8 + 255) / 256)), dim3(256), 0, s, kbar, vsum,
                      kb16, vs16, n / 8);
+  if (F8) {
+    k8 = wb + lay.k8;
+    ke = wb + lay.ke;
+    kb8 = wb + lay.kb8;
+    kbe = wb + lay.kbe;
+    const size_t krows = bh * p.L, crows = bh * T;
+    hipLaunchKernelGGL((k_quant_rows<uint16_t, D>), dim3(static_cast<unsigned>((krows * (D / 8) + 255) / 256)), dim3(256),
+                       0, s, static_cast<const uint16_t*>(K), krows, k8, ke);
+    hipLaunchKernelGGL((k_quant_rows<float, D>), dim3(static_cast<unsigned>((crows * (D / 4) + 255) / 256)), dim3(256), 0,
+                       s, kbar, crows, kb8, kbe);
+  }
   const int nw = ceil_div(T, 32);
-  const size_t lds = sizeof(uint16_t) * 2 * Geo<D>::BUF + 2 * sizeof(uint32_t) * kQB * nw + 12 * sizeof(int) +
+  const size_t lds = sizeof(uint16_t) * 2 * Geo<D, F8>::BUF + 2 * sizeof(uint32_t) * kQB * nw + 12 * sizeof(int) +
                      sizeof(uint16_t) * T;
   const size_t lds_al = (lds + 15) / 16 * 16;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_bf16<D>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_bf16<D, F8>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_al));
   if (e != hipSuccess) return e;
   const int nwg = ceil_div(T, kQB) * p.B * p.H;
-  hipLaunchKernelGGL(k_attn_bf16<D>, dim3(nwg), dim3(kAttnThreads), lds_al, s,
+  hipLaunchKernelGGL((k_attn_bf16<D, F8>), dim3(nwg), dim3(kAttnThreads), lds_al, s,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), kb16, vs16, Hbar, idx, static_cast<uint16_t*>(O), p.L, T,
-                     keep_k, static_cast<float>(p.scale), nwg, mode);
+                     keep_k, static_cast<float>(p.scale), nwg, mode, k8, ke, kb8, kbe);
   return hipGetLastError();
 }
 
@@ -842,15 +1160,44 @@ hipError_t launch_f32(const paro_problem& p, const void* Q, const void* K, const
 
 size_t attention_workspace_bytes(const paro_problem& p) {
   if (p.dtype != PARO_DTYPE_BF16) return 0;
-  return 2 * static_cast<size_t>(p.B) * p.H * ceil_div(p.L, 64) * p.d * sizeof(uint16_t);
+  return ws_layout(p, false).total;
+}
+
+hipError_t launch_fp8_rows(const void* src, int dtype, size_t nrows, int d, uint8_t* dst, uint8_t* ex, hipStream_t s) {
+  const size_t threads = nrows * static_cast<size_t>(d) / (dtype == PARO_DTYPE_BF16 ? 8 : 4);
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  if (dtype == PARO_DTYPE_BF16) {
+    if (d == 128)
+      hipLaunchKernelGGL((k_quant_rows<uint16_t, 128>), grid, dim3(256), 0, s, static_cast<const uint16_t*>(src), nrows, dst, ex);
+    else
+      hipLaunchKernelGGL((k_quant_rows<uint16_t, 64>), grid, dim3(256), 0, s, static_cast<const uint16_t*>(src), nrows, dst, ex);
+  } else {
+    if (d == 128)
+      hipLaunchKernelGGL((k_quant_rows<float, 128>), grid, dim3(256), 0, s, static_cast<const float*>(src), nrows, dst, ex);
+    else
+      hipLaunchKernelGGL((k_quant_rows<float, 64>), grid, dim3(256), 0, s, static_cast<const float*>(src), nrows, dst, ex);
+  }
+  return hipGetLastError();
+}
+
+size_t attention_fp8_workspace_bytes(const paro_problem& p) {
+  if (p.dtype != PARO_DTYPE_BF16) return 0;
+  return ws_layout(p, true).total;
+}
+
+hipError_t launch_attention_fp8(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
+                                const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O,
+                                int mode, void* ws, hipStream_t s) {
+  return p.d == 128 ? launch_bf16<128, true>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s)
+                    : launch_bf16<64, true>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s);
 }
 
 hipError_t launch_attention(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
                             const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, int mode,
                             void* ws, hipStream_t s) {
   if (p.dtype == PARO_DTYPE_BF16)
-    return p.d == 128 ? launch_bf16<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s)
-                      : launch_bf16<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s);
+    return p.d == 128 ? launch_bf16<128, false>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s)
+                      : launch_bf16<64, false>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s);
   return p.d == 128 ? launch_f32<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, s)
                     : launch_f32<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, s);
 }

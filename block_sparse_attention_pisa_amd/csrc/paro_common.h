@@ -111,6 +111,11 @@ hipError_t launch_attention(const paro_problem& p, const void* Q, const void* K,
                             const float* kbar, const float* vsum, const float* Hbar, const int32_t* idx,
                             int keep_k, void* O, int mode, void* ws, hipStream_t s);
 size_t attention_workspace_bytes(const paro_problem& p);
+hipError_t launch_attention_fp8(const paro_problem& p, const void* Q, const void* K, const void* V,
+                                const float* kbar, const float* vsum, const float* Hbar, const int32_t* idx,
+                                int keep_k, void* O, int mode, void* ws, hipStream_t s);
+size_t attention_fp8_workspace_bytes(const paro_problem& p);
+hipError_t launch_fp8_rows(const void* src, int dtype, size_t nrows, int d, uint8_t* dst, uint8_t* ex, hipStream_t s);
 // g must have its tile extents clamped to the grid extents.
 hipError_t launch_reorder(const paro_problem& p, const paro_grid& g, int direction, const void* X, void* Y,
                           hipStream_t s);

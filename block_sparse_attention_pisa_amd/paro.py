@@ -27,7 +27,8 @@ STATUS = {
 
 EXPORTED = (
     "paro_precompute", "paro_precompute_workspace_bytes", "paro_route", "paro_attention",
-    "paro_attention_mode", "paro_attention_workspace_bytes", "paro_reorder",
+    "paro_attention_mode", "paro_attention_workspace_bytes", "paro_attention_fp8",
+    "paro_attention_fp8_workspace_bytes", "paro_fp8_rows", "paro_reorder",
     "paro_reorder_source", "paro_num_blocks", "paro_status_string", "paro_version",
 )
 REORDER_GATHER = 0
@@ -82,6 +83,12 @@ def lib() -> ctypes.CDLL:
         L.paro_attention_mode.restype = ctypes.c_int
         L.paro_attention_workspace_bytes.argtypes = [pp]
         L.paro_attention_workspace_bytes.restype = sz
+        L.paro_attention_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
+        L.paro_attention_fp8.restype = ctypes.c_int
+        L.paro_attention_fp8_workspace_bytes.argtypes = [pp]
+        L.paro_attention_fp8_workspace_bytes.restype = sz
+        L.paro_fp8_rows.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp]
+        L.paro_fp8_rows.restype = ctypes.c_int
         gp = ctypes.POINTER(ParoGrid)
         L.paro_reorder.argtypes = [pp, gp, i32, vp, vp, vp]
         L.paro_reorder.restype = ctypes.c_int
@@ -188,19 +195,50 @@ def attention_workspace_bytes(p: ParoProblem) -> int:
     return int(lib().paro_attention_workspace_bytes(ctypes.byref(p)))
 
 
+def attention_fp8_workspace_bytes(p: ParoProblem) -> int:
+    return int(lib().paro_attention_fp8_workspace_bytes(ctypes.byref(p)))
+
+
+def fp8_rows(x: torch.Tensor):
+    """e4m3 rows of x [..., d] (bf16 or fp32, d in {64, 128}) with one
+    power-of-two scale per row: returns (codes uint8 [..., d], scales uint8
+    [...], the E8M0 codes e + 127)."""
+    d = x.shape[-1]
+    n = x.numel() // d
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    sc = torch.empty(x.shape[:-1], dtype=torch.uint8, device=x.device)
+    _check(lib().paro_fp8_rows(_dev(x, "x"), _dtype_code(x), n, d, _dev(codes, "codes"), _dev(sc, "scales"),
+                               _stream()), "paro_fp8_rows")
+    return codes, sc
+
+
 def attention(q, k, v, kbar, vsum, Hbar, idx, keep_k: int, scale: float | None = None,
               out: torch.Tensor | None = None, drop_tail: bool = False,
-              first_order: bool = True, workspace: torch.Tensor | None = None) -> torch.Tensor:
+              first_order: bool = True, workspace: torch.Tensor | None = None,
+              qk_fp8: bool = False) -> torch.Tensor:
     """Piecewise attention output [B, H, L, d] in the dtype of q.
 
     drop_tail=True drops U_i instead of approximating it (keep-or-drop
     sparse attention, the exact phase alone); first_order=False keeps the
     zeroth-order tail but leaves out the first-order correction. workspace:
     a device byte buffer of at least attention_workspace_bytes (allocated
-    here when not given)."""
+    here when not given). qk_fp8=True (bf16 only) takes the key-query
+    products on the fp8 matrix cores (paro_attention_fp8)."""
     p = problem(q, scale)
     o = torch.empty_like(q) if out is None else out
     ptr = _dev(idx, "idx", torch.int32) if keep_k > 0 else None
+    mode = TAIL_DROP if drop_tail else (TAIL_PISA if first_order else TAIL_ZEROTH)
+    if qk_fp8:
+        nws = attention_fp8_workspace_bytes(p)
+        if workspace is None:
+            workspace = torch.empty(max(16, nws), dtype=torch.uint8, device=q.device)
+        _check(lib().paro_attention_fp8(
+            ctypes.byref(p), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+            _dev(kbar, "kbar", torch.float32), _dev(vsum, "vsum", torch.float32),
+            _dev(Hbar, "Hbar", torch.float32), ptr, int(keep_k), mode, _dev(o, "o", q.dtype),
+            _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream()),
+            "paro_attention_fp8")
+        return o
     nws = attention_workspace_bytes(p)
     if nws > 0 and workspace is None:
         workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
@@ -209,8 +247,7 @@ def attention(q, k, v, kbar, vsum, Hbar, idx, keep_k: int, scale: float | None =
     _check(lib().paro_attention_mode(
         ctypes.byref(p), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
         _dev(kbar, "kbar", torch.float32), _dev(vsum, "vsum", torch.float32),
-        _dev(Hbar, "Hbar", torch.float32), ptr, int(keep_k),
-        TAIL_DROP if drop_tail else (TAIL_PISA if first_order else TAIL_ZEROTH),
+        _dev(Hbar, "Hbar", torch.float32), ptr, int(keep_k), mode,
         _dev(o, "o", q.dtype), wptr, wbytes, _stream()), "paro_attention_mode")
     return o
 

@@ -157,7 +157,8 @@ size_t paro_attention_workspace_bytes(const paro_problem* p);
  * chosen by `mode`:
  *   PARO_TAIL_PISA: the method (same as paro_attention);
  *   PARO_TAIL_DROP: U_i is dropped (no stage 2, no stage 3): softmax
- *     attention renormalised over the blocks of S_i, i.e. the keep-or-drop
+ *     attention renormalised over the blocks of S_i (with keep_k = 0 nothing
+ *     is left and every output is 0/0, NaN), i.e. the keep-or-drop
  *     sparse attention that section 1 (problem definition) describes as the
  *     approach the method improves on, and the exact phase of the method on
  *     its own.
@@ -214,6 +215,46 @@ int paro_reorder(const paro_problem* p, const paro_grid* g, int32_t direction, c
  * at tiled position i for L tokens, or -1 when g does not fit L or i is not
  * in [0, L). */
 int32_t paro_reorder_source(const paro_grid* g, int32_t L, int32_t i);
+
+/*
+ * paro_attention_fp8 - paro_attention_mode with the key-query products on
+ * the fp8 matrix cores, for bf16 problems. "PAROAttention: Pattern-Aware
+ * ReOrdering for Efficient Sparse and Quantized Attention in Visual
+ * Generation Models" (abstract) runs block-sparse attention at reduced
+ * bitwidth (INT8/INT4); here the same idea uses the e4m3 format that the
+ * CDNA4 matrix cores multiply at twice the bf16 rate:
+ *   - q' = scale * q is rounded to e4m3 with one power-of-two scale per query
+ *     row, K and kbar with one power-of-two scale per row (paro_fp8_rows);
+ *   - every logit q'.k (exact keys) and q'.kbar (tail centroids) is an e4m3
+ *     product summed in fp32, the scales applied inside the MFMA;
+ *   - the first-order correction (q' Hbar) uses the same rounded q';
+ *   - the softmax weights, P V and the tail sums are as in paro_attention
+ *     (bf16 operands, fp32 sums).
+ * That is, the method evaluated on q', K and kbar rounded to e4m3 as stated.
+ * Same arguments and contract as paro_attention_mode; fp32 problems return
+ * PARO_ERR_DTYPE. workspace: at least paro_attention_fp8_workspace_bytes(p)
+ * bytes (the e4m3 copies of K and kbar with their scales, and bf16 vsum).
+ */
+int paro_attention_fp8(const paro_problem* p, const void* Q, const void* K, const void* V,
+                       const float* kbar, const float* vsum, const float* Hbar,
+                       const int32_t* idx, int32_t keep_k, int32_t mode, void* O,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace paro_attention_fp8 needs (0 on bad shape and for fp32 problems). */
+size_t paro_attention_fp8_workspace_bytes(const paro_problem* p);
+
+/*
+ * paro_fp8_rows - the row quantiser of paro_attention_fp8: each of the nrows
+ * rows of d values (dtype PARO_DTYPE_BF16 bits or PARO_DTYPE_FP32) is scaled
+ * by 2^-e, with e the smallest integer, but no less than -127, such that
+ * the row's largest |x| times 2^-e is at most 448 (e = 0 for an all-zero
+ * row), and rounded to nearest even e4m3 (OCP FP8 E4M3: 4 exponent bits,
+ * bias 7, 3 mantissa bits).
+ * out: dst [nrows][d] e4m3 bytes; scales [nrows] the E8M0 codes e + 127.
+ * d in {64, 128}; src and dst 16-byte aligned device pointers.
+ */
+int paro_fp8_rows(const void* src, int32_t dtype, int64_t nrows, int32_t d, uint8_t* dst,
+                  uint8_t* scales, void* stream);
 
 /* T = ceil(L / block), or -1 when L < 1 or block < 1. */
 int32_t paro_num_blocks(int32_t L, int32_t block);

@@ -79,11 +79,12 @@ def run_gpu(q, k, v, keep_k, lam, scale=None):
     return (qd, kd, vd), stats, idx
 
 
-def full_parity(w, heads=None, qblocks=None, diag=True):
+def full_parity(w, heads=None, qblocks=None, diag=True, qk_fp8=False):
     """Run every stage on the GPU for workload w and compare with the oracle.
 
     heads: (b, h) pairs the oracle checks (all by default); qblocks: query
     blocks the oracle evaluates (all by default).
+    qk_fp8: the attention takes the fp8 key-query path.
     """
     from workloads import make_inputs
     q, k, v = make_inputs(w)
@@ -100,7 +101,8 @@ def full_parity(w, heads=None, qblocks=None, diag=True):
         ir, sc = pisa.route(qn[b, h], st["kbar"], st["M"], w.k, w.lam, w.scale, w.block)
         ref[(b, h)] = (st, ir, sc)
         idx_or[b, h] = torch.from_numpy(ir.astype(np.int32))
-    o = paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx_or.cuda(), w.k).float().cpu().numpy()
+    o = paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx_or.cuda(), w.k,
+                       qk_fp8=qk_fp8).float().cpu().numpy()
     summary = {"excused_rows": 0, "max_err": 0.0, "mean_err": 0.0}
     errs = []
     for b, h in pairs:

@@ -151,3 +151,27 @@ def test_reorder_validation():
     assert L.paro_reorder(pp, ctypes.byref(ok), 1, None, FAKE, None) == -1
     assert L.paro_reorder(pp, ctypes.byref(ok), 1, FAKE, FAKE + 4, None) == -4
     assert L.paro_reorder(ctypes.byref(_p(d=96)), ctypes.byref(ok), 0, FAKE, FAKE + 16, None) == -2
+
+
+def test_fp8_entry_points_validation():
+    L = paro.lib()
+    p = _p()
+    pp = ctypes.byref(p)
+    T = L.paro_num_blocks(1000, 64)
+    wf = L.paro_attention_fp8_workspace_bytes(pp)
+    # e4m3 K [2][1000][128] + its scales + e4m3 kbar [2][16][128] + scales + bf16 vsum, 256-byte aligned regions
+    up = lambda x: (x + 255) // 256 * 256
+    assert wf == up(2 * 1000 * 128) + up(2 * 1000) + up(2 * T * 128) + up(2 * T) + up(2 * T * 128 * 2)
+    assert L.paro_attention_fp8_workspace_bytes(ctypes.byref(_p(dtype=1))) == 0
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert L.paro_attention_fp8(ctypes.byref(_p(dtype=1)), *args, 2, 0, FAKE, FAKE, wf, None) == -3
+    assert L.paro_attention_fp8(pp, *args, T + 1, 0, FAKE, FAKE, wf, None) == -2
+    assert L.paro_attention_fp8(pp, *args, 2, 3, FAKE, FAKE, wf, None) == -7
+    assert L.paro_attention_fp8(pp, *args, 2, 0, FAKE, None, wf, None) == -1
+    assert L.paro_attention_fp8(pp, *args, 2, 0, FAKE, FAKE, wf - 1, None) == -5
+    assert L.paro_attention_fp8(pp, *args, 2, 0, FAKE + 4, FAKE, wf, None) == -4
+    assert L.paro_fp8_rows(FAKE, 7, 10, 128, FAKE, FAKE, None) == -3
+    assert L.paro_fp8_rows(FAKE, 0, 10, 96, FAKE, FAKE, None) == -2
+    assert L.paro_fp8_rows(FAKE, 0, 0, 128, FAKE, FAKE, None) == -2
+    assert L.paro_fp8_rows(FAKE, 0, 10, 128, FAKE, None, None) == -1
+    assert L.paro_fp8_rows(FAKE + 8, 0, 10, 128, FAKE, FAKE, None) == -4
