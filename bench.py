@@ -11,6 +11,11 @@ the kv-blocks exact). Prints one JSON line:
              correction) over its mean launch time measured with HIP events
   exact_phase   the same attention kernel on the all-exact (keep = 100%)
                 control of the long-video shape, against the bf16 MFMA peak
+  fp8           the same step with the key-query products on the fp8 matrix
+                cores (paro_attention_fp8): step time, dense-equivalent
+                TFLOP/s, and the attention against the mixed peak (the
+                key-query half of the FLOPs at the fp8 rate, the rest at the
+                bf16 rate); reported beside the bf16 headline, never as it
   reorder       the geometric token reordering (paro_reorder) of one
                 [B, H, L, d] tensor into the tiled order and back, against
                 the HBM peak (one read and one write of every row)
@@ -30,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic_video720p_75600.json")
 ATTN_SRCS = [os.path.join(ROOT, "block_sparse_attention_pisa_amd", "csrc", f)
@@ -147,6 +153,54 @@ def reorder_entry(w, x, out, reps: int = 5):
         gbs = nbytes / (ms * 1e-3) / 1e9
         res[name] = {"ms": round(ms, 4), "GBs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
     return res
+
+
+def fp8_entry(w, qd, kd, vd, stats, idx, out, attn_flops, exact_flops, reps: int = 3):
+    """The step with paro_attention_fp8: q', K and kbar in e4m3 for the
+    key-query products. Half of the exact and of the tail FLOPs are
+    key-query products (fp8 rate), the other half and the correction run at
+    the bf16 rate; the mixed-peak time is their sum at those rates."""
+    import torch
+    from block_sparse_attention_pisa_amd import paro
+    stream = torch.cuda.current_stream()
+    ws8 = torch.empty(paro.attention_fp8_workspace_bytes(paro.problem(qd)), dtype=torch.uint8, device=qd.device)
+
+    def attn(drop=False):
+        paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, w.k, out=out, drop_tail=drop, qk_fp8=True,
+                       workspace=ws8)
+
+    def step():
+        paro.precompute(kd, vd, out=stats)
+        paro.route(qd, stats[0], stats[3], w.k, w.lam, out=idx)
+        attn()
+
+    def timed(fn):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    step_ms = timed(step)
+    attn_ms = timed(attn)
+    drop_ms = timed(lambda: attn(True))
+    dense_flops = 4.0 * w.B * w.H * w.L * w.L * w.d
+    qk = (attn_flops - 2.0 * w.d * w.d * w.L * w.B * w.H) / 2.0   # key-query half of exact + tail
+    ideal_attn = qk / (PEAK_FP8_TFLOPS * 1e12) + (attn_flops - qk) / (PEAK_BF16_TFLOPS * 1e12)
+    ideal_exact = exact_flops / 2.0 / (PEAK_FP8_TFLOPS * 1e12) + exact_flops / 2.0 / (PEAK_BF16_TFLOPS * 1e12)
+    return {
+        "ms_per_step": round(step_ms, 4),
+        "value": round(dense_flops / (step_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s (dense-equivalent)",
+        "attention_ms": round(attn_ms, 4),
+        "attention_achieved": round(attn_flops / (attn_ms * 1e-3) / 1e12, 2),
+        "attention_frac_of_mixed_peak": round(ideal_attn * 1e3 / attn_ms, 4),
+        "exact_phase_ms": round(drop_ms, 4),
+        "exact_phase_frac_of_mixed_peak": round(ideal_exact * 1e3 / drop_ms, 4),
+        "note": "q', K and kbar rounded to e4m3 (per-row power-of-two scales); parity-tested at the bf16 bar",
+    }
 
 
 def cpu_baseline(w, q, k, v, nq: int, nheads: int):
@@ -268,6 +322,7 @@ def main():
     ex_ms = ex_ev[0].elapsed_time(ex_ev[1]) / 3
     ex_tf = exact_flops / (ex_ms * 1e-3) / 1e12
     reorder = reorder_entry(w, qd, out)
+    fp8 = fp8_entry(w, qd, kd, vd, stats, idx, out, attn_flops, exact_flops) if w.dtype == "bf16" else None
 
     # cold steps: L2 and MALL flushed by a 512 MB write before each step
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -324,6 +379,7 @@ def main():
                              "algorithmic_flops": exact_flops, "achieved": round(ex_tf, 2),
                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(ex_tf / PEAK_BF16_TFLOPS, 4)},
+        "fp8": fp8,
         "reorder": reorder,
         "cold_ms_per_step": round(sorted(cold)[1], 4),
         "input_generation_s": round(t_gen, 1),
