@@ -55,6 +55,42 @@ int check_grid(const paro_grid* g, int32_t L, paro_grid* out) {
 
 extern "C" {
 
+size_t paro_route_budget_workspace_bytes(const paro_problem* p) {
+  if (check_problem(p) != PARO_OK || paro::route_rows_per_group(num_blocks(p), p->d) < 1) return 0;
+  return paro::route_budget_workspace_bytes(*p);
+}
+
+int paro_route_budget(const paro_problem* p, const void* Q, const float* kbar, const double* M, int32_t k_total,
+                      int32_t k_min, double lambda, int64_t* weights, int32_t* offsets, int32_t* idx, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc != PARO_OK) return rc;
+  const int64_t T = num_blocks(p);
+  if (paro::route_rows_per_group(static_cast<int>(T), p->d) < 1) return PARO_ERR_SHAPE;
+  if (k_min < 0 || k_total < T * k_min || k_total > T * T || k_total < 1) return PARO_ERR_SHAPE;
+  if (!std::isfinite(lambda)) return PARO_ERR_ARG;
+  if ((rc = check_ptrs({Q, kbar, M, weights, offsets, idx, workspace})) != PARO_OK) return rc;
+  if (workspace_bytes < paro::route_budget_workspace_bytes(*p)) return PARO_ERR_WORKSPACE;
+  return from_hip(paro::launch_route_budget(*p, Q, kbar, M, k_total, k_min, lambda, weights, offsets, idx, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int paro_attention_csr(const paro_problem* p, const void* Q, const void* K, const void* V, const float* kbar,
+                       const float* vsum, const float* Hbar, const int32_t* offsets, const int32_t* idx,
+                       int32_t k_stride, int32_t mode, void* O, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc != PARO_OK) return rc;
+  if (k_stride < 0) return PARO_ERR_SHAPE;
+  if (mode != PARO_TAIL_PISA && mode != PARO_TAIL_DROP && mode != PARO_TAIL_ZEROTH) return PARO_ERR_ARG;
+  if ((rc = check_ptrs({Q, K, V, kbar, vsum, Hbar, O, offsets})) != PARO_OK) return rc;
+  if (k_stride > 0 && (rc = check_ptrs({idx})) != PARO_OK) return rc;
+  const size_t need = paro::attention_workspace_bytes(*p);
+  if (workspace_bytes < need) return PARO_ERR_WORKSPACE;
+  if (need > 0 && (rc = check_ptrs({workspace})) != PARO_OK) return rc;
+  return from_hip(paro::launch_attention(*p, Q, K, V, kbar, vsum, Hbar, idx, k_stride, O, mode, workspace,
+                                         static_cast<hipStream_t>(stream), offsets));
+}
+
 size_t paro_attention_fp8_workspace_bytes(const paro_problem* p) {
   if (check_problem(p) != PARO_OK) return 0;
   return paro::attention_fp8_workspace_bytes(*p);

@@ -562,6 +562,21 @@ __device__ __forceinline__ float exact_tile8(const uint8_t* kb, const uint8_t* s
   return ps;
 }
 
+// The exact list of query block qblk: fixed-length rows (offs == nullptr,
+// row stride keep) or CSR rows (offs [B H][T + 1], head stride keep),
+// clamped so that a malformed list can never read outside idx.
+__device__ __forceinline__ const int32_t* exact_list(const int32_t* idx, const int32_t* offs, int bh, int T, int qblk,
+                                                     int keep, int& cnt) {
+  if (!offs) {
+    cnt = keep;
+    return idx + (static_cast<size_t>(bh) * T + qblk) * keep;
+  }
+  const int32_t* o = offs + static_cast<size_t>(bh) * (T + 1) + qblk;
+  const int s0 = min(max(o[0], 0), keep);
+  cnt = min(max(o[1] - o[0], 0), min(T, keep - s0));
+  return idx + static_cast<size_t>(bh) * keep + s0;
+}
+
 // One tile through the bf16 or the fp8 (F8) S^T path.
 template <int D, bool F8, bool kMask, bool kLast = false>
 __device__ __forceinline__ float run_tile(const uint16_t* bc, int koff, int koff8, int ql, int voff, Acc<D>& a,
@@ -582,7 +597,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     const uint16_t* __restrict__ kb16, const uint16_t* __restrict__ vs16, const float* __restrict__ Hbar,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ O, int L, int T, int keep_k, float scale, int nwg,
     int mode, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ ke, const uint8_t* __restrict__ kb8,
-    const uint8_t* __restrict__ kbe) {
+    const uint8_t* __restrict__ kbe, const int32_t* __restrict__ offs) {
   const bool tail = mode != kModeDrop, corr = mode == kModePisa;
   constexpr int BUF = Geo<D, F8>::BUF, KS = Geo<D>::KS, KSB = Geo<D>::KSB, VS = Geo<D>::VS, HS = Geo<D>::HS;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -684,8 +699,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   for (int e = tid; e < kQB * nw; e += kAttnThreads) masks[e] = 0u;
   lds_barrier();
   if (qvalid && (w & 1) == 0) {
-    const int32_t* irow = idx + (static_cast<size_t>(bh) * T + qblk) * keep_k;
-    for (int e = l; e < keep_k; e += 64) {
+    int cnt;
+    const int32_t* irow = exact_list(idx, offs, bh, T, qblk, keep_k, cnt);
+    for (int e = l; e < cnt; e += 64) {
       const int j = min(max(irow[e], 0), T - 1);
       atomicOr(&masks[qi * nw + (j >> 5)], 1u << (j & 31));
     }
@@ -734,7 +750,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   const uint16_t* vs = vs16 + static_cast<size_t>(bh) * T * D;
   // stage 2 chunks (none when U_i is empty or the tail is dropped; step 0
   // still stages centroid chunk 0 for the softmax reference)
-  const int nch = (tail && keep_k < T) ? ceil_div(T, 64) : 0;
+  bool any_tail = keep_k < T;  // some query block of the group has a non-empty U_i
+  if (offs) {
+    any_tail = false;
+    for (int q = 0; q < kQB; ++q) {
+      int cq;
+      if (grp * kQB + q < T) {
+        exact_list(idx, offs, bh, T, grp * kQB + q, keep_k, cq);
+        any_tail = any_tail || cq < T;
+      }
+    }
+  }
+  const int nch = (tail && any_tail) ? ceil_div(T, 64) : 0;
 
   bool active = qvalid;
 #pragma unroll
@@ -995,7 +1022,8 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
                                                           const float* __restrict__ vsum,
                                                           const float* __restrict__ Hbar,
                                                           const int32_t* __restrict__ idx, float* __restrict__ O,
-                                                          int L, int T, int keep_k, float scale, int mode) {
+                                                          int L, int T, int keep_k, float scale, int mode,
+                                                          const int32_t* __restrict__ offs) {
   const bool tail = mode != kModeDrop, corr = mode == kModePisa;
   constexpr int DP = D / 4;  // dims per thread
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1006,7 +1034,8 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
   const int qblk = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, r = tid / 4, part = tid % 4;
   const size_t head = static_cast<size_t>(bh) * L * D;
-  const int32_t* irow = idx + (static_cast<size_t>(bh) * T + qblk) * keep_k;
+  int cnt;
+  const int32_t* irow = exact_list(idx, offs, bh, T, qblk, keep_k, cnt);
   const int row = qblk * 64 + r;
   const bool valid = row < L;
   float q[DP], o[DP];
@@ -1031,7 +1060,7 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
     for (int e = 0; e < DP; ++e) o[e] = o[e] * alpha + p * vv[part * DP + e];
   };
 
-  for (int it = 0; it < keep_k; ++it) {
+  for (int it = 0; it < cnt; ++it) {
     const int j = min(max(irow[it], 0), T - 1);
     const int nv = j == T - 1 ? nlast : 64;
     __syncthreads();
@@ -1043,11 +1072,11 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
     __syncthreads();
     for (int tk = 0; tk < nv; ++tk) key_step(kt[tk], vt[tk], 1.f, false);
   }
-  if (tail && keep_k < T) {
+  if (tail && cnt < T) {
     __syncthreads();
     for (int wd = tid; wd < nw; wd += kF32Threads) selmask[wd] = 0u;
     __syncthreads();
-    for (int e = tid; e < keep_k; e += kF32Threads) {
+    for (int e = tid; e < cnt; e += kF32Threads) {
       const int jj = min(max(irow[e], 0), T - 1);
       atomicOr(&selmask[jj >> 5], 1u << (jj & 31));
     }
@@ -1104,7 +1133,7 @@ __host__ inline WsLayout ws_layout(const paro_problem& p, bool fp8) {
 template <int D, bool F8>
 hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
                        const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, int mode,
-                       void* ws, hipStream_t s) {
+                       void* ws, hipStream_t s, const int32_t* offs) {
   const int T = ceil_div(p.L, 64);
   const size_t bh = static_cast<size_t>(p.B) * p.H;
   const size_t n = bh * T * D;
@@ -1137,14 +1166,14 @@ hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, cons
   hipLaunchKernelGGL((k_attn_bf16<D, F8>), dim3(nwg), dim3(kAttnThreads), lds_al, s,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), kb16, vs16, Hbar, idx, static_cast<uint16_t*>(O), p.L, T,
-                     keep_k, static_cast<float>(p.scale), nwg, mode, k8, ke, kb8, kbe);
+                     keep_k, static_cast<float>(p.scale), nwg, mode, k8, ke, kb8, kbe, offs);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_f32(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
                       const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, int mode,
-                      hipStream_t s) {
+                      hipStream_t s, const int32_t* offs) {
   const int T = ceil_div(p.L, 64);
   const size_t lds = 2 * sizeof(float) * 64 * D + sizeof(uint32_t) * ceil_div(T, 32);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_f32<D>),
@@ -1152,7 +1181,7 @@ hipError_t launch_f32(const paro_problem& p, const void* Q, const void* K, const
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_f32<D>, dim3(T, p.B * p.H), dim3(kF32Threads), lds, s, static_cast<const float*>(Q),
                      static_cast<const float*>(K), static_cast<const float*>(V), kbar, vsum, Hbar, idx,
-                     static_cast<float*>(O), p.L, T, keep_k, static_cast<float>(p.scale), mode);
+                     static_cast<float*>(O), p.L, T, keep_k, static_cast<float>(p.scale), mode, offs);
   return hipGetLastError();
 }
 
@@ -1188,18 +1217,18 @@ size_t attention_fp8_workspace_bytes(const paro_problem& p) {
 hipError_t launch_attention_fp8(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
                                 const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O,
                                 int mode, void* ws, hipStream_t s) {
-  return p.d == 128 ? launch_bf16<128, true>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s)
-                    : launch_bf16<64, true>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s);
+  return p.d == 128 ? launch_bf16<128, true>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s, nullptr)
+                    : launch_bf16<64, true>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s, nullptr);
 }
 
 hipError_t launch_attention(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
                             const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, int mode,
-                            void* ws, hipStream_t s) {
+                            void* ws, hipStream_t s, const int32_t* offs) {
   if (p.dtype == PARO_DTYPE_BF16)
-    return p.d == 128 ? launch_bf16<128, false>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s)
-                      : launch_bf16<64, false>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s);
-  return p.d == 128 ? launch_f32<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, s)
-                    : launch_f32<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, s);
+    return p.d == 128 ? launch_bf16<128, false>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s, offs)
+                      : launch_bf16<64, false>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s, offs);
+  return p.d == 128 ? launch_f32<128>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, s, offs)
+                    : launch_f32<64>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, s, offs);
 }
 
 }  // namespace paro

@@ -107,9 +107,12 @@ hipError_t launch_precompute(const paro_problem& p, const void* K, const void* V
                              float* vsum, float* Hbar, double* M, void* ws, hipStream_t s);
 hipError_t launch_route(const paro_problem& p, const void* Q, const float* kbar, const double* M,
                         int keep_k, double lambda, int32_t* idx, hipStream_t s);
+// offs: CSR row offsets [B H][T + 1] (keep_k is then the per-head stride of
+// idx), or nullptr for rows of keep_k.
 hipError_t launch_attention(const paro_problem& p, const void* Q, const void* K, const void* V,
                             const float* kbar, const float* vsum, const float* Hbar, const int32_t* idx,
-                            int keep_k, void* O, int mode, void* ws, hipStream_t s);
+                            int keep_k, void* O, int mode, void* ws, hipStream_t s,
+                            const int32_t* offs = nullptr);
 size_t attention_workspace_bytes(const paro_problem& p);
 hipError_t launch_attention_fp8(const paro_problem& p, const void* Q, const void* K, const void* V,
                                 const float* kbar, const float* vsum, const float* Hbar, const int32_t* idx,
@@ -121,4 +124,8 @@ hipError_t launch_reorder(const paro_problem& p, const paro_grid& g, int directi
                           hipStream_t s);
 __host__ __device__ int reorder_source(const paro_grid& g, int N, int i);
 int route_rows_per_group(int T, int d);
+size_t route_budget_workspace_bytes(const paro_problem& p);
+hipError_t launch_route_budget(const paro_problem& p, const void* Q, const float* kbar, const double* M, int k_total,
+                               int k_min, double lambda, int64_t* wq, int32_t* offsets, int32_t* idx, void* ws,
+                               hipStream_t s);
 }  // namespace paro

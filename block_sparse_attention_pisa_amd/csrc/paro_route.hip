@@ -77,11 +77,20 @@ __device__ __forceinline__ void add_piece<float>(double* acc, uint4 raw) {
   acc[3] += __uint_as_float(raw.w);
 }
 
-template <typename E, int D, int NI>
+// Modes of k_route: the fixed-k routing; the weights pass of the budgeted
+// routing (qbar kept for the select pass, and each row's need w_i = exp of
+// the entropy of its zeroth-order block masses, as 2^16 fixed point); the
+// select pass of the budgeted routing (qbar read back, row i keeps the
+// offsets[i + 1] - offsets[i] best blocks at idx + offsets[i]).
+constexpr int kRouteFixed = 0, kRouteWeights = 1, kRouteRagged = 2;
+
+template <typename E, int D, int NI, int kMode>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_route(const E* __restrict__ Q, const float* __restrict__ kbar,
                                                     const double* __restrict__ M, int32_t* __restrict__ idx,
                                                     int L, int T, int R, int keep_k, double scale,
-                                                    double lambda) {
+                                                    double lambda, float* __restrict__ qbar_ws,
+                                                    int64_t* __restrict__ wq, const int32_t* __restrict__ offsets,
+                                                    int kstride) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* qs = reinterpret_cast<float*>(smem);    // qbar [R][D]; dead once the MFMA operands are loaded
   float* dots = reinterpret_cast<float*>(smem);  // [R][T], written after qs is dead
@@ -93,7 +102,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const E* Qh = Q + static_cast<size_t>(bh) * L * D;
   const float* kb = kbar + static_cast<size_t>(bh) * T * D;
   const double* Mh = M + static_cast<size_t>(bh) * T;
+  float* qbh = qbar_ws + (static_cast<size_t>(bh) * T + i0) * D;  // this group's rows of the kept qbar
 
+  if (kMode == kRouteRagged) {
+    for (int e = t; e < nrows * D; e += kThreads) qs[e] = qbh[e];
+  } else {
   // 1. qbar. Lane l reads the 16-byte piece dg = l % G of rows rg, rg + RG,
   //    ... (rg = l / G) of the block, sums them in fp64, and the RG lanes of
   //    one piece are then reduced by shuffles.
@@ -128,9 +141,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         for (int e = 0; e < EPL; ++e) acc[e] += shfl_xor_f64(acc[e], o);
       if (rg == 0) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) qs[r * D + EPL * dg + e] = static_cast<float>(acc[e] / nvalid);
+        for (int e = 0; e < EPL; ++e) {
+          const float x = static_cast<float>(acc[e] / nvalid);
+          qs[r * D + EPL * dg + e] = x;
+          if (kMode == kRouteWeights) qbh[r * D + EPL * dg + e] = x;
+        }
       }
     }
+  }
   }
   __syncthreads();
 
@@ -187,9 +205,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // whenever they are needed. Padding keys (j >= T) are 0, which no finite
   // score maps to and no prefix test below matches.
   constexpr int tail0 = 64 * NI;
+  if (kMode == kRouteWeights) {
+    // w = exp(H), H the entropy of p_j = n_j e^{a_j} / sum, a_j = scale qbar . kbar_j;
+    // log n_j - log 64 is 0 except for a partial last block
+    const double lnlast = log(static_cast<double>(L - kBlock * (T - 1)) / kBlock);
+    for (int r = w; r < nrows; r += kWaves) {
+      const float* dr = dots + r * T;
+      auto xat = [&](int j) { return scale * static_cast<double>(dr[j]) + (j == T - 1 ? lnlast : 0.0); };
+      double mx = -__builtin_huge_val();
+      for (int j = l; j < T; j += 64) mx = fmax(mx, xat(j));
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) mx = fmax(mx, shfl_xor_f64(mx, o));
+      double z = 0.0, ez = 0.0;
+      for (int j = l; j < T; j += 64) {
+        const double y = xat(j) - mx, e = exp(y);
+        z += e;
+        ez += y * e;
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        z += shfl_xor_f64(z, o);
+        ez += shfl_xor_f64(ez, o);
+      }
+      if (l == 0) {
+        const double wgt = exp(log(z) - ez / z);
+        wq[static_cast<size_t>(bh) * T + i0 + r] = static_cast<int64_t>(floor(wgt * 65536.0 + 0.5));
+      }
+    }
+    return;
+  }
   for (int r = w; r < nrows; r += kWaves) {
     const float* dr = dots + r * T;
-    int32_t* out = idx + (static_cast<size_t>(bh) * T + i0 + r) * keep_k;
+    int32_t* out;
+    if (kMode == kRouteRagged) {
+      const int32_t* orow = offsets + static_cast<size_t>(bh) * (T + 1) + i0 + r;
+      keep_k = orow[1] - orow[0];
+      out = idx + static_cast<size_t>(bh) * kstride + orow[0];
+    } else {
+      out = idx + (static_cast<size_t>(bh) * T + i0 + r) * keep_k;
+    }
+    if (keep_k == 0) continue;
     if (keep_k >= T) {
       for (int j = l; j < T; j += 64) out[j] = j;
       continue;
@@ -275,34 +330,136 @@ size_t route_lds_bytes(int T, int d, int R) {
   return sizeof(float) * static_cast<size_t>(R) * static_cast<size_t>(std::max(T, d));
 }
 
-template <typename E, int D, int NI>
-hipError_t launch_ni(const paro_problem& p, const E* Q, const float* kbar, const double* M, int keep_k,
-                     double lambda, int32_t* idx, hipStream_t s) {
+// Arguments of one routing launch beyond the problem (the budgeted modes use
+// the workspace qbar, the integer weights and the CSR offsets).
+struct RouteArgs {
+  int keep_k;
+  double lambda;
+  int32_t* idx;
+  float* qbar_ws;
+  int64_t* wq;
+  const int32_t* offsets;
+  int kstride;
+};
+
+template <typename E, int D, int NI, int kMode>
+hipError_t launch_ni(const paro_problem& p, const E* Q, const float* kbar, const double* M, const RouteArgs& ra,
+                     hipStream_t s) {
   const int T = ceil_div(p.L, kBlock);
   const int R = route_rows_per_group(T, D);
   const size_t lds = route_lds_bytes(T, D, R);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_route<E, D, NI>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_route<E, D, NI, kMode>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_route<E, D, NI>), dim3(ceil_div(T, R), p.B * p.H), dim3(kThreads), lds, s, Q, kbar, M,
-                     idx, p.L, T, R, keep_k, p.scale, lambda);
+  hipLaunchKernelGGL((k_route<E, D, NI, kMode>), dim3(ceil_div(T, R), p.B * p.H), dim3(kThreads), lds, s, Q, kbar,
+                     M, ra.idx, p.L, T, R, ra.keep_k, p.scale, ra.lambda, ra.qbar_ws, ra.wq, ra.offsets, ra.kstride);
   return hipGetLastError();
 }
 
 // Register chunks per lane: ceil(T / 64) rounded up to a multiple of 4.
-template <typename E, int D>
-hipError_t launch_typed(const paro_problem& p, const E* Q, const float* kbar, const double* M, int keep_k,
-                        double lambda, int32_t* idx, hipStream_t s) {
+template <typename E, int D, int kMode>
+hipError_t launch_typed(const paro_problem& p, const E* Q, const float* kbar, const double* M, const RouteArgs& ra,
+                        hipStream_t s) {
   switch (std::min((ceil_div(ceil_div(p.L, kBlock), 64) + 3) / 4, kMaxKeyRegs / 4)) {
-    case 1: return launch_ni<E, D, 4>(p, Q, kbar, M, keep_k, lambda, idx, s);
-    case 2: return launch_ni<E, D, 8>(p, Q, kbar, M, keep_k, lambda, idx, s);
-    case 3: return launch_ni<E, D, 12>(p, Q, kbar, M, keep_k, lambda, idx, s);
-    case 4: return launch_ni<E, D, 16>(p, Q, kbar, M, keep_k, lambda, idx, s);
-    case 5: return launch_ni<E, D, 20>(p, Q, kbar, M, keep_k, lambda, idx, s);
-    case 6: return launch_ni<E, D, 24>(p, Q, kbar, M, keep_k, lambda, idx, s);
-    case 7: return launch_ni<E, D, 28>(p, Q, kbar, M, keep_k, lambda, idx, s);
-    default: return launch_ni<E, D, 32>(p, Q, kbar, M, keep_k, lambda, idx, s);
+    case 1: return launch_ni<E, D, 4, kMode>(p, Q, kbar, M, ra, s);
+    case 2: return launch_ni<E, D, 8, kMode>(p, Q, kbar, M, ra, s);
+    case 3: return launch_ni<E, D, 12, kMode>(p, Q, kbar, M, ra, s);
+    case 4: return launch_ni<E, D, 16, kMode>(p, Q, kbar, M, ra, s);
+    case 5: return launch_ni<E, D, 20, kMode>(p, Q, kbar, M, ra, s);
+    case 6: return launch_ni<E, D, 24, kMode>(p, Q, kbar, M, ra, s);
+    case 7: return launch_ni<E, D, 28, kMode>(p, Q, kbar, M, ra, s);
+    default: return launch_ni<E, D, 32, kMode>(p, Q, kbar, M, ra, s);
   }
+}
+
+template <int kMode>
+hipError_t launch_mode(const paro_problem& p, const void* Q, const float* kbar, const double* M, const RouteArgs& ra,
+                       hipStream_t s) {
+  if (p.dtype == PARO_DTYPE_BF16) {
+    const auto* q = static_cast<const uint16_t*>(Q);
+    return p.d == 128 ? launch_typed<uint16_t, 128, kMode>(p, q, kbar, M, ra, s)
+                      : launch_typed<uint16_t, 64, kMode>(p, q, kbar, M, ra, s);
+  }
+  const auto* q = static_cast<const float*>(Q);
+  return p.d == 128 ? launch_typed<float, 128, kMode>(p, q, kbar, M, ra, s)
+                    : launch_typed<float, 64, kMode>(p, q, kbar, M, ra, s);
+}
+
+// Budget sharing for one head (one workgroup): k_i = k_min + floor(R wq_i / S)
+// plus one for the R - sum(floors) rows of largest remainder R wq_i mod S
+// (ties to the lower i), capped at T; then the CSR offsets (exclusive sums).
+// The leftover rows are found as the keys (remainder << 20 | 2^20 - 1 - i),
+// all distinct, that are at least the left-th largest one, by a bitwise
+// search with block-wide counts.
+constexpr int kAllocThreads = 1024;
+__global__ __launch_bounds__(kAllocThreads) void k_budget_alloc(const int64_t* __restrict__ wq,
+                                                                 int32_t* __restrict__ offsets, int T, int k_total,
+                                                                 int k_min) {
+  __shared__ long long red[kAllocThreads / 64];
+  __shared__ int scan[kAllocThreads / 64];
+  const int bh = blockIdx.x, t = threadIdx.x, w = t / 64, l = t % 64;
+  const int64_t* wh = wq + static_cast<size_t>(bh) * T;
+  int32_t* oh = offsets + static_cast<size_t>(bh) * (T + 1);
+  auto block_sum = [&](long long v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    __syncthreads();
+    if (l == 0) red[w] = v;
+    __syncthreads();
+    long long sum = 0;
+#pragma unroll
+    for (int i = 0; i < kAllocThreads / 64; ++i) sum += red[i];
+    return sum;
+  };
+  long long part = 0;
+  for (int i = t; i < T; i += kAllocThreads) part += wh[i];
+  const long long S = block_sum(part);
+  const long long Rr = static_cast<long long>(k_total) - static_cast<long long>(T) * k_min;
+  part = 0;
+  for (int i = t; i < T; i += kAllocThreads) part += (S > 0 ? Rr * wh[i] / S : 0);
+  const long long left = Rr - block_sum(part);
+  auto key_of = [&](int i) -> unsigned long long {
+    const long long rem = S > 0 ? Rr * wh[i] % S : 0;
+    return (static_cast<unsigned long long>(rem) << 20) | static_cast<unsigned long long>((1 << 20) - 1 - i);
+  };
+  unsigned long long thr = ~0ull;  // no extra block when left == 0
+  if (left > 0) {
+    unsigned long long prefix = 0;
+    for (int b = 63; b >= 0; --b) {
+      const unsigned long long cand = prefix | (1ull << b);
+      long long c = 0;
+      for (int i = t; i < T; i += kAllocThreads) c += key_of(i) >= cand ? 1 : 0;
+      if (block_sum(c) >= left) prefix = cand;
+    }
+    thr = prefix;
+  }
+  // k_i and their exclusive prefix sums, in chunks of kAllocThreads rows
+  int base = 0;
+  for (int c0 = 0; c0 < T; c0 += kAllocThreads) {
+    const int i = c0 + t;
+    int k = 0;
+    if (i < T) {
+      const long long q = S > 0 ? Rr * wh[i] / S : 0;
+      k = static_cast<int>(min(static_cast<long long>(T), k_min + q + (key_of(i) >= thr ? 1 : 0)));
+    }
+    int incl = k;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (l >= o) incl += v;
+    }
+    __syncthreads();
+    if (l == 63) scan[w] = incl;
+    __syncthreads();
+    int before = base;
+    for (int v = 0; v < w; ++v) before += scan[v];
+    if (i < T) oh[i] = before + incl - k;
+    int total = 0;
+#pragma unroll
+    for (int v = 0; v < kAllocThreads / 64; ++v) total += scan[v];
+    base += total;
+  }
+  if (t == 0) oh[T] = base;
 }
 
 }  // namespace
@@ -316,14 +473,25 @@ int route_rows_per_group(int T, int d) {
 hipError_t launch_route(const paro_problem& p, const void* Q, const float* kbar, const double* M, int keep_k,
                         double lambda, int32_t* idx, hipStream_t s) {
   if (keep_k == 0) return hipSuccess;
-  if (p.dtype == PARO_DTYPE_BF16) {
-    const auto* q = static_cast<const uint16_t*>(Q);
-    return p.d == 128 ? launch_typed<uint16_t, 128>(p, q, kbar, M, keep_k, lambda, idx, s)
-                      : launch_typed<uint16_t, 64>(p, q, kbar, M, keep_k, lambda, idx, s);
-  }
-  const auto* q = static_cast<const float*>(Q);
-  return p.d == 128 ? launch_typed<float, 128>(p, q, kbar, M, keep_k, lambda, idx, s)
-                    : launch_typed<float, 64>(p, q, kbar, M, keep_k, lambda, idx, s);
+  const RouteArgs ra{keep_k, lambda, idx, nullptr, nullptr, nullptr, 0};
+  return launch_mode<kRouteFixed>(p, Q, kbar, M, ra, s);
+}
+
+size_t route_budget_workspace_bytes(const paro_problem& p) {
+  return static_cast<size_t>(p.B) * p.H * ceil_div(p.L, kBlock) * p.d * sizeof(float);
+}
+
+hipError_t launch_route_budget(const paro_problem& p, const void* Q, const float* kbar, const double* M, int k_total,
+                               int k_min, double lambda, int64_t* wq, int32_t* offsets, int32_t* idx, void* ws,
+                               hipStream_t s) {
+  const int T = ceil_div(p.L, kBlock);
+  RouteArgs ra{0, lambda, idx, static_cast<float*>(ws), wq, offsets, k_total};
+  hipError_t e = launch_mode<kRouteWeights>(p, Q, kbar, M, ra, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_budget_alloc, dim3(p.B * p.H), dim3(kAllocThreads), 0, s, static_cast<const int64_t*>(wq),
+                     offsets, T, k_total, k_min);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return launch_mode<kRouteRagged>(p, Q, kbar, M, ra, s);
 }
 
 }  // namespace paro

@@ -28,7 +28,8 @@ STATUS = {
 EXPORTED = (
     "paro_precompute", "paro_precompute_workspace_bytes", "paro_route", "paro_attention",
     "paro_attention_mode", "paro_attention_workspace_bytes", "paro_attention_fp8",
-    "paro_attention_fp8_workspace_bytes", "paro_fp8_rows", "paro_reorder",
+    "paro_attention_fp8_workspace_bytes", "paro_fp8_rows", "paro_route_budget",
+    "paro_route_budget_workspace_bytes", "paro_attention_csr", "paro_reorder",
     "paro_reorder_source", "paro_num_blocks", "paro_status_string", "paro_version",
 )
 REORDER_GATHER = 0
@@ -89,6 +90,12 @@ def lib() -> ctypes.CDLL:
         L.paro_attention_fp8_workspace_bytes.restype = sz
         L.paro_fp8_rows.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp]
         L.paro_fp8_rows.restype = ctypes.c_int
+        L.paro_route_budget.argtypes = [pp, vp, vp, vp, i32, i32, dbl, vp, vp, vp, vp, sz, vp]
+        L.paro_route_budget.restype = ctypes.c_int
+        L.paro_route_budget_workspace_bytes.argtypes = [pp]
+        L.paro_route_budget_workspace_bytes.restype = sz
+        L.paro_attention_csr.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
+        L.paro_attention_csr.restype = ctypes.c_int
         gp = ctypes.POINTER(ParoGrid)
         L.paro_reorder.argtypes = [pp, gp, i32, vp, vp, vp]
         L.paro_reorder.restype = ctypes.c_int
@@ -249,6 +256,44 @@ def attention(q, k, v, kbar, vsum, Hbar, idx, keep_k: int, scale: float | None =
         _dev(kbar, "kbar", torch.float32), _dev(vsum, "vsum", torch.float32),
         _dev(Hbar, "Hbar", torch.float32), ptr, int(keep_k), mode,
         _dev(o, "o", q.dtype), wptr, wbytes, _stream()), "paro_attention_mode")
+    return o
+
+
+def route_budget(q, kbar, M, k_total: int, k_min: int = 1, lam: float = 0.1, scale: float | None = None):
+    """Per-query-block budgets: returns (offsets [B, H, T + 1] int32, idx [B, H, k_total] int32,
+    weights [B, H, T] int64 = w * 2^16). Row i of head h is idx[h][offsets[h][i]:offsets[h][i + 1]]."""
+    p = problem(q, scale)
+    B, H, L, d = q.shape
+    T = -(-L // BLOCK)
+    offsets = torch.empty(B, H, T + 1, dtype=torch.int32, device=q.device)
+    idx = torch.zeros(B, H, max(1, k_total), dtype=torch.int32, device=q.device)
+    wq = torch.empty(B, H, T, dtype=torch.int64, device=q.device)
+    ws = torch.empty(max(16, int(lib().paro_route_budget_workspace_bytes(ctypes.byref(p)))), dtype=torch.uint8,
+                     device=q.device)
+    _check(lib().paro_route_budget(ctypes.byref(p), _dev(q, "q"), _dev(kbar, "kbar", torch.float32),
+                                   _dev(M, "M", torch.float64), int(k_total), int(k_min), float(lam), _dev(wq, "wq"),
+                                   _dev(offsets, "offsets"), _dev(idx, "idx"), _dev(ws, "workspace"),
+                                   ws.numel(), _stream()), "paro_route_budget")
+    return offsets, idx, wq
+
+
+def attention_csr(q, k, v, kbar, vsum, Hbar, offsets, idx, k_stride: int, scale: float | None = None,
+                  out: torch.Tensor | None = None, drop_tail: bool = False, first_order: bool = True,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """paro_attention_csr: exact lists of any lengths (offsets [B, H, T + 1], idx [B, H, k_stride])."""
+    p = problem(q, scale)
+    o = torch.empty_like(q) if out is None else out
+    nws = attention_workspace_bytes(p)
+    if nws > 0 and workspace is None:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    wptr = _dev(workspace, "workspace") if nws > 0 else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    mode = TAIL_DROP if drop_tail else (TAIL_PISA if first_order else TAIL_ZEROTH)
+    _check(lib().paro_attention_csr(
+        ctypes.byref(p), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+        _dev(kbar, "kbar", torch.float32), _dev(vsum, "vsum", torch.float32), _dev(Hbar, "Hbar", torch.float32),
+        _dev(offsets, "offsets", torch.int32), _dev(idx, "idx", torch.int32), int(k_stride), mode,
+        _dev(o, "o", q.dtype), wptr, wbytes, _stream()), "paro_attention_csr")
     return o
 
 

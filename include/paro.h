@@ -217,6 +217,50 @@ int paro_reorder(const paro_problem* p, const paro_grid* g, int32_t direction, c
 int32_t paro_reorder_source(const paro_grid* g, int32_t L, int32_t i);
 
 /*
+ * paro_route_budget - routing with per-query-block budgets ("Sparsity Should
+ * Be ALLOTted by Output: Training-Free Allocation of Block-Sparse Attention
+ * for Video Diffusion Transformers", review sections 1-3: a fixed total
+ * budget of block-sparse attention shared out by what each output needs).
+ * The page gives no estimator; the one used here, per (batch, head):
+ *   - need of query block i: w_i = exp(H_i), H_i the entropy of the
+ *     zeroth-order block masses p_ij proportional to n_j exp(scale qbar_i .
+ *     kbar_j) (the effective number of blocks its attention spreads over),
+ *     written to weights as wq_i = w_i 2^16 rounded to nearest (fp64);
+ *   - R = k_total - T k_min is shared in proportion to wq with integer
+ *     arithmetic: k_i = k_min + floor(R wq_i / S) (S = sum wq), and the
+ *     R - sum of the floors leftover blocks go to the rows of largest
+ *     remainder R wq_i mod S, ties to the lower i; k_i is capped at T (the
+ *     total is then below k_total);
+ *   - S_i = the k_i best blocks of row i by the covariance-aware score, as in
+ *     paro_route (ties to the lower j, ascending).
+ * out: weights [B, H, T] int64; offsets [B, H, T + 1] int32, row i of head h
+ *      in idx[h k_total + offsets[h][i] .. h k_total + offsets[h][i + 1]);
+ *      idx [B, H, k_total] int32 (entries past offsets[h][T] are not written).
+ * in : T k_min <= k_total <= T^2, k_total >= 1, k_min >= 0, lambda finite.
+ * workspace: at least paro_route_budget_workspace_bytes(p) bytes (qbar).
+ */
+int paro_route_budget(const paro_problem* p, const void* Q, const float* kbar, const double* M,
+                      int32_t k_total, int32_t k_min, double lambda, int64_t* weights,
+                      int32_t* offsets, int32_t* idx, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Bytes of device workspace paro_route_budget needs (0 on bad shape). */
+size_t paro_route_budget_workspace_bytes(const paro_problem* p);
+
+/*
+ * paro_attention_csr - paro_attention_mode on exact lists of any lengths:
+ * row i of head h is idx[h k_stride + offsets[h][i] ..
+ * h k_stride + offsets[h][i + 1]) (as paro_route_budget writes them), each
+ * list ascending with distinct indices in [0, T). Lists are clamped to
+ * [0, k_stride) and to T entries, so a malformed list gives undefined output
+ * values but never an out-of-bounds access. Same workspace as paro_attention.
+ */
+int paro_attention_csr(const paro_problem* p, const void* Q, const void* K, const void* V,
+                       const float* kbar, const float* vsum, const float* Hbar,
+                       const int32_t* offsets, const int32_t* idx, int32_t k_stride, int32_t mode,
+                       void* O, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paro_attention_fp8 - paro_attention_mode with the key-query products on
  * the fp8 matrix cores, for bf16 problems. "PAROAttention: Pattern-Aware
  * ReOrdering for Efficient Sparse and Quantized Attention in Visual

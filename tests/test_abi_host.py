@@ -175,3 +175,27 @@ def test_fp8_entry_points_validation():
     assert L.paro_fp8_rows(FAKE, 0, 0, 128, FAKE, FAKE, None) == -2
     assert L.paro_fp8_rows(FAKE, 0, 10, 128, FAKE, None, None) == -1
     assert L.paro_fp8_rows(FAKE + 8, 0, 10, 128, FAKE, FAKE, None) == -4
+
+
+def test_budget_entry_points_validation():
+    L = paro.lib()
+    p = _p()
+    pp = ctypes.byref(p)
+    T = L.paro_num_blocks(1000, 64)
+    wb = L.paro_route_budget_workspace_bytes(pp)
+    assert wb == 2 * T * 128 * 4   # qbar, fp32
+    rb = lambda K, kmin, lam=0.1, w=FAKE, ws=wb: L.paro_route_budget(pp, FAKE, FAKE, FAKE, K, kmin, lam, w, FAKE,
+                                                                       FAKE, FAKE, ws, None)
+    assert rb(T * 2 - 1, 2) == -2          # below the per-row floor
+    assert rb(T * T + 1, 1) == -2          # above T^2
+    assert rb(T, -1) == -2
+    assert rb(0, 0) == -2
+    assert rb(T * 3, 1, lam=float("nan")) == -7
+    assert rb(T * 3, 1, w=None) == -1
+    assert rb(T * 3, 1, ws=wb - 1) == -5
+    wa = L.paro_attention_workspace_bytes(pp)
+    ac = lambda stride, mode=0, offs=FAKE: L.paro_attention_csr(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, offs, FAKE,
+                                                                 stride, mode, FAKE, FAKE, wa, None)
+    assert ac(-1) == -2
+    assert ac(10, mode=3) == -7
+    assert ac(10, offs=None) == -1

@@ -1,0 +1,172 @@
+"""GPU checks of the per-query-block budgets (paro_route_budget) and of the
+attention on CSR lists (paro_attention_csr), against oracle/budget.py.
+
+The need w_i comes from fp32 dot products on the GPU and fp64 in the oracle,
+so it is compared with a relative tolerance; the sharing is integer
+arithmetic on the integer weights, so the GPU's k_i are compared bit for bit
+with the oracle's sharing of the GPU's own integer weights; the lists are
+compared like the fixed-k routing (bit-exact except rows whose swapped
+blocks are within 1e-5 in oracle score); attention is fed the oracle's lists.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_pisa_amd import paro
+from oracle import budget, pisa
+from workloads import WORKLOADS, make_inputs
+
+from parity_util import ROUTE_GAP, check_attention, log, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_lists(got, ref, score):
+    excused = 0
+    for i, (a, b) in enumerate(zip(got, ref)):
+        assert len(a) == len(b)
+        assert list(a) == sorted(a) and len(set(a.tolist())) == len(a)
+        sa, sb = set(a.tolist()), set(b.tolist())
+        if sa == sb:
+            continue
+        gap = max(score[i, jm] - score[i, je] for je in sa - sb for jm in sb - sa)
+        assert gap < ROUTE_GAP, ("routing mismatch", i, gap)
+        excused += 1
+    return excused
+
+
+@pytest.mark.parametrize("name,heads,keep_permille,k_min", [
+    ("image_4608", [0, 5], 250, 1),
+    ("video480p_32760", [0, 11], 125, 2),
+    ("tiny_fp32", [0, 1], 250, 0),
+])
+def test_budget_routing_and_attention(name, heads, keep_permille, k_min):
+    w = WORKLOADS[name]
+    q, k, v = make_inputs(w, heads=heads)
+    T = w.T
+    K = -(-keep_permille * T // 1000) * T
+    log(f"[budget] {name} heads {heads} k_total {K} k_min {k_min}")
+    (qd, kd, vd), stats, _ = run_gpu(q, k, v, 1, w.lam)
+    offsets, idx, wq = paro.route_budget(qd, stats[0], stats[3], K, k_min, w.lam)
+    att = None
+    offs_h, idx_h, wq_h = offsets.cpu().numpy(), idx.cpu().numpy(), wq.cpu().numpy()
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    idx_or = torch.zeros_like(idx.cpu())
+    refs = []
+    for h in range(len(heads)):
+        st = pisa.block_stats(kn[0, h], vn[0, h], 64)
+        w_ref = budget.block_weights(qn[0, h], st["kbar"], w.scale, 64)
+        rel = np.abs(wq_h[0, h] / budget.WEIGHT_ONE - w_ref) / w_ref
+        assert rel.max() < 1e-5, rel.max()
+        kk = np.diff(offs_h[0, h])
+        assert offs_h[0, h, 0] == 0
+        assert np.array_equal(kk, budget.allocate(wq_h[0, h], K, k_min))
+        lists = [idx_h[0, h, offs_h[0, h, i]:offs_h[0, h, i + 1]] for i in range(T)]
+        ref_lists, score = budget.route_ragged(qn[0, h], st["kbar"], st["M"], kk, w.lam, w.scale, 64)
+        ex = _check_lists(lists, ref_lists, score)
+        log(f"[budget] {name} h{heads[h]}: k_i {kk.min()}..{kk.max()} (sum {kk.sum()}), w rel err {rel.max():.2g}, "
+            f"excused rows {ex}")
+        for i in range(T):
+            idx_or[0, h, offs_h[0, h, i]:offs_h[0, h, i + 1]] = torch.from_numpy(ref_lists[i].astype(np.int32))
+        refs.append((st, ref_lists))
+    o = paro.attention_csr(qd, kd, vd, *stats[:3], offsets, idx_or.cuda(), K).float().cpu().numpy()
+    for h, (st, ref_lists) in enumerate(refs):
+        oref = pisa.attention(qn[0, h], kn[0, h], vn[0, h], st, ref_lists, w.scale, 64)
+        mx, mean = check_attention(o[0, h], oref, w.dtype)
+        log(f"[budget] {name} h{heads[h]}: attention max {mx:.3g} mean {mean:.3g}")
+
+
+def test_uniform_budget_is_the_fixed_k_path():
+    """k_min = keep and k_total = T keep leave nothing to share: every row
+    gets keep, and the CSR route and attention equal the fixed-k ones bit for bit."""
+    w = WORKLOADS["image_4608"]
+    q, k, v = make_inputs(w, heads=[2])
+    (qd, kd, vd), stats, idx = run_gpu(q, k, v, w.k, w.lam)
+    offsets, idx_b, _ = paro.route_budget(qd, stats[0], stats[3], w.T * w.k, w.k, w.lam)
+    assert torch.equal(offsets.cpu()[0, 0], torch.arange(0, w.T * w.k + 1, w.k, dtype=torch.int32))
+    assert torch.equal(idx_b.cpu().reshape(-1), idx.cpu().reshape(-1))
+    o1 = paro.attention(qd, kd, vd, *stats[:3], idx, w.k)
+    o2 = paro.attention_csr(qd, kd, vd, *stats[:3], offsets, idx_b, w.T * w.k)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_budget_with_strongly_varying_need():
+    """Keys of block j offset by a random mu_j (so centroid logits vary), and
+    queries pointing along one direction with a strength of 0.2, 1 or 5 by
+    block: sharper rows spread over fewer blocks, so the sharing is far from
+    uniform."""
+    from workloads import random_uniform_inputs
+    B, H, L, d = 1, 2, 64 * 40 + 9, 128
+    q, k, v = random_uniform_inputs(B, H, L, d, dtype=torch.float32, seed=17, scale=0.8)
+    g = torch.Generator().manual_seed(3)
+    T0 = -(-L // 64)
+    mu = torch.randn(B, H, T0, d, generator=g) * 3.0
+    k = (k + mu.repeat_interleave(64, dim=2)[:, :, :L]).to(torch.bfloat16)
+    u = torch.randn(d, generator=g)
+    u = 3.0 * u / u.norm()
+    f = torch.tensor([0.2, 1.0, 5.0]).repeat_interleave(64).repeat(-(-L // 192))[:L]
+    q = (0.1 * q + f[None, None, :, None] * u).to(torch.bfloat16)
+    v = v.to(torch.bfloat16)
+    T, scale = -(-L // 64), 1 / np.sqrt(d)
+    K = 10 * T
+    (qd, kd, vd), stats, _ = run_gpu(q, k, v, 1, 0.1)
+    offsets, idx, wq = paro.route_budget(qd, stats[0], stats[3], K, 1, 0.1)
+    offs_h, idx_h, wq_h = offsets.cpu().numpy(), idx.cpu().numpy(), wq.cpu().numpy()
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    idx_or = torch.zeros_like(idx.cpu())
+    refs = []
+    for h in range(H):
+        st = pisa.block_stats(kn[0, h], vn[0, h], 64)
+        w_ref = budget.block_weights(qn[0, h], st["kbar"], scale, 64)
+        assert (np.abs(wq_h[0, h] / budget.WEIGHT_ONE - w_ref) / w_ref).max() < 1e-5
+        kk = np.diff(offs_h[0, h])
+        assert np.array_equal(kk, budget.allocate(wq_h[0, h], K, 1))
+        assert kk.max() >= 2 * kk.min()  # genuinely ragged
+        lists = [idx_h[0, h, offs_h[0, h, i]:offs_h[0, h, i + 1]] for i in range(T)]
+        ref_lists, score = budget.route_ragged(qn[0, h], st["kbar"], st["M"], kk, 0.1, scale, 64)
+        ex = _check_lists(lists, ref_lists, score)
+        log(f"[budget] varying need h{h}: k_i {kk.min()}..{kk.max()}, excused rows {ex}")
+        for i in range(T):
+            idx_or[0, h, offs_h[0, h, i]:offs_h[0, h, i + 1]] = torch.from_numpy(ref_lists[i].astype(np.int32))
+        refs.append((st, ref_lists))
+    o = paro.attention_csr(qd, kd, vd, *stats[:3], offsets, idx_or.cuda(), K).float().cpu().numpy()
+    for h, (st, ref_lists) in enumerate(refs):
+        check_attention(o[0, h], pisa.attention(qn[0, h], kn[0, h], vn[0, h], st, ref_lists, scale, 64), "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_csr_attention_on_random_ragged_lists(dtype):
+    """Hand-made lists: every row a random count in [0, T] (0 and T included)
+    of random distinct blocks, neighbouring rows of one workgroup very
+    different, a head stride larger than the total."""
+    from workloads import random_uniform_inputs
+    B, H, L, d = 2, 1, 64 * 21 - 30, 64
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v = random_uniform_inputs(B, H, L, d, dtype=tdt, seed=23, scale=0.8)
+    T, scale = -(-L // 64), 1 / np.sqrt(d)
+    g = np.random.default_rng(5)
+    stride = T * T + 7
+    offsets = torch.zeros(B, H, T + 1, dtype=torch.int32)
+    idx = torch.full((B, H, stride), -1, dtype=torch.int32)
+    lists = {}
+    for b in range(B):
+        for h in range(H):
+            ks = g.integers(0, T + 1, T)
+            ks[:3] = [0, T, 1]
+            pos = 0
+            for i in range(T):
+                sel = np.sort(g.choice(T, size=int(ks[i]), replace=False))
+                lists[(b, h, i)] = sel
+                offsets[b, h, i] = pos
+                idx[b, h, pos:pos + len(sel)] = torch.from_numpy(sel.astype(np.int32))
+                pos += len(sel)
+            offsets[b, h, T] = pos
+    (qd, kd, vd), stats, _ = run_gpu(q, k, v, 1, 0.1)
+    o = paro.attention_csr(qd, kd, vd, *stats[:3], offsets.cuda(), idx.cuda(), stride).float().cpu().numpy()
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    for b in range(B):
+        for h in range(H):
+            st = pisa.block_stats(kn[b, h], vn[b, h], 64)
+            ref = pisa.attention(qn[b, h], kn[b, h], vn[b, h], st, [lists[(b, h, i)] for i in range(T)], scale, 64)
+            check_attention(o[b, h], ref, dtype)
