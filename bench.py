@@ -16,6 +16,9 @@ the kv-blocks exact). Prints one JSON line:
                 TFLOP/s, and the attention against the mixed peak (the
                 key-query half of the FLOPs at the fp8 rate, the rest at the
                 bf16 rate); reported beside the bf16 headline, never as it
+  budget        per-query-block budgets: paro_route_budget with the same
+                total (keep_k T blocks per head, at least one per row) and
+                paro_attention_csr on its lists; times and the spread of k_i
   reorder       the geometric token reordering (paro_reorder) of one
                 [B, H, L, d] tensor into the tiled order and back, against
                 the HBM peak (one read and one write of every row)
@@ -203,6 +206,31 @@ def fp8_entry(w, qd, kd, vd, stats, idx, out, attn_flops, exact_flops, reps: int
     }
 
 
+def budget_entry(w, qd, kd, vd, stats, out, reps: int = 3):
+    """paro_route_budget (the fixed-k total, k_min = 1) and paro_attention_csr."""
+    import torch
+    from block_sparse_attention_pisa_amd import paro
+    stream = torch.cuda.current_stream()
+    K = w.k * w.T
+    res = {}
+
+    def timed(fn):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            r = fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps, r
+
+    route_ms, (offsets, idx, _) = timed(lambda: paro.route_budget(qd, stats[0], stats[3], K, 1, w.lam))
+    attn_ms, _ = timed(lambda: paro.attention_csr(qd, kd, vd, stats[0], stats[1], stats[2], offsets, idx, K, out=out))
+    kk = torch.diff(offsets.to(torch.int64), dim=-1)
+    return {"k_total_per_head": K, "k_min": 1, "route_ms": round(route_ms, 4), "attention_ms": round(attn_ms, 4),
+            "k_i_min": int(kk.min()), "k_i_max": int(kk.max())}
+
+
 def cpu_baseline(w, q, k, v, nq: int, nheads: int):
     """Time the fp64 oracle on host cores on a bounded sample of the workload.
 
@@ -322,6 +350,7 @@ def main():
     ex_ms = ex_ev[0].elapsed_time(ex_ev[1]) / 3
     ex_tf = exact_flops / (ex_ms * 1e-3) / 1e12
     reorder = reorder_entry(w, qd, out)
+    budget = budget_entry(w, qd, kd, vd, stats, out)
     fp8 = fp8_entry(w, qd, kd, vd, stats, idx, out, attn_flops, exact_flops) if w.dtype == "bf16" else None
 
     # cold steps: L2 and MALL flushed by a 512 MB write before each step
@@ -380,6 +409,7 @@ def main():
                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(ex_tf / PEAK_BF16_TFLOPS, 4)},
         "fp8": fp8,
+        "budget": budget,
         "reorder": reorder,
         "cold_ms_per_step": round(sorted(cold)[1], 4),
         "input_generation_s": round(t_gen, 1),
