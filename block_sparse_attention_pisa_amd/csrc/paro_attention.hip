@@ -10,17 +10,18 @@
 //  * The exact lists of the 4 blocks are merged into their sorted union; each
 //    union tile (64 keys x d) is staged once into LDS for all 8 waves (the
 //    global loads of the tile after next sit in registers while the current
-//    one is consumed; two LDS buffers; one LDS-only barrier per tile). K is
-//    stored row-major and V transposed (V^T[dim][key]); rows are padded so
-//    every MFMA operand is one conflict-free ds_read_b128 at a per-lane base
-//    plus a compile-time offset.
+//    one is consumed; two LDS buffers; one LDS-only barrier per tile). K and
+//    V are both stored row-major, rows padded so that no operand read has a
+//    bank conflict: a K operand is one ds_read_b128, a V^T operand two
+//    transposing reads (ds_read_b64_tr_b16, new in CDNA4), each at a per-lane
+//    base plus a compile-time offset, so V needs no transpose on its way in.
 //  * A wave computes S^T = K Q^T for its 32 queries on
 //    v_mfma_f32_32x32x16_bf16 with Q^T held in registers. In the C layout of
 //    S^T each lane owns one query and 32 keys of the tile, so the softmax
 //    state is per lane.
 //  * O^T += V^T P^T with P straight from the S^T accumulators (K rows are read
 //    in a permuted order so each lane's 8 consecutive P values are 8
-//    consecutive keys of a V^T row).
+//    consecutive keys, the 8 keys its V^T operand holds).
 //  * The softmax reference m is fixed by the first tile a wave sees and never
 //    moves, so O needs no rescaling: N and D share the factor exp(-m), which
 //    cancels in N / D. A tile whose maximum exceeds m by more than 2^64 (far
@@ -59,24 +60,25 @@ struct Geo {
   static constexpr int CG = D / 8;                         // 16-byte chunks in a bf16 K row
   static constexpr int KS = D + 24;                        // bf16 K tile row stride (elements): D dims and padding
   static constexpr int KSB = D + 16;                       // fp8 K tile row stride (bytes): D dims and padding
-  static constexpr int VS = 64 + 8;                        // V^T tile row stride
+  static constexpr int VSR = D + 32;                       // V tile row stride (row-major, read transposed)
   static constexpr int HS = D + 8;                         // Hbar^T row stride
   // K tile (elements of 2 bytes); fp8: 64 rows, then the 64 row-scale bytes
   static constexpr int KTILE = F8 ? (64 * KSB + 64) / 2 : 64 * KS;
-  static constexpr int VTILE = D * VS;
+  static constexpr int VTILE = 64 * VSR;
   static constexpr int BUF = KTILE + VTILE;                // one staging buffer (elements)
   static constexpr int NK = D / 16;                        // bf16 k-steps of S^T = K Q^T over the D dims
   static constexpr int NK8 = D / 64;                       // fp8 k-steps
   static constexpr int NU = D / 32;                        // 32-dim output tiles
   // K items (16 bytes) staged per thread and tile; fp8: 4 D items, threads < 4 D take one each
   static constexpr int KPT = F8 ? 1 : 64 * CG / kAttnThreads;
+  static constexpr int VPT = 64 * CG / kAttnThreads;       // V chunks staged per thread and tile
   static constexpr int VI = KPT;                           // first V register
-  static constexpr int EI = KPT + 2;                       // fp8: the row-scale item (threads 0-3)
-  static constexpr int NR = KPT + 2 + (F8 ? 1 : 0);        // staging registers (16 B)
+  static constexpr int EI = KPT + VPT;                     // fp8: the row-scale item (threads 0-3)
+  static constexpr int NR = KPT + VPT + (F8 ? 1 : 0);      // staging registers (16 B)
   static_assert(D * HS <= 2 * BUF, "Hbar^T must fit in the staging buffers");
-  static_assert(32 * CG == kAttnThreads || 32 * CG * 2 == kAttnThreads, "V items per thread");
+  static_assert(64 * CG % kAttnThreads == 0, "V items per thread");
   static_assert(!F8 || 4 * D <= kAttnThreads, "fp8 K items per thread");
-  static_assert(KTILE % 8 == 0, "V^T tile alignment");
+  static_assert(KTILE % 8 == 0, "V tile alignment");
 };
 
 // Key (tile row) that MFMA row m of S^T sub-tile t reads, chosen so that
@@ -109,9 +111,8 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 
 // One step's data in flight, NR registers of 16 bytes per thread:
-// r[0..KPT) = K chunks; r[VI..VI+2) = 2 keys x 8 dims of V.
-// V items put consecutive lanes on consecutive keys, so each LDS write
-// instruction fills whole V^T rows.
+// r[0..KPT) = K chunks; r[VI..VI+VPT) = V chunks, laid out as the K chunks
+// (8 dims of one key each, consecutive lanes on consecutive chunks of a row).
 template <int D, bool F8 = false>
 struct Stage {
   uint4 r[Geo<D, F8>::NR];
@@ -122,7 +123,7 @@ template <int D, bool F8 = false>
 struct StageOffs {
   uint32_t k[Geo<D, F8>::KPT];  // K chunk i: row q / CG, chunk q % CG (q = tid + threads * i);
                                 // fp8: row tid / (D / 16), chunk tid % (D / 16)
-  uint32_t v;                   // V rows 2 kp, 2 kp + 1 (this one and + D * 2), dims 8 dg
+  uint32_t v[Geo<D, F8>::VPT];  // V chunk i: row q / CG, chunk q % CG (q = tid + threads * i)
   __device__ __forceinline__ void init() {
     constexpr int CG = Geo<D>::CG;
     const int tid = threadIdx.x;
@@ -135,9 +136,11 @@ struct StageOffs {
         k[i] = static_cast<uint32_t>((q / CG) * D * 2 + 16 * (q % CG));
       }
     }
-    const int item = tid % (32 * CG);
-    const int kp = item & 31, dg = item >> 5;
-    v = static_cast<uint32_t>(2 * kp * D * 2 + 16 * dg);
+#pragma unroll
+    for (int i = 0; i < Geo<D, F8>::VPT; ++i) {
+      const int q = tid + kAttnThreads * i;
+      v[i] = static_cast<uint32_t>((q / CG) * D * 2 + 16 * (q % CG));
+    }
   }
 };
 
@@ -163,16 +166,12 @@ __device__ __forceinline__ void load_rows(const void* kr, const uint16_t* vr, co
 #pragma unroll
     for (int i = 0; i < KPT; ++i) st.r[i] = bload(rk, of.k[i]);
   }
-  st.r[VI] = bload(rv, of.v);
-  st.r[VI + 1] = bload(rv, of.v + D * 2);
-}
-// Interleave the 16-bit elements e of two rows: low half from a, high from b.
-__device__ __forceinline__ uint32_t pair16(uint32_t a, uint32_t b, bool high) {
-  return __builtin_amdgcn_perm(b, a, high ? 0x07060302u : 0x05040100u);
+#pragma unroll
+  for (int i = 0; i < Geo<D, F8>::VPT; ++i) st.r[VI + i] = bload(rv, of.v[i]);
 }
 template <int D, bool F8 = false>
 __device__ __forceinline__ void store_exact(const Stage<D, F8>& st, uint16_t* buf) {
-  constexpr int CG = Geo<D>::CG, KPT = Geo<D, F8>::KPT, KS = Geo<D>::KS, VS = Geo<D>::VS, VI = Geo<D, F8>::VI;
+  constexpr int CG = Geo<D>::CG, KPT = Geo<D, F8>::KPT, KS = Geo<D>::KS, VSR = Geo<D>::VSR, VI = Geo<D, F8>::VI;
   uint16_t* vt = buf + Geo<D, F8>::KTILE;
   if (F8) {
     constexpr int KSB = Geo<D>::KSB;
@@ -187,14 +186,10 @@ __device__ __forceinline__ void store_exact(const Stage<D, F8>& st, uint16_t* bu
       *reinterpret_cast<uint4*>(buf + (q / CG) * KS + 8 * (q % CG)) = st.r[i];
     }
   }
-  if (threadIdx.x < 32 * CG) {
-    const int item = threadIdx.x;
-    const int kp = item & 31, dg = item >> 5;
-    const uint32_t a[4] = {st.r[VI].x, st.r[VI].y, st.r[VI].z, st.r[VI].w};
-    const uint32_t b[4] = {st.r[VI + 1].x, st.r[VI + 1].y, st.r[VI + 1].z, st.r[VI + 1].w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<uint32_t*>(vt + (8 * dg + e) * VS + 2 * kp) = pair16(a[e >> 1], b[e >> 1], e & 1);
+  for (int i = 0; i < Geo<D, F8>::VPT; ++i) {
+    const int q = threadIdx.x + kAttnThreads * i;
+    *reinterpret_cast<uint4*>(vt + (q / CG) * VSR + 8 * (q % CG)) = st.r[VI + i];
   }
 }
 // ------------------------------------------------------------ fp8
@@ -316,14 +311,25 @@ __device__ __forceinline__ f32x16 qk_half8(const uint8_t* kt, int sa, const Acc<
   return mfma32x32x16(a.kref, a.qx, s);
 }
 
-// O^T += V^T P^T for 32 keys (vt: the lane's V^T row base plus the key offset).
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+// V^T operand (8 keys x 1 dim per lane) from the row-major V tile: two
+// transposing reads, keys key0 .. key0 + 3 and key0 + 4 .. key0 + 7, where
+// p is the lane's supplier address (see voff in the kernel).
+template <int D>
+__device__ __forceinline__ bf16x8 v_op(const uint16_t* p) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const_cast<uint16_t*>(p)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const_cast<uint16_t*>(p + 4 * Geo<D>::VSR)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// O^T += V^T P^T for 32 keys (vt: the lane's supplier base plus the key offset).
 template <int D>
 __device__ __forceinline__ void pv_half(const uint16_t* vt, const bf16x8 (&pb)[2], Acc<D>& a) {
 #pragma unroll
   for (int u = 0; u < Geo<D>::NU; ++u)
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-      a.o[u] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(vt + 32 * u * Geo<D>::VS + 16 * s), pb[s], a.o[u]);
+    for (int s = 0; s < 2; ++s) a.o[u] = mfma32x32x16(v_op<D>(vt + 16 * s * Geo<D>::VSR + 32 * u), pb[s], a.o[u]);
 }
 
 // Lane predicate for accumulator register i of a 32-key S^T half: whether the
@@ -408,7 +414,7 @@ constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
 template <int D, bool kMask, bool kLast = false>
 __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int voff, Acc<D>& a, uint64_t km,
                                             uint64_t kl, float& pl) {
-  constexpr int NK = Geo<D>::NK, NU = Geo<D>::NU, KS = Geo<D>::KS, VS = Geo<D>::VS;
+  constexpr int NK = Geo<D>::NK, NU = Geo<D>::NU, KS = Geo<D>::KS, VSR = Geo<D>::VSR;
   constexpr int NV = 2 * NU;
   constexpr int kValu = kMask ? 52 : 36;  // VALU instructions of one softmax half (approximate)
   const uint16_t* kp = bc + koff;
@@ -437,7 +443,7 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) v0[2 * u + h] = *reinterpret_cast<const bf16x8*>(vp + 32 * u * VS + 16 * h);
+    for (int h = 0; h < 2; ++h) v0[2 * u + h] = v_op<D>(vp + 16 * h * VSR + 32 * u);
 #pragma unroll
   for (int ks = 0; ks < NKX; ++ks) s1 = mfma32x32x16(kop(k1, ks), qop(ks), s1);
   float pl0 = 0.f, pl1 = 0.f;
@@ -454,7 +460,7 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) v1[2 * u + h] = *reinterpret_cast<const bf16x8*>(vp + 32 + 32 * u * VS + 16 * h);
+    for (int h = 0; h < 2; ++h) v1[2 * u + h] = v_op<D>(vp + (32 + 16 * h) * VSR + 32 * u);
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
@@ -484,7 +490,7 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
 template <int D, bool kMask, bool kLast = false>
 __device__ __forceinline__ float exact_tile8(const uint8_t* kb, const uint8_t* sc, int ql, const uint16_t* bc,
                                              int voff, Acc<D>& a, uint64_t km, uint64_t kl, float& pl) {
-  constexpr int NK8 = Geo<D>::NK8, NU = Geo<D>::NU, KSB = Geo<D>::KSB, VS = Geo<D>::VS;
+  constexpr int NK8 = Geo<D>::NK8, NU = Geo<D>::NU, KSB = Geo<D>::KSB, VSR = Geo<D>::VSR;
   constexpr int NV = 2 * NU;
   constexpr int kValu = kMask ? 52 : 36;
   constexpr int NKX = NK8 + 1;
@@ -520,7 +526,7 @@ __device__ __forceinline__ float exact_tile8(const uint8_t* kb, const uint8_t* s
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) v0[2 * u + h] = *reinterpret_cast<const bf16x8*>(vp + 32 * u * VS + 16 * h);
+    for (int h = 0; h < 2; ++h) v0[2 * u + h] = v_op<D>(vp + 16 * h * VSR + 32 * u);
 #pragma unroll
   for (int st = 0; st < NK8; ++st)
     s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k1[st], a.q8[st], s1, 0, 0, 0, sa1, 0, a.qe);
@@ -539,7 +545,7 @@ __device__ __forceinline__ float exact_tile8(const uint8_t* kb, const uint8_t* s
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) v1[2 * u + h] = *reinterpret_cast<const bf16x8*>(vp + 32 + 32 * u * VS + 16 * h);
+    for (int h = 0; h < 2; ++h) v1[2 * u + h] = v_op<D>(vp + (32 + 16 * h) * VSR + 32 * u);
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
@@ -599,7 +605,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     int mode, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ ke, const uint8_t* __restrict__ kb8,
     const uint8_t* __restrict__ kbe, const int32_t* __restrict__ offs) {
   const bool tail = mode != kModeDrop, corr = mode == kModePisa;
-  constexpr int BUF = Geo<D, F8>::BUF, KS = Geo<D>::KS, KSB = Geo<D>::KSB, VS = Geo<D>::VS, HS = Geo<D>::HS;
+  constexpr int BUF = Geo<D, F8>::BUF, KS = Geo<D>::KS, KSB = Geo<D>::KSB, VSR = Geo<D>::VSR, HS = Geo<D>::HS;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* buf = reinterpret_cast<uint16_t*>(smem);  // 2 staging buffers
   const int nw = ceil_div(T, 32);
@@ -629,7 +635,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   // per-lane operand offsets inside a staging buffer
   const int koff = perm_key(0, ql) * KS + 8 * g;              // K rows of sub-tile 0 (+32 KS for 1)
   const int koff8 = perm_key(0, ql) * KSB + 32 * g;           // fp8: bytes, (+32 KSB for sub-tile 1)
-  const int voff = Geo<D, F8>::KTILE + ql * VS + 8 * g;       // V^T rows 32 u + ql (+16 s + 32 t keys)
+  // supplier address of the transposing V reads: in 16-lane group G = l / 16,
+  // lane 4 k + j reads row (key) 8 g + k, dims 16 (G % 2) + 4 j .. + 4, so
+  // that the group's output lane i gets dim 16 (G % 2) + i of keys .. + 3
+  const int voff = Geo<D, F8>::KTILE + (8 * g + (l & 15) / 4) * VSR + 16 * ((l >> 4) & 1) + 4 * (l & 3);
 
   Acc<D> a;
   {
@@ -910,7 +919,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
           ps += softmax_half<D, true, true, true>(s1, a, shift, static_cast<uint32_t>(km >> 32),
                                                   static_cast<uint32_t>(kl >> 32), p1, pl1);
           pv_half<D>(buf + voff, p0, a);
-          pv_half<D>(buf + voff + 32, p1, a);
+          pv_half<D>(buf + voff + 32 * VSR, p1, a);
           a.dsum += 64.f * ps + (static_cast<float>(nlast) - 64.f) * (pl0 + pl1);
           a.csum += ps;
         }
