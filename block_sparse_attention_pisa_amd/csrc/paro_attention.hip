@@ -16,9 +16,10 @@
 //    transposing reads (ds_read_b64_tr_b16, new in CDNA4), each at a per-lane
 //    base plus a compile-time offset, so V needs no transpose on its way in.
 //  * A wave computes S^T = K Q^T for its 32 queries on
-//    v_mfma_f32_32x32x16_bf16 with Q^T held in registers. In the C layout of
-//    S^T each lane owns one query and 32 keys of the tile, so the softmax
-//    state is per lane.
+//    v_mfma_f32_32x32x16_bf16 with Q^T held in registers, the accumulators
+//    starting at -m (the softmax reference). In the C layout of S^T each
+//    lane owns one query and 32 keys of the tile, so the softmax state is
+//    per lane.
 //  * O^T += V^T P^T with P straight from the S^T accumulators (K rows are read
 //    in a permuted order so each lane's 8 consecutive P values are 8
 //    consecutive keys, the 8 keys its V^T operand holds).
@@ -273,8 +274,7 @@ struct Acc {
   bf16x8 qb[Geo<D>::NK];   // B operand (scale log2(e) Q)^T in bf16: query lane % 32, dims 16 s + 8 g .. + 8
   i32x8 q8[Geo<D>::NK8];   // fp8 path: B operand (scale log2(e) Q)^T 2^-qe in e4m3: dims 64 s + 32 g .. + 32
   int qe;                  // fp8 path: E8M0 code of the lane's query scale
-  bf16x8 qx;               // B operand of the reference k-step: -m of the lane's query (half 0 lanes, element 0)
-  bf16x8 kref;             // A operand of the reference k-step: 1 for every key (half 0 lanes, element 0)
+  f32x16 nm;               // -m in every element: the C operand that starts each S^T chain
   f32x16 o[Geo<D>::NU];    // O^T: dims 32 u + 8 (i / 4) + 4 g + i % 4, query lane % 32
   float m;                 // softmax reference (log2 units); the logits S^T come out as logit - m
   float dsum;              // this lane's part of D
@@ -286,12 +286,11 @@ struct Acc {
 // units relative to the reference: scale log2(e) q.k - m.
 template <int D>
 __device__ __forceinline__ f32x16 qk_half(const uint16_t* kt, const Acc<D>& a) {
-  f32x16 s = f32x16{};
+  f32x16 s = a.nm;
 #pragma unroll
   for (int ks = 0; ks < Geo<D>::NK; ++ks)
     s = mfma32x32x16(*reinterpret_cast<const bf16x8*>(kt + 16 * ks), a.qb[ks], s);
-  // reference k-step: a K column of ones against Q^T rows (-m, 0, ..)
-  return mfma32x32x16(a.kref, a.qx, s);
+  return s;
 }
 
 // fp8 path: S^T of 32 keys (kt: the lane's permuted fp8 K row plus 32 g
@@ -299,7 +298,7 @@ __device__ __forceinline__ f32x16 qk_half(const uint16_t* kt, const Acc<D>& a) {
 // their power-of-two scales into the MFMA, which applies them.
 template <int D>
 __device__ __forceinline__ f32x16 qk_half8(const uint8_t* kt, int sa, const Acc<D>& a) {
-  f32x16 s = f32x16{};
+  f32x16 s = a.nm;
 #pragma unroll
   for (int st = 0; st < Geo<D>::NK8; ++st) {
     const uint4 lo = *reinterpret_cast<const uint4*>(kt + 64 * st);
@@ -308,7 +307,7 @@ __device__ __forceinline__ f32x16 qk_half8(const uint8_t* kt, int sa, const Acc<
                       static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
     s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kk, a.q8[st], s, 0, 0, 0, sa, 0, a.qe);
   }
-  return mfma32x32x16(a.kref, a.qx, s);
+  return s;
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -355,12 +354,12 @@ __device__ __forceinline__ float half_max_masked(const f32x16& s, uint32_t km) {
 template <int D>
 __device__ __forceinline__ void set_reference(Acc<D>& a, float m) {
   a.m = m;
-  const uint32_t w0 = (threadIdx.x & 32) ? 0u : static_cast<uint32_t>(f32_to_bf16(-m));
-  a.qx = __builtin_bit_cast(bf16x8, make_uint4(w0, 0u, 0u, 0u));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a.nm[i] = -m;
 }
 
 // Softmax weights exp2(S^T) of one 32-key sub-tile (the reference is already
-// subtracted by the MFMA; kShift adds shift first), with no data-dependent
+// in the accumulators, which start at -m; kShift adds shift first), with no data-dependent
 // branches; returns this lane's sum of the bf16-rounded weights, which is
 // also what the numerator sees.
 // kMask: keys whose bit is set in the wave-uniform mask km get weight 0.
@@ -419,10 +418,8 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
   constexpr int kValu = kMask ? 52 : 36;  // VALU instructions of one softmax half (approximate)
   const uint16_t* kp = bc + koff;
   const uint16_t* vp = bc + voff;
-  constexpr int NKX = NK + 1;  // the D dims plus the reference k-step
+  constexpr int NKX = NK;
   bf16x8 k0[NK], k1[NK], v0[NV], v1[NV];
-  auto qop = [&](int ks) { return ks < NK ? a.qb[ks] : a.qx; };
-  auto kop = [&](const bf16x8 (&k)[NK], int ks) { return ks < NK ? k[ks] : a.kref; };
   // region 1: K operands of half 0
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks) k0[ks] = *reinterpret_cast<const bf16x8*>(kp + 16 * ks);
@@ -430,9 +427,9 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
   // region 2: S^T half 0 | K operands of half 1
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks) k1[ks] = *reinterpret_cast<const bf16x8*>(kp + 32 * KS + 16 * ks);
-  f32x16 s0 = f32x16{}, s1 = f32x16{};
+  f32x16 s0 = a.nm, s1 = a.nm;
 #pragma unroll
-  for (int ks = 0; ks < NKX; ++ks) s0 = mfma32x32x16(kop(k0, ks), qop(ks), s0);
+  for (int ks = 0; ks < NK; ++ks) s0 = mfma32x32x16(k0[ks], a.qb[ks], s0);
 #pragma unroll
   for (int i = 0; i < NKX; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
@@ -445,7 +442,7 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
 #pragma unroll
     for (int h = 0; h < 2; ++h) v0[2 * u + h] = v_op<D>(vp + 16 * h * VSR + 32 * u);
 #pragma unroll
-  for (int ks = 0; ks < NKX; ++ks) s1 = mfma32x32x16(kop(k1, ks), qop(ks), s1);
+  for (int ks = 0; ks < NK; ++ks) s1 = mfma32x32x16(k1[ks], a.qb[ks], s1);
   float pl0 = 0.f, pl1 = 0.f;
   bf16x8 p0[2], p1[2];
   float ps = softmax_half<D, kMask, kLast>(s0, a, 0.f, static_cast<uint32_t>(km), static_cast<uint32_t>(kl), p0, pl0);
@@ -493,7 +490,7 @@ __device__ __forceinline__ float exact_tile8(const uint8_t* kb, const uint8_t* s
   constexpr int NK8 = Geo<D>::NK8, NU = Geo<D>::NU, KSB = Geo<D>::KSB, VSR = Geo<D>::VSR;
   constexpr int NV = 2 * NU;
   constexpr int kValu = kMask ? 52 : 36;
-  constexpr int NKX = NK8 + 1;
+  constexpr int NKX = NK8;
   const uint16_t* vp = bc + voff;
   i32x8 k0[NK8], k1[NK8];
   bf16x8 v0[NV], v1[NV];
@@ -511,11 +508,10 @@ __device__ __forceinline__ float exact_tile8(const uint8_t* kb, const uint8_t* s
   // region 2: S^T half 0 | K operands of half 1
 #pragma unroll
   for (int st = 0; st < NK8; ++st) k1[st] = ld(kb + 32 * KSB + 64 * st);
-  f32x16 s0 = f32x16{}, s1 = f32x16{};
+  f32x16 s0 = a.nm, s1 = a.nm;
 #pragma unroll
   for (int st = 0; st < NK8; ++st)
     s0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k0[st], a.q8[st], s0, 0, 0, 0, sa0, 0, a.qe);
-  s0 = mfma32x32x16(a.kref, a.qx, s0);
 #pragma unroll
   for (int i = 0; i < NKX; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
@@ -530,7 +526,6 @@ __device__ __forceinline__ float exact_tile8(const uint8_t* kb, const uint8_t* s
 #pragma unroll
   for (int st = 0; st < NK8; ++st)
     s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k1[st], a.q8[st], s1, 0, 0, 0, sa1, 0, a.qe);
-  s1 = mfma32x32x16(a.kref, a.qx, s1);
   float pl0 = 0.f, pl1 = 0.f;
   bf16x8 p0[2], p1[2];
   float ps = softmax_half<D, kMask, kLast>(s0, a, 0.f, static_cast<uint32_t>(km), static_cast<uint32_t>(kl), p0, pl0);
@@ -700,7 +695,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
                                                       pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7])));
     }
   }
-  a.kref = __builtin_bit_cast(bf16x8, make_uint4(g == 0 ? 0x3F80u : 0u, 0u, 0u, 0u));
   StageOffs<D, F8> of;
   of.init();
 
