@@ -969,10 +969,17 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   // ---- stage 3: global first-order correction, then N / D
   const float csum = a.csum + __shfl_xor(a.csum, 32);
   const float dsum = a.dsum + __shfl_xor(a.dsum, 32);
+  // the per-lane indices again, from an opaque copy of the thread id: the
+  // compiler recomputes them here instead of keeping them live (and spilled
+  // to memory) across the tile loops
+  int t3 = threadIdx.x;
+  asm volatile("" : "+v"(t3));
+  const int g3 = (t3 >> 5) & 1, ql3 = t3 & 31;
+  const int row3 = (grp * kQB + (t3 >> 7)) * 64 + 32 * ((t3 >> 6) & 1) + ql3;
   if (nch > 0 && corr) {
     // Hbar^T in bf16: ht[v][k] = Hbar[k][v], rows padded to HS
     const float* Hh = Hbar + static_cast<size_t>(bh) * D * D;
-    for (int item = tid; item < (D / 4) * Geo<D>::CG; item += kAttnThreads) {
+    for (int item = t3; item < (D / 4) * Geo<D>::CG; item += kAttnThreads) {
       const int kg = item % (D / 4), vg = item / (D / 4);
       float f[4][8];
 #pragma unroll
@@ -991,9 +998,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   }
   // MFMAs need the whole wave: only the stores are guarded per lane.
   if (qvalid) {
-    const uint16_t* hrow = buf + ql * HS + 8 * g;
+    const uint16_t* hrow = buf + ql3 * HS + 8 * g3;
     const float inv = 1.f / dsum;
-    uint16_t* op = O + head + static_cast<size_t>(row) * D;
+    uint16_t* op = O + static_cast<size_t>(bh) * L * D + static_cast<size_t>(row3) * D;
 #pragma unroll
     for (int u = 0; u < Geo<D>::NU; ++u) {
       f32x16 o = a.o[u];
@@ -1004,10 +1011,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
           r = mfma32x32x16(*reinterpret_cast<const bf16x8*>(hrow + 32 * u * HS + 16 * ks), a.qb[ks], r);
         o += (kLn2 * csum) * r;  // r = Hbar^T (scale log2(e) q): scale c Hbar^T q = ln2 c r
       }
-      if (row < L) {
+      if (row3 < L) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int dim = 32 * u + 8 * q + 4 * g;
+          const int dim = 32 * u + 8 * q + 4 * g3;
           *reinterpret_cast<uint2*>(op + dim) = make_uint2(pack_bf16x2(o[4 * q] * inv, o[4 * q + 1] * inv),
                                                            pack_bf16x2(o[4 * q + 2] * inv, o[4 * q + 3] * inv));
         }
