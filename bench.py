@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact-phase", action="store_true",
                     help="skip the all-exact control run that isolates the exact phase")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the error-against-dense table of the method and its ablations")
     ap.add_argument("--cpu-qblocks", type=int, default=48, help="query blocks per head in the oracle sample")
     ap.add_argument("--cpu-heads", type=int, default=1)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -229,6 +231,43 @@ def budget_entry(w, qd, kd, vd, stats, out, reps: int = 3):
     kk = torch.diff(offsets.to(torch.int64), dim=-1)
     return {"k_total_per_head": K, "k_min": 1, "route_ms": round(route_ms, 4), "attention_ms": round(attn_ms, 4),
             "k_i_min": int(kk.min()), "k_i_max": int(kk.max())}
+
+
+def ablation_entry(name: str = "video480p_32760", permille=(50, 100, 125, 250, 500)):
+    """Error against dense attention of the method and its two ablations,
+    the zeroth-order tail alone and keep-or-drop, as a function of density
+    (the paradigm contrast of the PISA page, sections 1 and 3). Dense
+    attention is the fp32 pipeline on the same bf16 values with every block
+    exact (keep_k = T leaves no tail). Error: relative Frobenius norm over
+    all heads and rows, in fp32 on the device."""
+    import torch
+    from block_sparse_attention_pisa_amd import paro
+    from workloads import WORKLOADS, make_inputs
+    w = WORKLOADS[name]
+    T = w.T
+    q, k, v = make_inputs(w)
+    q32, k32, v32 = (x.float().cuda() for x in (q, k, v))
+    st32 = paro.precompute(k32, v32)
+    dense = paro.attention(q32, k32, v32, st32[0], st32[1], st32[2],
+                           paro.route(q32, st32[0], st32[3], T, w.lam), T)
+    del q32, k32, v32, st32
+    nd = float(dense.norm())
+    qd, kd, vd = (x.cuda() for x in (q, k, v))
+    stats = paro.precompute(kd, vd)
+    rows = []
+    for pm in permille:
+        kk = -(-pm * T // 1000)
+        idx = paro.route(qd, stats[0], stats[3], kk, w.lam)
+        r = {"keep_permille": pm, "k": kk}
+        for mode, kw in (("pisa", {}), ("zeroth", {"first_order": False}), ("drop", {"drop_tail": True})):
+            o = paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, kk, **kw)
+            r[mode] = round(float((o.float() - dense).norm()) / nd, 6)
+        rows.append(r)
+    full = paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], paro.route(qd, stats[0], stats[3], T, w.lam), T)
+    floor = round(float((full.float() - dense).norm()) / nd, 6)
+    torch.cuda.synchronize()
+    return {"workload": name, "error": "relative Frobenius norm of O - O_dense over all heads",
+            "dense_reference": "fp32 path, every block exact", "bf16_dense_floor": floor, "rows": rows}
 
 
 def cpu_baseline(w, q, k, v, nq: int, nheads: int):
@@ -418,6 +457,8 @@ def main():
         del qd, kd, vd, stats, idx, out
         torch.cuda.empty_cache()
         res["exact_phase"] = exact_phase_entry()
+    if not a.no_ablation:
+        res["ablation"] = ablation_entry()
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, a.cpu_qblocks, a.cpu_heads)
     print(json.dumps(res), flush=True)
