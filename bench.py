@@ -233,13 +233,15 @@ def budget_entry(w, qd, kd, vd, stats, out, reps: int = 3):
             "k_i_min": int(kk.min()), "k_i_max": int(kk.max())}
 
 
-def ablation_entry(name: str = "video480p_32760", permille=(50, 100, 125, 250, 500)):
+def ablation_entry(name: str = "video480p_32760", permille=(50, 100, 125, 250, 500), tile=(2, 4, 8)):
     """Error against dense attention of the method and its two ablations,
     the zeroth-order tail alone and keep-or-drop, as a function of density
-    (the paradigm contrast of the PISA page, sections 1 and 3). Dense
-    attention is the fp32 pipeline on the same bf16 values with every block
-    exact (keep_k = T leaves no tail). Error: relative Frobenius norm over
-    all heads and rows, in fp32 on the device."""
+    (the paradigm contrast of the PISA page, sections 1 and 3), and of the
+    method run on tokens moved into compact (t, y, x) boxes first (the
+    geometric reordering of the PAROAttention page). Dense attention is the
+    fp32 pipeline on the same bf16 values with every block exact (keep_k = T
+    leaves no tail). Error: relative Frobenius norm over all heads and rows,
+    in fp32 on the device."""
     import torch
     from block_sparse_attention_pisa_amd import paro
     from workloads import WORKLOADS, make_inputs
@@ -254,6 +256,9 @@ def ablation_entry(name: str = "video480p_32760", permille=(50, 100, 125, 250, 5
     nd = float(dense.norm())
     qd, kd, vd = (x.cuda() for x in (q, k, v))
     stats = paro.precompute(kd, vd)
+    qt, kt, vt = (paro.reorder(x, w.grid, tile) for x in (qd, kd, vd))
+    stats_t = paro.precompute(kt, vt)
+    tname = "pisa_tiled_" + "x".join(map(str, tile))
     rows = []
     for pm in permille:
         kk = -(-pm * T // 1000)
@@ -262,6 +267,10 @@ def ablation_entry(name: str = "video480p_32760", permille=(50, 100, 125, 250, 5
         for mode, kw in (("pisa", {}), ("zeroth", {"first_order": False}), ("drop", {"drop_tail": True})):
             o = paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, kk, **kw)
             r[mode] = round(float((o.float() - dense).norm()) / nd, 6)
+        idx_t = paro.route(qt, stats_t[0], stats_t[3], kk, w.lam)
+        o_t = paro.attention(qt, kt, vt, stats_t[0], stats_t[1], stats_t[2], idx_t, kk)
+        o = paro.reorder(o_t, w.grid, tile, inverse=True)
+        r[tname] = round(float((o.float() - dense).norm()) / nd, 6)
         rows.append(r)
     full = paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], paro.route(qd, stats[0], stats[3], T, w.lam), T)
     floor = round(float((full.float() - dense).norm()) / nd, 6)
