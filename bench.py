@@ -238,7 +238,9 @@ def ablation_entry(name: str = "video480p_32760", permille=(50, 100, 125, 250, 5
     the zeroth-order tail alone and keep-or-drop, as a function of density
     (the paradigm contrast of the PISA page, sections 1 and 3), and of the
     method run on tokens moved into compact (t, y, x) boxes first (the
-    geometric reordering of the PAROAttention page). Dense attention is the
+    geometric reordering of the PAROAttention page) or with the same total of
+    exact blocks per head shared out by need (per-query-block budgets, the
+    ALLOT review page). Dense attention is the
     fp32 pipeline on the same bf16 values with every block exact (keep_k = T
     leaves no tail). Error: relative Frobenius norm over all heads and rows,
     in fp32 on the device."""
@@ -271,6 +273,11 @@ def ablation_entry(name: str = "video480p_32760", permille=(50, 100, 125, 250, 5
         o_t = paro.attention(qt, kt, vt, stats_t[0], stats_t[1], stats_t[2], idx_t, kk)
         o = paro.reorder(o_t, w.grid, tile, inverse=True)
         r[tname] = round(float((o.float() - dense).norm()) / nd, 6)
+        # the same total per head, shared out by need (per-query-block budgets)
+        kt_ = kk * T
+        offs, idx_b, _ = paro.route_budget(qd, stats[0], stats[3], kt_, 1, w.lam)
+        o = paro.attention_csr(qd, kd, vd, stats[0], stats[1], stats[2], offs, idx_b, kt_)
+        r["pisa_budget"] = round(float((o.float() - dense).norm()) / nd, 6)
         rows.append(r)
     full = paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], paro.route(qd, stats[0], stats[3], T, w.lam), T)
     floor = round(float((full.float() - dense).norm()) / nd, 6)
