@@ -95,8 +95,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   float* qs = reinterpret_cast<float*>(smem);    // qbar [R][D]; dead once the MFMA operands are loaded
   float* dots = reinterpret_cast<float*>(smem);  // [R][T], written after qs is dead
 
-  const int bh = blockIdx.y;
-  const int i0 = blockIdx.x * R;
+  // XCD-aware order: consecutive workgroup ids go to different XCDs, so each
+  // XCD gets a contiguous run of (head, row group) items and a head's kbar,
+  // which every row group of the head reads in full, stays in one L2.
+  const int nwg = gridDim.x, ngrp = ceil_div(T, R);
+  int wg = blockIdx.x;
+  const int n8 = (nwg / 8) * 8;
+  if (wg < n8) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  const int bh = wg / ngrp;
+  const int i0 = (wg % ngrp) * R;
   const int nrows = min(R, T - i0);
   const int t = threadIdx.x, w = t / 64, l = t % 64;
   const E* Qh = Q + static_cast<size_t>(bh) * L * D;
@@ -351,7 +358,7 @@ hipError_t launch_ni(const paro_problem& p, const E* Q, const float* kbar, const
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_route<E, D, NI, kMode>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_route<E, D, NI, kMode>), dim3(ceil_div(T, R), p.B * p.H), dim3(kThreads), lds, s, Q, kbar,
+  hipLaunchKernelGGL((k_route<E, D, NI, kMode>), dim3(ceil_div(T, R) * p.B * p.H), dim3(kThreads), lds, s, Q, kbar,
                      M, ra.idx, p.L, T, R, ra.keep_k, p.scale, ra.lambda, ra.qbar_ws, ra.wq, ra.offsets, ra.kstride);
   return hipGetLastError();
 }
