@@ -25,10 +25,10 @@
 //    consecutive keys, the 8 keys its V^T operand holds).
 //  * The softmax reference m is fixed by the first tile a wave sees and never
 //    moves, so O needs no rescaling: N and D share the factor exp(-m), which
-//    cancels in N / D. A tile whose maximum exceeds m by more than 2^64 (far
-//    beyond real attention logits) marks the wave, and after the pass the
-//    marked waves recompute their rows with m set to the exact maximum
-//    recorded during the first pass.
+//    cancels in N / D. A tile whose weight sum reaches 2^64 (some logit at
+//    least 64 log2 units above m, far beyond real attention logits) marks
+//    the wave, and after the pass the marked waves recompute their rows with
+//    m set to the exact maximum, found by a max-only pass.
 //  * Stage 2 streams all T centroids in chunks of 64 through the same staging
 //    and the same pipelined tile code as the exact tiles (kbar as keys, vsum
 //    as values, rounded to bf16 by a small kernel into a caller workspace),
@@ -36,6 +36,9 @@
 //    p to c.
 //  * Stage 3 forms r^T = Hbar^T q^T on MFMA (Hbar transposed into LDS in
 //    bf16) and adds (scale c) r before the division.
+//  * With F8 (paro_attention_fp8) S^T of every tile runs on the fp8 matrix
+//    cores instead: K, kbar and q' rounded to e4m3 with per-row power-of-two
+//    scales that the MFMA applies; softmax, P V and stage 3 are unchanged.
 //
 // fp32 kernel (k_attn_f32): the same three stages in plain fp32 arithmetic,
 // one key at a time; used for fp32 problems.
