@@ -48,7 +48,7 @@ ATTN_SRCS = [os.path.join(ROOT, "block_sparse_attention_pisa_amd", "csrc", f)
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video720p_75600")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -92,7 +92,7 @@ def attention_flops(w, idx_cpu, with_exact: bool = False):
     return (total, exact_total) if with_exact else total
 
 
-def exact_phase_entry(reps: int = 3):
+def exact_phase_entry(reps: int = 5):
     """The exact phase alone: the same attention kernel on the keep = 100% control
     of the long-video shape (every kv-block exact, no tail, no correction), so
     every MFMA is stage-1 work. FLOPs 4 d sum_i n_i L per head."""
@@ -384,6 +384,12 @@ def main():
     pre = [e[0].elapsed_time(e[1]) for e in evs]
     rou = [e[1].elapsed_time(e[2]) for e in evs]
     att = [e[2].elapsed_time(e[3]) for e in evs]
+    per_step = [e[0].elapsed_time(e[3]) for e in evs]
+
+    def median(x):
+        x = sorted(x)
+        n = len(x)
+        return x[n // 2] if n % 2 else 0.5 * (x[n // 2 - 1] + x[n // 2])
     ms_step = wall * 1e3 / a.steps
     dense_flops = 4.0 * w.B * w.H * w.L * w.L * w.d
     value = dense_flops / (ms_step * 1e-3) / 1e12
@@ -445,6 +451,8 @@ def main():
         "config": {**w.describe(), "parallelism": "none (1 GPU)"},
         "phases_ms": {"precompute": round(pre_ms, 4), "route": round(route_ms, 4),
                       "attention": round(attn_ms, 4)},
+        "median_ms": {"step": round(median(per_step), 4), "precompute": round(median(pre), 4),
+                      "route": round(median(rou), 4), "attention": round(median(att), 4)},
         "precompute_hbm": {"algorithmic_GBs": round(kv_bytes / (pre_ms * 1e-3) / 1e9, 1),
                            "frac_of_peak": round(kv_bytes / (pre_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "route_hbm": {"algorithmic_GBs": round(route_bytes / (route_ms * 1e-3) / 1e9, 1),
