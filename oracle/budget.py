@@ -21,7 +21,12 @@ PISA quantities support:
     rounded to nearest) so the sharing is exact integer arithmetic: row i
     gets floor(R wq_i / sum wq) and the R - sum of those leftover blocks go
     to the rows with the largest remainders (R wq_i mod sum wq), ties to the
-    lower i (the largest-remainder method); rows are capped at T;
+    lower i (the largest-remainder method);
+  * a row holds at most T blocks. The total is fixed, so what a full row
+    cannot take is shared again: every row whose floor share reaches
+    T - k_min is set to T and leaves, and the rest of R is shared among the
+    remaining rows by the same rule, until no share reaches the cap
+    (water-filling). The total is then exactly K whenever K <= T^2;
   * each row then keeps its k_i best blocks by the covariance-aware PISA
     score, exactly as the fixed-k routing does.
 """
@@ -63,19 +68,37 @@ def quantise_weights(w: np.ndarray) -> np.ndarray:
 
 
 def allocate(wq: np.ndarray, k_total: int, k_min: int) -> np.ndarray:
-    """k_i for one head from the integer weights (largest-remainder method)."""
+    """k_i for one head from the integer weights (largest-remainder method,
+    rows capped at T with the excess shared again among the others)."""
     wq = [int(x) for x in wq]
     T = len(wq)
     R = k_total - T * k_min
     assert R >= 0
-    S = sum(wq)
-    base = [R * x // S for x in wq]
-    rem = [R * x % S for x in wq]
-    left = R - sum(base)
-    order = sorted(range(T), key=lambda i: (-rem[i], i))   # largest remainder first, ties to lower i
-    k = [k_min + b for b in base]
-    for i in order[:left]:
-        k[i] += 1
+    cap = T - k_min
+    full = [False] * T
+    while True:
+        act = [i for i in range(T) if not full[i]]
+        S = sum(wq[i] for i in act)
+        if S == 0:
+            break
+        newly = [i for i in act if R * wq[i] // S >= cap]
+        if not newly:
+            break
+        for i in newly:
+            full[i] = True
+        R -= cap * len(newly)
+    k = [T if full[i] else k_min for i in range(T)]
+    act = [i for i in range(T) if not full[i]]
+    if act:
+        S = sum(wq[i] for i in act)
+        base = {i: R * wq[i] // S for i in act}
+        rem = {i: R * wq[i] % S for i in act}
+        left = R - sum(base.values())
+        order = sorted(act, key=lambda i: (-rem[i], i))   # largest remainder first, ties to lower i
+        for i in act:
+            k[i] += base[i]
+        for i in order[:left]:
+            k[i] += 1
     return np.minimum(np.array(k, dtype=np.int64), T)
 
 

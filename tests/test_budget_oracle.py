@@ -53,8 +53,7 @@ def test_allocate_invariants():
         K = int(g.integers(T * k_min, T * k_min + 8 * T))
         wq = budget.quantise_weights(g.uniform(1, T, T))
         k = budget.allocate(wq, K, k_min)
-        if k.max() < T:
-            assert k.sum() == K
+        assert k.sum() == min(K, T * T)   # the total is fixed (all rows full past T^2)
         assert (k >= min(k_min, T)).all()
         # a larger weight never gets fewer blocks, and equal weights differ by at most one
         for i in range(T - 1):
@@ -65,8 +64,17 @@ def test_allocate_invariants():
                 assert abs(int(k[i]) - int(k[j])) <= 1
     # equal weights and K = T k: every row gets k
     assert budget.allocate(np.full(7, 99), 7 * 5, 1).tolist() == [5] * 7
-    # a row that would exceed T is capped
-    assert budget.allocate(np.array([10 ** 6, 1, 1]), 8, 1).tolist() == [3, 1, 1]
+    # a row that would exceed T is capped and its excess shared again: R = 5,
+    # row 0's share 4.99 reaches the cap T - k_min = 2, so it gets 3; the 3
+    # blocks left go to rows 1 and 2 (weights 1, 1: 1.5 each, the odd one to
+    # the lower row)
+    assert budget.allocate(np.array([10 ** 6, 1, 1]), 8, 1).tolist() == [3, 3, 2]
+    # a cascade: T = 4, K = 12, weights 8, 4, 1, 1 (sum 14). Shares 6.9, 3.4,
+    # 0.9, 0.9: row 0 is full (4), 8 left over rows 1-3 (sum 6): 5.3, 1.3,
+    # 1.3, so row 1 is full too; 4 left over rows 2 and 3: 2 each
+    assert budget.allocate(np.array([8, 4, 1, 1]), 12, 0).tolist() == [4, 4, 2, 2]
+    # K = T^2: every row full
+    assert budget.allocate(np.array([5, 1, 1, 1]), 16, 0).tolist() == [4, 4, 4, 4]
 
 
 def test_ragged_routing_with_constant_k_is_the_fixed_k_routing():
