@@ -404,6 +404,7 @@ __global__ __launch_bounds__(kAllocThreads) void k_budget_alloc(const int64_t* _
                                                                  int k_min) {
   __shared__ long long red[kAllocThreads / 64];
   __shared__ int scan[kAllocThreads / 64];
+  __shared__ uint32_t full[PARO_MAX_BLOCKS / 32];  // rows set to T (their excess is shared again)
   const int bh = blockIdx.x, t = threadIdx.x, w = t / 64, l = t % 64;
   const int64_t* wh = wq + static_cast<size_t>(bh) * T;
   int32_t* oh = offsets + static_cast<size_t>(bh) * (T + 1);
@@ -418,15 +419,37 @@ __global__ __launch_bounds__(kAllocThreads) void k_budget_alloc(const int64_t* _
     for (int i = 0; i < kAllocThreads / 64; ++i) sum += red[i];
     return sum;
   };
+  for (int e = t; e < (T + 31) / 32; e += kAllocThreads) full[e] = 0u;
+  __syncthreads();
+  auto is_full = [&](int i) { return ((full[i >> 5] >> (i & 31)) & 1u) != 0u; };
+  // Water-filling: a row whose floor share reaches the cap T - k_min is set
+  // to T and leaves; the rest of R is shared again among the others, until
+  // no share reaches the cap. Each thread tests and sets only its own rows'
+  // bits; block_sum's barriers separate the rounds.
+  const long long cap = static_cast<long long>(T) - k_min;
+  long long Rr = static_cast<long long>(k_total) - static_cast<long long>(T) * k_min;
+  long long S = 0;
+  for (;;) {
+    long long part = 0;
+    for (int i = t; i < T; i += kAllocThreads) part += is_full(i) ? 0 : wh[i];
+    S = block_sum(part);
+    if (S == 0) break;
+    long long c = 0;
+    for (int i = t; i < T; i += kAllocThreads) c += (!is_full(i) && Rr * wh[i] / S >= cap) ? 1 : 0;
+    const long long nf = block_sum(c);
+    if (nf == 0) break;
+    for (int i = t; i < T; i += kAllocThreads)
+      if (!is_full(i) && Rr * wh[i] / S >= cap) atomicOr(&full[i >> 5], 1u << (i & 31));
+    __syncthreads();
+    Rr -= nf * cap;
+  }
   long long part = 0;
-  for (int i = t; i < T; i += kAllocThreads) part += wh[i];
-  const long long S = block_sum(part);
-  const long long Rr = static_cast<long long>(k_total) - static_cast<long long>(T) * k_min;
-  part = 0;
-  for (int i = t; i < T; i += kAllocThreads) part += (S > 0 ? Rr * wh[i] / S : 0);
+  for (int i = t; i < T; i += kAllocThreads) part += (S > 0 && !is_full(i) ? Rr * wh[i] / S : 0);
   const long long left = Rr - block_sum(part);
+  // full rows get key 0, which no candidate below reaches
   auto key_of = [&](int i) -> unsigned long long {
-    const long long rem = S > 0 ? Rr * wh[i] % S : 0;
+    if (S == 0 || is_full(i)) return 0ull;
+    const long long rem = Rr * wh[i] % S;
     return (static_cast<unsigned long long>(rem) << 20) | static_cast<unsigned long long>((1 << 20) - 1 - i);
   };
   unsigned long long thr = ~0ull;  // no extra block when left == 0
@@ -446,8 +469,12 @@ __global__ __launch_bounds__(kAllocThreads) void k_budget_alloc(const int64_t* _
     const int i = c0 + t;
     int k = 0;
     if (i < T) {
-      const long long q = S > 0 ? Rr * wh[i] / S : 0;
-      k = static_cast<int>(min(static_cast<long long>(T), k_min + q + (key_of(i) >= thr ? 1 : 0)));
+      if (is_full(i)) {
+        k = T;
+      } else {
+        const long long q = S > 0 ? Rr * wh[i] / S : 0;
+        k = static_cast<int>(min(static_cast<long long>(T), k_min + q + (key_of(i) >= thr ? 1 : 0)));
+      }
     }
     int incl = k;
 #pragma unroll

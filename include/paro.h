@@ -229,8 +229,10 @@ int32_t paro_reorder_source(const paro_grid* g, int32_t L, int32_t i);
  *   - R = k_total - T k_min is shared in proportion to wq with integer
  *     arithmetic: k_i = k_min + floor(R wq_i / S) (S = sum wq), and the
  *     R - sum of the floors leftover blocks go to the rows of largest
- *     remainder R wq_i mod S, ties to the lower i; k_i is capped at T (the
- *     total is then below k_total);
+ *     remainder R wq_i mod S, ties to the lower i. A row holds at most T
+ *     blocks: every row whose floor share reaches T - k_min is set to T,
+ *     and the rest of R is shared again among the other rows by the same
+ *     rule until no share reaches that cap, so offsets[h][T] = k_total;
  *   - S_i = the k_i best blocks of row i by the covariance-aware score, as in
  *     paro_route (ties to the lower j, ascending).
  * out: weights [B, H, T] int64; offsets [B, H, T + 1] int32, row i of head h

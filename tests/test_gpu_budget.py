@@ -91,11 +91,13 @@ def test_uniform_budget_is_the_fixed_k_path():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
-def test_budget_with_strongly_varying_need():
+@pytest.mark.parametrize("per_row", [10, 30])
+def test_budget_with_strongly_varying_need(per_row):
     """Keys of block j offset by a random mu_j (so centroid logits vary), and
     queries pointing along one direction with a strength of 0.2, 1 or 5 by
     block: sharper rows spread over fewer blocks, so the sharing is far from
-    uniform."""
+    uniform. With 30 blocks per row on average (T = 41) the neediest rows
+    reach T and what they cannot take is shared again among the others."""
     from workloads import random_uniform_inputs
     B, H, L, d = 1, 2, 64 * 40 + 9, 128
     q, k, v = random_uniform_inputs(B, H, L, d, dtype=torch.float32, seed=17, scale=0.8)
@@ -109,7 +111,7 @@ def test_budget_with_strongly_varying_need():
     q = (0.1 * q + f[None, None, :, None] * u).to(torch.bfloat16)
     v = v.to(torch.bfloat16)
     T, scale = -(-L // 64), 1 / np.sqrt(d)
-    K = 10 * T
+    K = per_row * T
     (qd, kd, vd), stats, _ = run_gpu(q, k, v, 1, 0.1)
     offsets, idx, wq = paro.route_budget(qd, stats[0], stats[3], K, 1, 0.1)
     offs_h, idx_h, wq_h = offsets.cpu().numpy(), idx.cpu().numpy(), wq.cpu().numpy()
@@ -122,7 +124,9 @@ def test_budget_with_strongly_varying_need():
         assert (np.abs(wq_h[0, h] / budget.WEIGHT_ONE - w_ref) / w_ref).max() < 1e-5
         kk = np.diff(offs_h[0, h])
         assert np.array_equal(kk, budget.allocate(wq_h[0, h], K, 1))
-        assert kk.max() >= 2 * kk.min()  # genuinely ragged
+        assert kk.max() >= 2 * kk.min() and kk.sum() == K  # genuinely ragged, the total fixed
+        if per_row == 30:
+            assert kk.max() == T and kk.min() < T      # some rows full, the rest shared again
         lists = [idx_h[0, h, offs_h[0, h, i]:offs_h[0, h, i + 1]] for i in range(T)]
         ref_lists, score = budget.route_ragged(qn[0, h], st["kbar"], st["M"], kk, 0.1, scale, 64)
         ex = _check_lists(lists, ref_lists, score)
@@ -170,3 +174,36 @@ def test_csr_attention_on_random_ragged_lists(dtype):
             st = pisa.block_stats(kn[b, h], vn[b, h], 64)
             ref = pisa.attention(qn[b, h], kn[b, h], vn[b, h], st, [lists[(b, h, i)] for i in range(T)], scale, 64)
             check_attention(o[b, h], ref, dtype)
+
+
+@pytest.mark.parametrize("total", ["one", "all"])
+def test_budget_extremes(total):
+    """The smallest and the largest total the ABI accepts (k_min = 0): one
+    block in all (one row gets it, every other row is all tail), and T^2
+    (every row keeps every block: dense attention). Sharing, lists and
+    attention against the oracle."""
+    w = WORKLOADS["tiny_fp32"]
+    q, k, v = make_inputs(w, heads=[1])
+    T = w.T
+    K = 1 if total == "one" else T * T
+    (qd, kd, vd), stats, _ = run_gpu(q, k, v, 1, w.lam)
+    offsets, idx, wq = paro.route_budget(qd, stats[0], stats[3], K, 0, w.lam)
+    offs_h, idx_h, wq_h = offsets.cpu().numpy()[0, 0], idx.cpu().numpy()[0, 0], wq.cpu().numpy()[0, 0]
+    kk = np.diff(offs_h)
+    assert offs_h[0] == 0 and np.array_equal(kk, budget.allocate(wq_h, K, 0))
+    assert kk.sum() == K
+    assert kk.max() == 1 if total == "one" else (kk == T).all()
+    qn, kn, vn = (x[0, 0].double().numpy() for x in (q, k, v))
+    st = pisa.block_stats(kn, vn, 64)
+    ref_lists, score = budget.route_ragged(qn, st["kbar"], st["M"], kk, w.lam, w.scale, 64)
+    _check_lists([idx_h[offs_h[i]:offs_h[i + 1]] for i in range(T)], ref_lists, score)
+    idx_or = torch.zeros_like(idx.cpu())
+    for i in range(T):
+        idx_or[0, 0, offs_h[i]:offs_h[i + 1]] = torch.from_numpy(ref_lists[i].astype(np.int32))
+    o = paro.attention_csr(qd, kd, vd, *stats[:3], offsets, idx_or.cuda(), K).float().cpu().numpy()[0, 0]
+    oref = pisa.attention(qn, kn, vn, st, ref_lists, w.scale, 64)
+    mx, mean = check_attention(o, oref, w.dtype)
+    log(f"[budget] extremes {total}: k_i {kk.min()}..{kk.max()}, attention max {mx:.3g} mean {mean:.3g}")
+    if total == "all":
+        dense = pisa.dense_attention(qn, kn, vn, w.scale)
+        assert np.abs(o - dense).max() < 1e-5
