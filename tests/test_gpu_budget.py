@@ -143,7 +143,9 @@ def test_budget_with_strongly_varying_need(per_row):
 def test_csr_attention_on_random_ragged_lists(dtype):
     """Hand-made lists: every row a random count in [0, T] (0 and T included)
     of random distinct blocks, neighbouring rows of one workgroup very
-    different, a head stride larger than the total."""
+    different, a head stride larger than the total; in all three tail modes
+    (in keep-or-drop mode a row with an empty list has nothing to normalise,
+    0 / 0, so those rows are left out)."""
     from workloads import random_uniform_inputs
     B, H, L, d = 2, 1, 64 * 21 - 30, 64
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -167,13 +169,19 @@ def test_csr_attention_on_random_ragged_lists(dtype):
                 pos += len(sel)
             offsets[b, h, T] = pos
     (qd, kd, vd), stats, _ = run_gpu(q, k, v, 1, 0.1)
-    o = paro.attention_csr(qd, kd, vd, *stats[:3], offsets.cuda(), idx.cuda(), stride).float().cpu().numpy()
     qn, kn, vn = (x.double().numpy() for x in (q, k, v))
-    for b in range(B):
-        for h in range(H):
-            st = pisa.block_stats(kn[b, h], vn[b, h], 64)
-            ref = pisa.attention(qn[b, h], kn[b, h], vn[b, h], st, [lists[(b, h, i)] for i in range(T)], scale, 64)
-            check_attention(o[b, h], ref, dtype)
+    for mode, kw, okw in (("pisa", {}, {}), ("zeroth", {"first_order": False}, {"first_order": "none"}),
+                          ("drop", {"drop_tail": True}, {"tail": False})):
+        o = paro.attention_csr(qd, kd, vd, *stats[:3], offsets.cuda(), idx.cuda(), stride, **kw).float().cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                st = pisa.block_stats(kn[b, h], vn[b, h], 64)
+                rl = [lists[(b, h, i)] for i in range(T)]
+                keep = [i for i in range(T) if mode != "drop" or len(rl[i]) > 0]
+                ref = pisa.attention(qn[b, h], kn[b, h], vn[b, h], st, rl, scale, 64, qblocks=keep, **okw)
+                rows = [r for i in keep for r in range(64 * i, min(64 * i + 64, L))]
+                check_attention(o[b, h, rows], np.concatenate([ref[i] for i in keep]), dtype)
+        log(f"[budget] csr random lists {dtype} {mode}: ok")
 
 
 @pytest.mark.parametrize("total", ["one", "all"])

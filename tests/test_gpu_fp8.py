@@ -72,14 +72,15 @@ def test_fp8_video720p_sampled():
     dict(L=64 * 9 - 17, d=64, keep=3, H=3, B=1),    # d = 64, ragged tail
     dict(L=64 * 40 + 1, d=128, keep=5, H=2, B=2),   # last block of one token
 ])
-@pytest.mark.parametrize("drop", [False, True])
-def test_fp8_edge_shapes(case, drop):
+@pytest.mark.parametrize("mode", ["pisa", "zeroth", "drop"])
+def test_fp8_edge_shapes(case, mode):
     B, H, L, d, keep = case["B"], case["H"], case["L"], case["d"], case["keep"]
+    drop = mode == "drop"
     if drop and keep == 0:
         pytest.skip("no exact block and the tail dropped: every output is 0/0 (NaN) by definition")
     q, k, v = random_uniform_inputs(B, H, L, d, dtype=torch.bfloat16, seed=L + d, scale=0.8)
     scale = 1 / np.sqrt(d)
-    log(f"[fp8] edge {case} drop={drop}")
+    log(f"[fp8] edge {case} mode={mode}")
     (qd, kd, vd), stats, idx = run_gpu(q, k, v, keep, 0.1)
     qn, kn, vn = (x.double().numpy() for x in (q, k, v))
     idx_or = torch.empty_like(idx.cpu())
@@ -90,12 +91,14 @@ def test_fp8_edge_shapes(case, drop):
             ir, _ = pisa.route(qn[b, h], st["kbar"], st["M"], keep, 0.1, scale, 64)
             idx_or[b, h] = torch.from_numpy(ir.astype(np.int32))
             refs[(b, h)] = (st, ir)
-    o = paro.attention(qd, kd, vd, *stats[:3], idx_or.cuda(), keep, drop_tail=drop, qk_fp8=True)
+    o = paro.attention(qd, kd, vd, *stats[:3], idx_or.cuda(), keep, drop_tail=drop,
+                       first_order=mode != "zeroth", qk_fp8=True)
     o = o.float().cpu().numpy()
     kbar_gpu = stats[0].cpu().numpy()
     for (b, h), (st, ir) in refs.items():
         qq, kq, stq = fp8_operands(q[b, h], k[b, h], kbar_gpu[b, h], st, scale)
-        oref = pisa.attention(qq, kq, vn[b, h], stq, ir, scale, 64, tail=not drop)
+        oref = pisa.attention(qq, kq, vn[b, h], stq, ir, scale, 64, tail=not drop,
+                              first_order="none" if mode == "zeroth" else "global")
         mx, mean = check_attention(o[b, h], oref, "bf16")
         log(f"[fp8] edge b{b}h{h} vs the oracle on e4m3 operands: max {mx:.3g} mean {mean:.3g}")
 
