@@ -394,7 +394,9 @@ hipError_t launch_mode(const paro_problem& p, const void* Q, const float* kbar, 
 
 // Budget sharing for one head (one workgroup): k_i = k_min + floor(R wq_i / S)
 // plus one for the R - sum(floors) rows of largest remainder R wq_i mod S
-// (ties to the lower i), capped at T; then the CSR offsets (exclusive sums).
+// (ties to the lower i), where rows whose floor share reaches T - k_min are
+// first set to T and R, S are re-formed over the others until none does
+// (the total stays k_total); then the CSR offsets (exclusive sums).
 // The leftover rows are found as the keys (remainder << 20 | 2^20 - 1 - i),
 // all distinct, that are at least the left-th largest one, by a bitwise
 // search with block-wide counts.
