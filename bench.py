@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-exact-phase", action="store_true",
                     help="skip the all-exact control run that isolates the exact phase")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 480p and long-video steps (the other shapes of the metric)")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the error-against-dense table of the method and its ablations")
     ap.add_argument("--cpu-qblocks", type=int, default=48, help="query blocks per head in the oracle sample")
@@ -231,6 +233,54 @@ def budget_entry(w, qd, kd, vd, stats, out, reps: int = 3):
     kk = torch.diff(offsets.to(torch.int64), dim=-1)
     return {"k_total_per_head": K, "k_min": 1, "route_ms": round(route_ms, 4), "attention_ms": round(attn_ms, 4),
             "k_i_min": int(kk.min()), "k_i_max": int(kk.max())}
+
+
+def configs_entry(names=("video480p_32760", "video_long_118800"), steps: int = 5):
+    """The other DiT shapes the metric spans (32k and 119k tokens), timed like
+    the headline step: precompute + route + attention on one stream, inputs
+    resident, HIP events around each step after two warm-up steps."""
+    import torch
+    from block_sparse_attention_pisa_amd import paro
+    from workloads import WORKLOADS, make_inputs
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name in names:
+        w = WORKLOADS[name]
+        q, k, v = make_inputs(w)
+        qd, kd, vd = (x.cuda() for x in (q, k, v))
+        del q, k, v
+        stats = paro.alloc_stats(kd)
+        idx = torch.empty(w.B, w.H, w.T, w.k, dtype=torch.int32, device="cuda")
+        o = torch.empty_like(qd)
+        ws = torch.empty(max(16, paro.attention_workspace_bytes(paro.problem(qd))), dtype=torch.uint8, device="cuda")
+
+        def step(ev=None):
+            if ev:
+                ev[0].record(stream)
+            paro.precompute(kd, vd, out=stats)
+            paro.route(qd, stats[0], stats[3], w.k, w.lam, out=idx)
+            if ev:
+                ev[1].record(stream)
+            paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, w.k, out=o, workspace=ws)
+            if ev:
+                ev[2].record(stream)
+
+        for _ in range(2):
+            step()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for e in evs:
+            step(e)
+        torch.cuda.synchronize()
+        ms = sorted(e[0].elapsed_time(e[2]) for e in evs)[steps // 2]
+        att = sorted(e[1].elapsed_time(e[2]) for e in evs)[steps // 2]
+        flops = attention_flops(w, idx.cpu().numpy())
+        out[name] = {"L": w.L, "H": w.H, "keep_k": w.k, "T": w.T, "median_ms_per_step": round(ms, 4),
+                     "dense_equiv_TFLOPs": round(4.0 * w.B * w.H * w.L * w.L * w.d / (ms * 1e-3) / 1e12, 1),
+                     "attention_ms": round(att, 4),
+                     "attention_frac_of_bf16_peak": round(flops / (att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del qd, kd, vd, stats, idx, o, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def ablation_entry(name: str = "video480p_32760", permille=(50, 100, 125, 250, 500), tile=(2, 4, 8)):
@@ -483,6 +533,8 @@ def main():
         res["exact_phase"] = exact_phase_entry()
     if not a.no_ablation:
         res["ablation"] = ablation_entry()
+    if not a.no_configs:
+        res["other_configs"] = configs_entry()
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, a.cpu_qblocks, a.cpu_heads)
     print(json.dumps(res), flush=True)
