@@ -74,14 +74,17 @@ __device__ __forceinline__ uint32_t half16(const uint4& v, int e) {
 template <int D>
 __device__ __forceinline__ void load_item(const uint16_t* __restrict__ src, int row0, int nvalid, int item,
                                           uint4 (&r)[4]) {
+  // a buffer descriptor over the valid rows only: rows past nvalid read as
+  // zeros, with no per-row select (so the loads stay unconditional and the
+  // compiler can count them across loop iterations)
   const int tg = item % 16, dg = item / 16;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(src + static_cast<size_t>(row0) * D), static_cast<short>(0),
+      static_cast<int>(nvalid * D * 2), 0x00020000);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int tok = 4 * tg + q;
-    const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row0 + min(tok, nvalid - 1)) * D +
-                                                     8 * dg);
-    r[q] = tok < nvalid ? v : make_uint4(0, 0, 0, 0);
-  }
+  for (int q = 0; q < 4; ++q)
+    r[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rs, static_cast<uint32_t>(((4 * tg + q) * D + 8 * dg) * 2), 0, 0));
 }
 __device__ __forceinline__ void store_item(uint16_t (*dst)[kLdT], int item, const uint4 (&r)[4]) {
   const int tg = item % 16, dg = item / 16;
@@ -203,7 +206,7 @@ __device__ __forceinline__ void subtract_rank1(const TileLds<E, D>& s, HAcc<D>& 
 // thread) while the current block is reduced, and the column sums come from
 // those registers; only LDS barriers separate the steps.
 template <typename E, int D>
-__global__ __launch_bounds__(kThreads) void k_block_stats(const E* __restrict__ K, const E* __restrict__ V,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_block_stats(const E* __restrict__ K, const E* __restrict__ V,
                                                           float* __restrict__ kbar, float* __restrict__ vsum,
                                                           float* __restrict__ ws, int L, int T, int G, int nchunk) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -221,12 +224,20 @@ __global__ __launch_bounds__(kThreads) void k_block_stats(const E* __restrict__ 
     static_assert(2 * D <= kThreads, "one staging item per thread");
     const int item = threadIdx.x;
     const bool has_item = item < 2 * D;
-    uint4 rk[4], rv[4];
+    // two blocks in flight: block j is staged from one register set while
+    // the loads of block j + 1 are outstanding in the other; after staging,
+    // the set is refilled with block j + 2 (the loop is unrolled by two so
+    // that both sets stay in registers)
+    uint4 rkA[4], rvA[4], rkB[4], rvB[4];
+    auto fetch = [&](int j, uint4 (&rk)[4], uint4 (&rv)[4]) {
+      load_item<D>(Kh, j * kBlock, min(kBlock, L - j * kBlock), item, rk);
+      load_item<D>(Vh, j * kBlock, min(kBlock, L - j * kBlock), item, rv);
+    };
     if (has_item) {
-      load_item<D>(Kh, j0 * kBlock, min(kBlock, L - j0 * kBlock), item, rk);
-      load_item<D>(Vh, j0 * kBlock, min(kBlock, L - j0 * kBlock), item, rv);
+      fetch(j0, rkA, rvA);
+      if (j0 + 1 < j1) fetch(j0 + 1, rkB, rvB);
     }
-    for (int j = j0; j < j1; ++j) {
+    auto body = [&](int j, uint4 (&rk)[4], uint4 (&rv)[4]) {
       const int row0 = j * kBlock, nvalid = min(kBlock, L - row0);
       lds_barrier();  // the previous block's tiles have been consumed
       if (has_item) {
@@ -250,15 +261,15 @@ __global__ __launch_bounds__(kThreads) void k_block_stats(const E* __restrict__ 
           *reinterpret_cast<f32x4*>(vsum + o) = f32x4{vs[0], vs[1], vs[2], vs[3]};
           *reinterpret_cast<f32x4*>(vsum + o + 4) = f32x4{vs[4], vs[5], vs[6], vs[7]};
         }
-        if (j + 1 < j1) {
-          const int nr0 = row0 + kBlock, nv = min(kBlock, L - nr0);
-          load_item<D>(Kh, nr0, nv, item, rk);
-          load_item<D>(Vh, nr0, nv, item, rv);
-        }
+        if (j + 2 < j1) fetch(j + 2, rk, rv);
       }
       lds_barrier();
       accumulate_ktv<D>(s, acc);
       subtract_rank1(s, acc);
+    };
+    for (int j = j0; j < j1; j += 2) {
+      body(j, rkA, rvA);
+      if (j + 1 < j1) body(j + 1, rkB, rvB);
     }
   } else {
     for (int j = j0; j < j1; ++j) {
