@@ -20,6 +20,7 @@ int check_problem(const paro_problem* p) {
   const int64_t T = (static_cast<int64_t>(p->L) + p->block - 1) / p->block;
   if (T > PARO_MAX_BLOCKS) return PARO_ERR_SHAPE;
   if (T * p->B * p->H > INT32_MAX) return PARO_ERR_SHAPE;
+  if (static_cast<int64_t>(p->B) * p->H * p->L * p->d > INT32_MAX) return PARO_ERR_SHAPE;
   if (!std::isfinite(p->scale) || !(p->scale > 0.0)) return PARO_ERR_ARG;
   return PARO_OK;
 }

@@ -23,12 +23,15 @@
 //  * O^T += V^T P^T with P straight from the S^T accumulators (K rows are read
 //    in a permuted order so each lane's 8 consecutive P values are 8
 //    consecutive keys, the 8 keys its V^T operand holds).
-//  * The softmax reference m is fixed by the first tile a wave sees and never
-//    moves, so O needs no rescaling: N and D share the factor exp(-m), which
-//    cancels in N / D. A tile whose weight sum reaches 2^64 (some logit at
-//    least 64 log2 units above m, far beyond real attention logits) marks
-//    the wave, and after the pass the marked waves recompute their rows with
-//    m set to the exact maximum, found by a max-only pass.
+//  * The softmax reference m is fixed by the first tile a wave sees (the
+//    largest logit of centroid chunk 0 among the blocks that carry weight)
+//    and never moves, so O needs no rescaling: N and D share the factor
+//    exp(-m), which cancels in N / D. A tile whose weight sum reaches 2^64
+//    (some logit at least 64 log2 units above m, far beyond real attention
+//    logits) marks the wave, and so does a row whose D ends below 2^-64
+//    (every weighted logit far below m); after the pass the marked waves
+//    recompute their rows with m set to the exact maximum, found by a
+//    max-only pass.
 //  * Stage 2 streams all T centroids in chunks of 64 through the same staging
 //    and the same pipelined tile code as the exact tiles (kbar as keys, vsum
 //    as values, rounded to bf16 by a small kernel into a caller workspace),
@@ -869,7 +872,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
             mx = fmaxf(mx, fmaxf(half_max_masked(s0, static_cast<uint32_t>(km)),
                                  half_max_masked(s1, static_cast<uint32_t>(km >> 32))));
           }
-        } else if (active) {
+        } else if (active && nch > 0) {
+          // (centroids count only where some carry weight: with no tail
+          // chunk 0 is staged for the reference alone)
           const uint64_t km = past_T(step == 0 ? 0 : step - nu);
           const f32x16 s0 = s_half(bc, 0);
           const f32x16 s1 = s_half(bc, 1);
@@ -879,7 +884,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
         advance(step);
       }
       if (active) {
-        set_reference(a, a.m + mx);  // mx is relative to the current reference
+        // mx is relative to the current reference; a row with nothing to
+        // weigh (keep-or-drop with an empty S_i: 0 / 0 by definition) keeps it
+        if (mx > -INFINITY) set_reference(a, a.m + mx);
 #pragma unroll
         for (int u = 0; u < Geo<D>::NU; ++u) a.o[u] = f32x16{};
         a.dsum = 0.f;
@@ -897,12 +904,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
         float shift = 0.f;
         if (pass == 0) {
           // reference: the largest centroid logit of the chunk (computed with
-          // the reference 0); a centroid logit is the mean of its block's key
-          // logits, so the reference never exceeds the largest logit that
-          // carries weight
-          const uint64_t km = past_T(0);
-          const float v = fmaxf(half_max_masked(s0, static_cast<uint32_t>(km)),
-                                half_max_masked(s1, static_cast<uint32_t>(km >> 32)));
+          // the reference 0) over the blocks that carry weight: every block
+          // below T when the tail is on, only the blocks of S_i when it is
+          // not. A centroid logit is the mean of its block's key logits, so
+          // the reference never exceeds the largest logit that carries
+          // weight. With no such block in the chunk the reference stays 0;
+          // a row whose weights then all underflow is caught after the pass.
+          const uint64_t km = nch > 0 ? past_T(0) : ~(chunk_mask(0) & ~past_T(0));
+          float v = fmaxf(half_max_masked(s0, static_cast<uint32_t>(km)),
+                          half_max_masked(s1, static_cast<uint32_t>(km >> 32)));
+          if (!(v > -INFINITY)) v = 0.f;
           set_reference(a, v);
           shift = -v;
         }
@@ -957,7 +968,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       lds_barrier();
     }
 
-    // ---- rerun the rows whose logits outgrew their reference max
+    // ---- rerun the rows whose logits outgrew their reference max, and the
+    // rows whose weights all fell below 2^-64 of it (D would lose its
+    // precision or underflow to 0)
+    if (pass == 0 && active) {
+      const float drow = a.dsum + __shfl_xor(a.dsum, 32);
+      a.over = a.over || !(drow >= 0x1p-64f);
+    }
     const bool mine = active && __any(a.over);
     if (l == 0) sh[1 + w] = mine ? 1 : 0;
     lds_barrier();

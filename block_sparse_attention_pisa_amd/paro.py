@@ -143,6 +143,42 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
     return t.data_ptr()
 
 
+def _shape(t: torch.Tensor, name: str, shape, ref: torch.Tensor | None = None) -> None:
+    """Shape (and device) check done before any call into the library: the C
+    ABI receives bare pointers and cannot check buffer sizes itself."""
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
+    if ref is not None and t.device != ref.device:
+        raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _bytes_at_least(t: torch.Tensor, name: str, need: int) -> int:
+    n = t.numel() * t.element_size()
+    if n < need:
+        raise ValueError(f"{name} holds {n} bytes, the call needs {need}")
+    return n
+
+
+def _dims(q: torch.Tensor):
+    """(B, H, L, d, T) of a [B, H, L, d] tensor."""
+    if q.dim() != 4:
+        raise ValueError(f"expected a [B, H, L, d] tensor, got shape {tuple(q.shape)}")
+    B, H, L, d = q.shape
+    return B, H, L, d, -(-L // BLOCK)
+
+
+def _stats_shapes(ref: torch.Tensor, kbar, vsum, Hbar, M) -> None:
+    B, H, L, d, T = _dims(ref)
+    if kbar is not None:
+        _shape(kbar, "kbar", (B, H, T, d), ref)
+    if vsum is not None:
+        _shape(vsum, "vsum", (B, H, T, d), ref)
+    if Hbar is not None:
+        _shape(Hbar, "Hbar", (B, H, d, d), ref)
+    if M is not None:
+        _shape(M, "M", (B, H, T), ref)
+
+
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
@@ -173,6 +209,9 @@ def precompute(k: torch.Tensor, v: torch.Tensor, out=None, scale: float | None =
     """Block statistics (kbar, vsum, Hbar, M) of [B, H, L, d] keys and values."""
     p = problem(k, scale)
     kbar, vsum, Hbar, M, ws = alloc_stats(k) if out is None else out
+    _shape(v, "v", k.shape, k)
+    _stats_shapes(k, kbar, vsum, Hbar, M)
+    _bytes_at_least(ws, "workspace", workspace_bytes(p))
     _check(lib().paro_precompute(
         ctypes.byref(p), _dev(k, "k"), _dev(v, "v", k.dtype), _dev(kbar, "kbar", torch.float32),
         _dev(vsum, "vsum", torch.float32), _dev(Hbar, "Hbar", torch.float32),
@@ -185,9 +224,12 @@ def route(q: torch.Tensor, kbar: torch.Tensor, M: torch.Tensor, keep_k: int, lam
           scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
     """Top-keep_k kv-block indices [B, H, T, keep_k] (int32, ascending per row)."""
     p = problem(q, scale)
-    B, H, L, d = q.shape
-    T = -(-L // BLOCK)
+    B, H, L, d, T = _dims(q)
+    if not 0 <= keep_k <= T:
+        raise ValueError(f"keep_k must be in [0, {T}], got {keep_k}")
+    _stats_shapes(q, kbar, None, None, M)
     idx = torch.empty(B, H, T, keep_k, dtype=torch.int32, device=q.device) if out is None else out
+    _shape(idx, "idx", (B, H, T, keep_k), q)
     ptr = _dev(idx, "idx", torch.int32) if keep_k > 0 else None
     _check(lib().paro_route(ctypes.byref(p), _dev(q, "q"), _dev(kbar, "kbar", torch.float32),
                             _dev(M, "M", torch.float64), int(keep_k), float(lam), ptr, _stream()),
@@ -232,13 +274,23 @@ def attention(q, k, v, kbar, vsum, Hbar, idx, keep_k: int, scale: float | None =
     here when not given). qk_fp8=True (bf16 only) takes the key-query
     products on the fp8 matrix cores (paro_attention_fp8)."""
     p = problem(q, scale)
+    B, H, L, d, T = _dims(q)
+    if not 0 <= keep_k <= T:
+        raise ValueError(f"keep_k must be in [0, {T}], got {keep_k}")
+    _shape(k, "k", q.shape, q)
+    _shape(v, "v", q.shape, q)
+    _stats_shapes(q, kbar, vsum, Hbar, None)
+    if keep_k > 0:
+        _shape(idx, "idx", (B, H, T, keep_k), q)
     o = torch.empty_like(q) if out is None else out
-    ptr = _dev(idx, "idx", torch.int32) if keep_k > 0 else None
+    _shape(o, "out", q.shape, q)
     mode = TAIL_DROP if drop_tail else (TAIL_PISA if first_order else TAIL_ZEROTH)
     if qk_fp8:
         nws = attention_fp8_workspace_bytes(p)
         if workspace is None:
             workspace = torch.empty(max(16, nws), dtype=torch.uint8, device=q.device)
+        _bytes_at_least(workspace, "workspace", nws)
+        ptr = _dev(idx, "idx", torch.int32) if keep_k > 0 else None
         _check(lib().paro_attention_fp8(
             ctypes.byref(p), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
             _dev(kbar, "kbar", torch.float32), _dev(vsum, "vsum", torch.float32),
@@ -249,8 +301,9 @@ def attention(q, k, v, kbar, vsum, Hbar, idx, keep_k: int, scale: float | None =
     nws = attention_workspace_bytes(p)
     if nws > 0 and workspace is None:
         workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    wbytes = _bytes_at_least(workspace, "workspace", nws) if workspace is not None else 0
     wptr = _dev(workspace, "workspace") if nws > 0 else None
-    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ptr = _dev(idx, "idx", torch.int32) if keep_k > 0 else None
     _check(lib().paro_attention_mode(
         ctypes.byref(p), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
         _dev(kbar, "kbar", torch.float32), _dev(vsum, "vsum", torch.float32),
@@ -259,21 +312,33 @@ def attention(q, k, v, kbar, vsum, Hbar, idx, keep_k: int, scale: float | None =
     return o
 
 
-def route_budget(q, kbar, M, k_total: int, k_min: int = 1, lam: float = 0.1, scale: float | None = None):
+def route_budget(q, kbar, M, k_total: int, k_min: int = 1, lam: float = 0.1, scale: float | None = None,
+                 out=None):
     """Per-query-block budgets: returns (offsets [B, H, T + 1] int32, idx [B, H, k_total] int32,
-    weights [B, H, T] int64 = w * 2^16). Row i of head h is idx[h][offsets[h][i]:offsets[h][i + 1]]."""
+    weights [B, H, T] int64 = w * 2^16). Row i of head h is idx[h][offsets[h][i]:offsets[h][i + 1]].
+    out: optional (offsets, idx, weights, workspace) buffers of those shapes (and at least
+    paro_route_budget_workspace_bytes bytes of workspace)."""
     p = problem(q, scale)
-    B, H, L, d = q.shape
-    T = -(-L // BLOCK)
-    offsets = torch.empty(B, H, T + 1, dtype=torch.int32, device=q.device)
-    idx = torch.zeros(B, H, max(1, k_total), dtype=torch.int32, device=q.device)
-    wq = torch.empty(B, H, T, dtype=torch.int64, device=q.device)
-    ws = torch.empty(max(16, int(lib().paro_route_budget_workspace_bytes(ctypes.byref(p)))), dtype=torch.uint8,
-                     device=q.device)
+    B, H, L, d, T = _dims(q)
+    _stats_shapes(q, kbar, None, None, M)
+    nws = int(lib().paro_route_budget_workspace_bytes(ctypes.byref(p)))
+    if out is None:
+        offsets = torch.empty(B, H, T + 1, dtype=torch.int32, device=q.device)
+        idx = torch.zeros(B, H, max(1, k_total), dtype=torch.int32, device=q.device)
+        wq = torch.empty(B, H, T, dtype=torch.int64, device=q.device)
+        ws = torch.empty(max(16, nws), dtype=torch.uint8, device=q.device)
+    else:
+        offsets, idx, wq, ws = out
+    _shape(offsets, "offsets", (B, H, T + 1), q)
+    _shape(idx, "idx", (B, H, max(1, k_total)), q)
+    _shape(wq, "weights", (B, H, T), q)
+    _bytes_at_least(ws, "workspace", nws)
     _check(lib().paro_route_budget(ctypes.byref(p), _dev(q, "q"), _dev(kbar, "kbar", torch.float32),
-                                   _dev(M, "M", torch.float64), int(k_total), int(k_min), float(lam), _dev(wq, "wq"),
-                                   _dev(offsets, "offsets"), _dev(idx, "idx"), _dev(ws, "workspace"),
-                                   ws.numel(), _stream()), "paro_route_budget")
+                                   _dev(M, "M", torch.float64), int(k_total), int(k_min), float(lam),
+                                   _dev(wq, "weights", torch.int64),
+                                   _dev(offsets, "offsets", torch.int32), _dev(idx, "idx", torch.int32),
+                                   _dev(ws, "workspace"), ws.numel() * ws.element_size(), _stream()),
+           "paro_route_budget")
     return offsets, idx, wq
 
 
@@ -282,12 +347,21 @@ def attention_csr(q, k, v, kbar, vsum, Hbar, offsets, idx, k_stride: int, scale:
                   workspace: torch.Tensor | None = None) -> torch.Tensor:
     """paro_attention_csr: exact lists of any lengths (offsets [B, H, T + 1], idx [B, H, k_stride])."""
     p = problem(q, scale)
+    B, H, L, d, T = _dims(q)
+    _shape(k, "k", q.shape, q)
+    _shape(v, "v", q.shape, q)
+    _stats_shapes(q, kbar, vsum, Hbar, None)
+    _shape(offsets, "offsets", (B, H, T + 1), q)
+    if k_stride < 0:
+        raise ValueError(f"k_stride must be >= 0, got {k_stride}")
+    _shape(idx, "idx", (B, H, k_stride), q)
     o = torch.empty_like(q) if out is None else out
+    _shape(o, "out", q.shape, q)
     nws = attention_workspace_bytes(p)
     if nws > 0 and workspace is None:
         workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    wbytes = _bytes_at_least(workspace, "workspace", nws) if workspace is not None else 0
     wptr = _dev(workspace, "workspace") if nws > 0 else None
-    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     mode = TAIL_DROP if drop_tail else (TAIL_PISA if first_order else TAIL_ZEROTH)
     _check(lib().paro_attention_csr(
         ctypes.byref(p), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),

@@ -39,8 +39,8 @@
  *   is launched and no output is touched. The library never prints or aborts.
  *   NaN/Inf inputs are not detected.
  * - Supported: block == 64; d in {64, 128}; 1 <= B, H; B*H <= 65535; 1 <= L;
- *   B*H*L*d < 2^31;
- *   T <= PARO_MAX_BLOCKS.
+ *   B*H*L*d < 2^31 elements per tensor; T <= PARO_MAX_BLOCKS. Anything
+ *   else returns PARO_ERR_SHAPE.
  */
 #ifndef PARO_H_
 #define PARO_H_

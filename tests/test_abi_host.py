@@ -66,6 +66,7 @@ def test_workspace_bytes():
     (dict(d=96), -2), (dict(block=32), -2), (dict(L=0), -2), (dict(B=0), -2), (dict(H=-1), -2),
     (dict(dtype=7), -3), (dict(scale=0.0), -7), (dict(scale=float("nan")), -7),
     (dict(L=64 * 16384 + 1), -2), (dict(B=300, H=300), -2),
+    (dict(B=16, H=1, L=64 * 16384, d=128), -2),   # B*H*L*d = 2^31 elements: past the 32-bit bound
 ])
 def test_problem_validation(kw, code):
     L = paro.lib()
@@ -74,6 +75,21 @@ def test_problem_validation(kw, code):
     assert L.paro_precompute(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == code
     assert L.paro_route(ctypes.byref(p), FAKE, FAKE, FAKE, 2, 0.1, FAKE, None) == code
     assert L.paro_attention(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, ws, None) == code
+
+
+def test_element_count_bound():
+    """B*H*L*d must stay below 2^31: one element less per tensor passes the
+    shape checks (the call then stops at the workspace size, before any launch)."""
+    L = paro.lib()
+    big = _p(B=16, H=1, L=64 * 16384, d=128)
+    assert L.paro_precompute_workspace_bytes(ctypes.byref(big)) == 0
+    ok = _p(B=16, H=1, L=64 * 16384 - 1, d=128)
+    ws = L.paro_precompute_workspace_bytes(ctypes.byref(ok))
+    assert ws > 0
+    assert L.paro_precompute(ctypes.byref(ok), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == -5
+    assert L.paro_precompute(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == -2
+    assert L.paro_route(ctypes.byref(big), FAKE, FAKE, FAKE, 2, 0.1, FAKE, None) == -2
+    assert L.paro_reorder(ctypes.byref(big), ctypes.byref(_g(1, 1, 1, 1, 1, 1)), 0, FAKE, FAKE + 16, None) == -2
 
 
 def test_pointer_and_argument_validation():

@@ -93,3 +93,15 @@ def test_ragged_routing_with_constant_k_is_the_fixed_k_routing():
         if 0 < ks[i] < 10:
             rest = np.setdiff1d(np.arange(10), got[i])
             assert sc[i, got[i]].min() >= sc[i, rest].max()
+
+
+def test_quantise_weights_worked_values():
+    """wq = w 2^16 rounded to nearest, halves up (both sides of the sharing
+    read the weights as these integers): 1.5 -> 98304 exactly; quotients that
+    fall on a half go up (3 / 2^17 -> 1.5 -> 2, 1 / 2^17 -> 0.5 -> 1), just
+    below a half go down; a truncating or half-even rounding fails here."""
+    one = budget.WEIGHT_ONE
+    assert one == 65536
+    w = np.array([1.5, 3 / 2 ** 17, 1 / 2 ** 17, 5 / 2 ** 17, (2.5 - 2 ** -20) / one, 1.0, 72.0, (7 + 0.5) / one])
+    assert budget.quantise_weights(w).tolist() == [98304, 2, 1, 3, 2, 65536, 72 * 65536, 8]
+    assert budget.quantise_weights(np.array([0.25])).dtype == np.int64

@@ -9,9 +9,11 @@ rounding of q' and k (relative 2^-4 per factor). Two bars:
   * on the DiT workloads, against the exact fp64 oracle at the bf16 bar
     (max 1e-2, mean 1e-3), which the fp8 path meets there;
   * on every shape, against the fp64 oracle applied to the e4m3-rounded
-    operands (q' per query row, K and kbar per row, rounded exactly as the
-    kernel rounds them), i.e. the definition of what the fp8 path computes,
-    at the same bf16 bar. (Small iid inputs with a few dozen keys do not
+    operands (q' per query row, K and the oracle's own kbar per row, rounded
+    exactly as the kernel rounds them), i.e. the definition of what the fp8
+    path computes, at the same bf16 bar; on the DiT workloads that
+    definition must also sit within a tenth of the smallest gap between
+    PISA and dense, zeroth-order or keep-or-drop attention. (Small iid inputs with a few dozen keys do not
     average the e4m3 error out; against the exact oracle they miss the bf16
     bar by design.)
 Attention is always fed the oracle's routing.
@@ -24,7 +26,7 @@ from block_sparse_attention_pisa_amd import paro
 from oracle import pisa, quant
 from workloads import WORKLOADS, random_uniform_inputs
 
-from parity_util import check_attention, full_parity, log, run_gpu, sample_qblocks
+from parity_util import check_attention, fp8_operands, full_parity, log, run_gpu, sample_qblocks
 
 pytestmark = pytest.mark.gpu
 
@@ -61,7 +63,7 @@ def test_fp8_video480p_sampled():
 
 def test_fp8_video720p_sampled():
     w = WORKLOADS["video720p_75600"]
-    s = full_parity(w, heads=[(0, 0), (0, 39)], qblocks=lambda T: sample_qblocks(T, 12), diag=False, qk_fp8=True)
+    s = full_parity(w, heads=[(0, 0), (0, 20), (0, 39)], qblocks=lambda T: sample_qblocks(T, 48), qk_fp8=True)
     log("[fp8] 720p summary", s)
 
 
@@ -94,26 +96,12 @@ def test_fp8_edge_shapes(case, mode):
     o = paro.attention(qd, kd, vd, *stats[:3], idx_or.cuda(), keep, drop_tail=drop,
                        first_order=mode != "zeroth", qk_fp8=True)
     o = o.float().cpu().numpy()
-    kbar_gpu = stats[0].cpu().numpy()
     for (b, h), (st, ir) in refs.items():
-        qq, kq, stq = fp8_operands(q[b, h], k[b, h], kbar_gpu[b, h], st, scale)
+        qq, kq, stq = fp8_operands(q[b, h], k[b, h], st["kbar"], st, scale)
         oref = pisa.attention(qq, kq, vn[b, h], stq, ir, scale, 64, tail=not drop,
                               first_order="none" if mode == "zeroth" else "global")
         mx, mean = check_attention(o[b, h], oref, "bf16")
         log(f"[fp8] edge b{b}h{h} vs the oracle on e4m3 operands: max {mx:.3g} mean {mean:.3g}")
-
-
-def fp8_operands(q, k, kbar32, st, scale):
-    """The operands the fp8 path multiplies, as fp64: q' = bf16(q) * fp32(scale
-    log2 e) rounded per query row, returned divided back by that factor; K
-    rows and the (GPU, fp32) kbar rows rounded per row."""
-    cl2 = np.float32(scale * 1.4426950408889634)
-    x = q.float().numpy() * cl2
-    qq = quant.dequantize_rows(*quant.quantize_rows(x)) / np.float64(cl2)
-    kq = quant.dequantize_rows(*quant.quantize_rows(k.float().numpy()))
-    stq = dict(st)
-    stq["kbar"] = quant.dequantize_rows(*quant.quantize_rows(kbar32.astype(np.float32)))
-    return qq, kq, stq
 
 
 def test_fp8_rejects_fp32():

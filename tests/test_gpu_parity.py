@@ -37,13 +37,13 @@ def test_video480p_sampled():
 
 def test_video720p_sampled():
     w = WORKLOADS["video720p_75600"]
-    s = full_parity(w, heads=[(0, 0), (0, 39)], qblocks=lambda T: sample_qblocks(T, 12), diag=False)
+    s = full_parity(w, heads=[(0, 0), (0, 13), (0, 26), (0, 39)], qblocks=lambda T: sample_qblocks(T, 48))
     log("[parity] 720p summary", s)
 
 
 def test_video_long_sampled():
     w = WORKLOADS["video_long_118800"]
-    s = full_parity(w, heads=[(0, 23)], qblocks=lambda T: sample_qblocks(T, 8), diag=False)
+    s = full_parity(w, heads=[(0, 0), (0, 23)], qblocks=lambda T: sample_qblocks(T, 24))
     log("[parity] long summary", s)
 
 
@@ -274,3 +274,68 @@ def test_logit_jump_rerun_keeps_every_row_exact():
     ref = pisa.attention(qn, kn, vn, st, idx.astype(np.int64), 1 / np.sqrt(d), 64)
     assert np.isfinite(o).all()
     check_attention(o[0, 0], ref, "bf16")
+
+
+def _drop_mode_case(q, k, v, idx, fp8):
+    """GPU keep-or-drop attention (the tail dropped) on the given rows against
+    the oracle's tail=False mode; for the fp8 path the oracle runs on the
+    e4m3-rounded operands."""
+    from parity_util import fp8_operands
+    d = q.shape[-1]
+    scale = 1 / np.sqrt(d)
+    qt, kt, vt = (torch.from_numpy(x)[None, None].to(torch.bfloat16) for x in (q, k, v))
+    qd, kd, vd = (x.cuda() for x in (qt, kt, vt))
+    stats = paro.precompute(kd, vd)
+    keep = idx.shape[1]
+    o = paro.attention(qd, kd, vd, *stats[:3], torch.from_numpy(idx)[None, None].cuda(), keep, drop_tail=True,
+                       qk_fp8=fp8).float().cpu().numpy()[0, 0]
+    qn, kn, vn = (x[0, 0].double().numpy() for x in (qt, kt, vt))
+    st = pisa.block_stats(kn, vn, 64)
+    if fp8:
+        qn, kn, st = fp8_operands(qt[0, 0], kt[0, 0], st["kbar"], st, scale)
+    ref = pisa.attention(qn, kn, vn, st, idx.astype(np.int64), scale, 64, tail=False)
+    assert np.isfinite(o).all()
+    return check_attention(o, ref, "bf16")
+
+
+@pytest.mark.parametrize("jump", [1000.0, 2000.0])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_drop_mode_with_a_dropped_block_far_above_the_kept_ones(jump, fp8):
+    """Keep-or-drop: block 5's logits sit ~88 (jump 1000) or ~177 (jump 2000)
+    nats above every other block's, and the rows with S_i = {0, 1}, {2, 3} or
+    {0, 7} leave it out. The softmax reference must come from blocks that
+    carry weight only: taken over all centroids of the first chunk, every
+    weight of those rows would underflow (exp2 of about -127 or -255) and
+    D would be 0."""
+    d, nb = 128, 8
+    L = 64 * nb
+    g = np.random.default_rng(7)
+    e0 = np.zeros(d, dtype=np.float32)
+    e0[0] = 1.0
+    q = (0.1 * g.standard_normal((L, d)) + e0).astype(np.float32)
+    k = (0.5 * g.standard_normal((L, d))).astype(np.float32)
+    k[5 * 64:6 * 64] = jump * e0 + 0.5 * g.standard_normal((64, d))
+    v = g.standard_normal((L, d)).astype(np.float32)
+    idx = np.array([[0, 5], [0, 5], [0, 1], [0, 1], [0, 5], [2, 3], [1, 5], [0, 7]], dtype=np.int32)
+    mx, mean = _drop_mode_case(q, k, v, idx, fp8)
+    log(f"[parity] drop mode, jump {jump}, fp8 {fp8}: max {mx:.3g} mean {mean:.3g}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_drop_mode_with_all_logits_far_below_zero(fp8):
+    """Keep-or-drop with T = 66 blocks and every logit about -133 nats: rows
+    whose S_i has no block in the first centroid chunk (blocks 64 and 65, the
+    last one partial) start from the reference 0, so every weight underflows;
+    such a row must be caught (D below 2^-64) and recomputed with its exact
+    maximum. Rows with a block of the first chunk take their reference from it."""
+    d, nb = 128, 66
+    L = 64 * nb - 5
+    g = np.random.default_rng(9)
+    e0 = np.zeros(d, dtype=np.float32)
+    e0[0] = 1.0
+    q = (0.1 * g.standard_normal((L, d)) + e0).astype(np.float32)
+    k = (-1500.0 * e0 + 0.5 * g.standard_normal((L, d))).astype(np.float32)
+    v = g.standard_normal((L, d)).astype(np.float32)
+    idx = np.array([[64, 65] if i % 2 == 0 else [3, 64] for i in range(nb)], dtype=np.int32)
+    mx, mean = _drop_mode_case(q, k, v, idx, fp8)
+    log(f"[parity] drop mode, logits far below zero, fp8 {fp8}: max {mx:.3g} mean {mean:.3g}")

@@ -427,3 +427,76 @@ def test_keep_or_drop_mode_is_renormalised_sparse_attention():
         rows = slice(i * block, (i + 1) * block)
         ref = scipy.special.softmax(0.5 * q[rows] @ k[keys].T, axis=1) @ v[keys]
         assert np.abs(o[rows] - ref).max() < 1e-12
+
+
+def test_captured_mass_pins():
+    """captured_mass (share of the dense softmax mass on S_i, the coverage
+    measure of the vector-quantized attention review, Table 6) pinned three
+    ways: it is 1 when S_i holds every block; with equal logits the softmax is
+    uniform over the L keys, so the share is sum_{j in S_i} n_j / L (a partial
+    last block counts its valid keys only); and on random inputs it equals a
+    per-token loop of math.exp over every key."""
+    g = np.random.default_rng(12)
+    L, block, d = 64 * 5 + 23, 64, 8
+    T = -(-L // block)
+    q, k = g.standard_normal((L, d)), g.standard_normal((L, d))
+    scale = 1 / math.sqrt(d)
+    idx_all = np.tile(np.arange(T), (T, 1))
+    cm = pisa.captured_mass(q, k, idx_all, scale, block, range(T))
+    for i in range(T):
+        assert np.allclose(cm[i], 1.0, atol=1e-12)
+    # equal logits: q = 0 (every logit 0); the partial block 5 holds 23 keys
+    idx = np.array([[0, 5], [1, 2], [3, 5], [0, 4], [2, 3], [1, 5]])
+    cm = pisa.captured_mass(np.zeros((L, d)), k, idx, scale, block, range(T))
+    n = np.array([64, 64, 64, 64, 64, 23])
+    for i in range(T):
+        assert np.allclose(cm[i], n[idx[i]].sum() / L, atol=1e-13), i
+    # brute force on random inputs (a scale large enough for a peaked softmax)
+    cm = pisa.captured_mass(q, k, idx, 1.3, block, [0, 5])
+    for i in (0, 5):
+        s, e = i * block, min(i * block + block, L)
+        keep = set()
+        for j in idx[i]:
+            keep.update(range(j * block, min(j * block + block, L)))
+        for r, t in enumerate(range(s, e)):
+            ws = [math.exp(1.3 * float(q[t] @ k[u])) for u in range(L)]
+            want = sum(ws[u] for u in keep) / sum(ws)
+            assert abs(cm[i][r] - want) < 1e-12
+    # and it is what the exact part of PISA sees: the keep-or-drop output
+    # times the captured share equals the dense numerator's S_i part over D_dense
+    v = g.standard_normal((L, d))
+    st = pisa.block_stats(k, v, block)
+    od = pisa.attention(q, k, v, st, idx, scale, block, tail=False, qblocks=[2])[2]
+    cm = pisa.captured_mass(q, k, idx, scale, block, [2])[2]
+    s, e = 2 * block, 3 * block
+    lg = scale * q[s:e] @ k.T
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    mask = np.zeros(L, bool)
+    for j in idx[2]:
+        mask[j * block:min(j * block + block, L)] = True
+    want = (p[:, mask] @ v[mask]) / p.sum(axis=1, keepdims=True)
+    assert np.allclose(od * cm[:, None], want, atol=1e-12)
+
+
+def test_dense_attention_and_block_ranges():
+    """dense_attention (the reference of the dense control and of the
+    discriminating gates) is textbook softmax attention: equal to scipy's
+    softmax times V, row subsets included, and invariant to a logit shift of
+    1000 (max subtraction). block_ranges cuts L into ceil(L / block) blocks,
+    the last one partial."""
+    g = np.random.default_rng(3)
+    L, d = 150, 8
+    q, k, v = g.standard_normal((L, d)), g.standard_normal((L, d)), g.standard_normal((L, d))
+    ref = scipy.special.softmax(0.4 * q @ k.T, axis=1) @ v
+    assert np.abs(pisa.dense_attention(q, k, v, 0.4) - ref).max() < 1e-13
+    rows = [0, 7, 149]
+    assert np.abs(pisa.dense_attention(q, k, v, 0.4, rows=rows) - ref[rows]).max() < 1e-13
+    # a constant added to every logit of a row changes nothing
+    e = np.zeros(d)
+    e[0] = 1.0
+    qs = q + 1000.0 * e
+    ks = np.concatenate([k[:, :1] * 0 + 1.0, k[:, 1:]], axis=1)     # k_0 = 1 for every key
+    ref_s = scipy.special.softmax(0.4 * (q + 0 * e) @ ks.T, axis=1) @ v
+    assert np.abs(pisa.dense_attention(qs, ks, v, 0.4) - ref_s).max() < 1e-9
+    assert pisa.block_ranges(150, 64) == [(0, 64), (64, 128), (128, 150)]
+    assert pisa.block_ranges(64, 64) == [(0, 64)] and pisa.block_ranges(1, 64) == [(0, 1)]
