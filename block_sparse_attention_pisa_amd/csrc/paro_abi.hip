@@ -213,6 +213,24 @@ int paro_attention_mode(const paro_problem* p, const void* Q, const void* K, con
                                          static_cast<hipStream_t>(stream)));
 }
 
+int paro_attention_noalloc(const paro_problem* p, const void* Q, const void* K, const void* V, const float* kbar,
+                           const float* vsum, const float* Hbar, const int32_t* idx, int32_t keep_k, int32_t mode,
+                           void* O, void* stream) {
+  int rc = check_problem(p);
+  if (rc != PARO_OK) return rc;
+  const int T = num_blocks(p);
+  if (keep_k < 0 || keep_k > T) return PARO_ERR_SHAPE;
+  if (mode != PARO_TAIL_PISA && mode != PARO_TAIL_DROP && mode != PARO_TAIL_ZEROTH) return PARO_ERR_ARG;
+  if ((rc = check_ptrs({Q, K, V, kbar, vsum, Hbar, O})) != PARO_OK) return rc;
+  if (keep_k > 0 && (rc = check_ptrs({idx})) != PARO_OK) return rc;
+  const size_t need = paro::attention_workspace_bytes(*p);
+  if (need > PARO_NOALLOC_SCRATCH_BYTES) return PARO_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && (rc = from_hip(paro::attention_scratch(&ws))) != PARO_OK) return rc;
+  return from_hip(paro::launch_attention(*p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int paro_attention(const paro_problem* p, const void* Q, const void* K, const void* V, const float* kbar,
                    const float* vsum, const float* Hbar, const int32_t* idx, int32_t keep_k, void* O,
                    void* workspace, size_t workspace_bytes, void* stream) {

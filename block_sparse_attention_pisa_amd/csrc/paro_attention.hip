@@ -46,8 +46,15 @@
 // fp32 kernel (k_attn_f32): the same three stages in plain fp32 arithmetic,
 // one key at a time; used for fp32 problems.
 #include <algorithm>
+#include <mutex>
 
 #include "paro_common.h"
+
+// Device scratch of paro_attention_noalloc, for callers that cannot allocate:
+// it holds the bf16 copies of kbar and vsum that paro_attention otherwise
+// keeps in the caller's workspace. Every GPU the library runs on holds its
+// own copy until the process ends; calls on one GPU share it.
+static __device__ __align__(256) unsigned char scratch[PARO_NOALLOC_SCRATCH_BYTES];
 
 namespace paro {
 namespace {
@@ -1249,6 +1256,32 @@ hipError_t launch_attention_fp8(const paro_problem& p, const void* Q, const void
                                 int mode, void* ws, hipStream_t s) {
   return p.d == 128 ? launch_bf16<128, true>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s, nullptr)
                     : launch_bf16<64, true>(p, Q, K, V, kbar, vsum, Hbar, idx, keep_k, O, mode, ws, s, nullptr);
+}
+
+// Per-device address of the static attention scratch (see `scratch` below):
+// the host-side name of a __device__ array is only a stand-in, so kernels are
+// given the address the runtime reports for the current device, looked up
+// once per device.
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+hipError_t attention_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attention(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,

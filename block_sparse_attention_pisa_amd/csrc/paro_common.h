@@ -114,6 +114,9 @@ hipError_t launch_attention(const paro_problem& p, const void* Q, const void* K,
                             int keep_k, void* O, int mode, void* ws, hipStream_t s,
                             const int32_t* offs = nullptr);
 size_t attention_workspace_bytes(const paro_problem& p);
+// Address of this device's static attention scratch (PARO_NOALLOC_SCRATCH_BYTES
+// bytes), looked up with hipGetSymbolAddress on the first call per device.
+hipError_t attention_scratch(void** out);
 hipError_t launch_attention_fp8(const paro_problem& p, const void* Q, const void* K, const void* V,
                                 const float* kbar, const float* vsum, const float* Hbar, const int32_t* idx,
                                 int keep_k, void* O, int mode, void* ws, hipStream_t s);

@@ -31,7 +31,9 @@ EXPORTED = (
     "paro_attention_fp8_workspace_bytes", "paro_fp8_rows", "paro_route_budget",
     "paro_route_budget_workspace_bytes", "paro_attention_csr", "paro_reorder",
     "paro_reorder_source", "paro_num_blocks", "paro_status_string", "paro_version",
+    "paro_attention_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PARO_NOALLOC_SCRATCH_BYTES
 REORDER_GATHER = 0
 REORDER_SCATTER = 1
 
@@ -82,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.paro_attention.restype = ctypes.c_int
         L.paro_attention_mode.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
         L.paro_attention_mode.restype = ctypes.c_int
+        L.paro_attention_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp]
+        L.paro_attention_noalloc.restype = ctypes.c_int
         L.paro_attention_workspace_bytes.argtypes = [pp]
         L.paro_attention_workspace_bytes.restype = sz
         L.paro_attention_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
@@ -310,6 +314,32 @@ def attention(q, k, v, kbar, vsum, Hbar, idx, keep_k: int, scale: float | None =
         _dev(Hbar, "Hbar", torch.float32), ptr, int(keep_k), mode,
         _dev(o, "o", q.dtype), wptr, wbytes, _stream()), "paro_attention_mode")
     return o
+
+
+def attention_noalloc(q, k, v, kbar, vsum, Hbar, idx, keep_k: int, out: torch.Tensor, scale: float | None = None,
+                      drop_tail: bool = False, first_order: bool = True) -> torch.Tensor:
+    """paro_attention_noalloc: the attention with its workspace in the
+    library's static device scratch (nothing allocated by the library or
+    here: the caller passes `out`). Calls that overlap on one GPU race on
+    that scratch."""
+    p = problem(q, scale)
+    B, H, L, d, T = _dims(q)
+    if not 0 <= keep_k <= T:
+        raise ValueError(f"keep_k must be in [0, {T}], got {keep_k}")
+    _shape(k, "k", q.shape, q)
+    _shape(v, "v", q.shape, q)
+    _stats_shapes(q, kbar, vsum, Hbar, None)
+    if keep_k > 0:
+        _shape(idx, "idx", (B, H, T, keep_k), q)
+    _shape(out, "out", q.shape, q)
+    mode = TAIL_DROP if drop_tail else (TAIL_PISA if first_order else TAIL_ZEROTH)
+    ptr = _dev(idx, "idx", torch.int32) if keep_k > 0 else None
+    _check(lib().paro_attention_noalloc(
+        ctypes.byref(p), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+        _dev(kbar, "kbar", torch.float32), _dev(vsum, "vsum", torch.float32),
+        _dev(Hbar, "Hbar", torch.float32), ptr, int(keep_k), mode, _dev(out, "out", q.dtype), _stream()),
+        "paro_attention_noalloc")
+    return out
 
 
 def route_budget(q, kbar, M, k_total: int, k_min: int = 1, lam: float = 0.1, scale: float | None = None,

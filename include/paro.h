@@ -175,6 +175,32 @@ int paro_attention_mode(const paro_problem* p, const void* Q, const void* K, con
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paro_attention_noalloc - paro_attention_mode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the workspace of paro_attention_mode
+ * (the bf16 copies of kbar and vsum) lives in a static device array of
+ * PARO_NOALLOC_SCRATCH_BYTES bytes inside the library instead of a caller
+ * buffer. Nothing is allocated or freed by the call.
+ *   - Same arguments, results and errors as paro_attention_mode, minus the
+ *     workspace. A problem whose paro_attention_workspace_bytes() exceeds
+ *     PARO_NOALLOC_SCRATCH_BYTES returns PARO_ERR_WORKSPACE (the 720p video
+ *     shape, B*H = 40, T = 1182, d = 128, needs 24.2 MB; fp32 problems need
+ *     none).
+ *   - The array of the current device is used (hipGetDevice); `stream` must
+ *     belong to that device. Its address is looked up once per device on the
+ *     first call (a failure there returns PARO_ERR_HIP).
+ *   - Every GPU holds its own array until the process ends, and every call
+ *     on one GPU shares it: calls that overlap on one GPU (on different
+ *     streams, or from several threads without ordering) race and give
+ *     undefined results. Calls ordered on one stream are safe; each call
+ *     overwrites what it reads before reading it.
+ */
+#define PARO_NOALLOC_SCRATCH_BYTES (32u << 20)
+int paro_attention_noalloc(const paro_problem* p, const void* Q, const void* K, const void* V,
+                           const float* kbar, const float* vsum, const float* Hbar,
+                           const int32_t* idx, int32_t keep_k, int32_t mode, void* O, void* stream);
+
+/*
  * Geometric token reordering before blocking ("PAROAttention: Pattern-Aware
  * ReOrdering for Efficient Sparse and Quantized Attention in Visual
  * Generation Models", abstract: visual tokens are reordered so that their

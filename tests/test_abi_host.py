@@ -215,3 +215,23 @@ def test_budget_entry_points_validation():
     assert ac(-1) == -2
     assert ac(10, mode=3) == -7
     assert ac(10, offs=None) == -1
+
+
+def test_noalloc_validation():
+    """paro_attention_noalloc validates like paro_attention_mode and refuses a
+    problem whose workspace would not fit its static scratch, before any HIP call."""
+    L = paro.lib()
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    p = _p()
+    T = L.paro_num_blocks(1000, 64)
+    na = lambda pr, keep=2, mode=0, o=FAKE: L.paro_attention_noalloc(ctypes.byref(pr), *args, keep, mode, o, None)
+    assert na(p, keep=T + 1) == -2
+    assert na(p, mode=3) == -7
+    assert na(p, o=None) == -1
+    assert na(p, o=FAKE + 4) == -4
+    assert na(_p(d=96)) == -2
+    big = _p(B=1, H=60, L=64 * 1100)        # 2 * 60 * 1100 * 128 * 2 bytes > 32 MiB
+    assert L.paro_attention_workspace_bytes(ctypes.byref(big)) > paro.NOALLOC_SCRATCH_BYTES
+    assert na(big) == -5
+    fits = _p(B=1, H=40, L=75600)           # the 720p video shape: 24.2 MB
+    assert L.paro_attention_workspace_bytes(ctypes.byref(fits)) <= paro.NOALLOC_SCRATCH_BYTES
