@@ -23,6 +23,13 @@ the kv-blocks exact). Prints one JSON line:
                 [B, H, L, d] tensor into the tiled order and back, against
                 the HBM peak (one read and one write of every row)
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload
+  other_configs the image (4.6k tokens), 480p and long-video shapes: step,
+                per-phase and cold times, attention against the bf16 peak
+  measured_peaks  practical peaks of this GPU (MFMA chains, streaming read,
+                device copy); the headline fractions are also given against them
+  precompute_kernels  per-kernel times of one step (torch.profiler): block
+                statistics against the HBM peak, the spectral kernel against
+                the fp32 VALU peak (nominal 8 Lanczos steps per block)
 """
 from __future__ import annotations
 
@@ -40,6 +47,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP32_VALU_TFLOPS = 78.6   # MI355X fp32 vector FMA without packed-fp32 instructions (the build disables them)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic_video720p_75600.json")
 ATTN_SRCS = [os.path.join(ROOT, "block_sparse_attention_pisa_amd", "csrc", f)
              for f in ("paro_attention.hip", "paro_common.h")]
@@ -58,6 +66,8 @@ def parse():
                     help="skip the 480p and long-video steps (the other shapes of the metric)")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the error-against-dense table of the method and its ablations")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured practical peaks")
+    ap.add_argument("--no-split", action="store_true", help="skip the per-kernel profiler split of one step")
     ap.add_argument("--cpu-qblocks", type=int, default=48, help="query blocks per head in the oracle sample")
     ap.add_argument("--cpu-heads", type=int, default=1)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -235,10 +245,12 @@ def budget_entry(w, qd, kd, vd, stats, out, reps: int = 3):
             "k_i_min": int(kk.min()), "k_i_max": int(kk.max())}
 
 
-def configs_entry(names=("video480p_32760", "video_long_118800"), steps: int = 5):
-    """The other DiT shapes the metric spans (32k and 119k tokens), timed like
-    the headline step: precompute + route + attention on one stream, inputs
-    resident, HIP events around each step after two warm-up steps."""
+def configs_entry(names=("image_4608", "video480p_32760", "video_long_118800"), steps: int = 5):
+    """The other DiT shapes (the 4.6k-token image, and the 32k and 119k-token
+    videos the metric spans), timed like the headline step: precompute +
+    route + attention on one stream, inputs resident, HIP events around each
+    phase after two warm-up steps (medians of `steps`); cold: the median of 3
+    steps each after a 512 MB write that evicts L2 and MALL."""
     import torch
     from block_sparse_attention_pisa_amd import paro
     from workloads import WORKLOADS, make_inputs
@@ -258,26 +270,46 @@ def configs_entry(names=("video480p_32760", "video_long_118800"), steps: int = 5
             if ev:
                 ev[0].record(stream)
             paro.precompute(kd, vd, out=stats)
-            paro.route(qd, stats[0], stats[3], w.k, w.lam, out=idx)
             if ev:
                 ev[1].record(stream)
-            paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, w.k, out=o, workspace=ws)
+            paro.route(qd, stats[0], stats[3], w.k, w.lam, out=idx)
             if ev:
                 ev[2].record(stream)
+            paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, w.k, out=o, workspace=ws)
+            if ev:
+                ev[3].record(stream)
 
         for _ in range(2):
             step()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         for e in evs:
             step(e)
         torch.cuda.synchronize()
-        ms = sorted(e[0].elapsed_time(e[2]) for e in evs)[steps // 2]
-        att = sorted(e[1].elapsed_time(e[2]) for e in evs)[steps // 2]
+
+        def med(a, b):
+            return sorted(e[a].elapsed_time(e[b]) for e in evs)[steps // 2]
+        ms, pre, rou, att = med(0, 3), med(0, 1), med(1, 2), med(2, 3)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold = []
+        for i in range(3):
+            flush.fill_(i & 255)
+            cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            cev[0].record(stream)
+            step()
+            cev[1].record(stream)
+            torch.cuda.synchronize()
+            cold.append(cev[0].elapsed_time(cev[1]))
+        del flush
         flops = attention_flops(w, idx.cpu().numpy())
+        kv_bytes = 2.0 * w.B * w.H * w.L * w.d * 2
         out[name] = {"L": w.L, "H": w.H, "keep_k": w.k, "T": w.T, "median_ms_per_step": round(ms, 4),
                      "dense_equiv_TFLOPs": round(4.0 * w.B * w.H * w.L * w.L * w.d / (ms * 1e-3) / 1e12, 1),
+                     "phases_ms": {"precompute": round(pre, 4), "route": round(rou, 4), "attention": round(att, 4)},
                      "attention_ms": round(att, 4),
-                     "attention_frac_of_bf16_peak": round(flops / (att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                     "attention_TFLOPs": round(flops / (att * 1e-3) / 1e12, 1),
+                     "attention_frac_of_bf16_peak": round(flops / (att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "precompute_frac_of_hbm_peak": round(kv_bytes / (pre * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "cold_ms_per_step": round(sorted(cold)[1], 4)}
         del qd, kd, vd, stats, idx, o, ws
         torch.cuda.empty_cache()
     return out
@@ -315,7 +347,8 @@ def ablation_entry(name: str = "video480p_32760", permille=(50, 100, 125, 250, 5
     for pm in permille:
         kk = -(-pm * T // 1000)
         idx = paro.route(qd, stats[0], stats[3], kk, w.lam)
-        r = {"keep_permille": pm, "k": kk}
+        r = {"keep_permille": pm, "k": kk,
+             "captured_mass": round(captured_mass(qd, kd, idx, w.scale, list(range(0, T, 8)) + [T - 1]), 4)}
         for mode, kw in (("pisa", {}), ("zeroth", {"first_order": False}), ("drop", {"drop_tail": True})):
             o = paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, kk, **kw)
             r[mode] = round(float((o.float() - dense).norm()) / nd, 6)
@@ -333,7 +366,110 @@ def ablation_entry(name: str = "video480p_32760", permille=(50, 100, 125, 250, 5
     floor = round(float((full.float() - dense).norm()) / nd, 6)
     torch.cuda.synchronize()
     return {"workload": name, "error": "relative Frobenius norm of O - O_dense over all heads",
-            "dense_reference": "fp32 path, every block exact", "bf16_dense_floor": floor, "rows": rows}
+            "dense_reference": "fp32 path, every block exact", "bf16_dense_floor": floor,
+            "captured_mass": "mean share of the dense softmax mass on S_i, every 8th query block of every head",
+            "rows": rows}
+
+
+def peaks_entry(reps: int = 3):
+    """Practical peaks of this GPU, measured with the helper kernels of
+    libparo_peaks.so (include/paro_peaks.h) and a device copy: dense bf16
+    MFMA chains from registers (8 independent 32x32x16 chains per wave,
+    2 waves per SIMD), a streaming read of 4 GiB, and a 2 GiB
+    device-to-device copy (bytes read + written)."""
+    import ctypes
+
+    import torch
+    from block_sparse_attention_pisa_amd import build as _b
+    lib = ctypes.CDLL(_b.LIB_PEAKS)
+    lib.paro_peak_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.paro_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    nwg, iters = 256 * 2, 4000
+    sink = torch.zeros(1 << 14, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    def mfma():
+        assert lib.paro_peak_mfma_bf16(nwg, iters, sink.data_ptr(), sp) == 0
+    ms = timed(mfma)
+    mfma_tf = nwg * 4 * iters * 8 * 32768.0 / (ms * 1e-3) / 1e12
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+
+    def read():
+        assert lib.paro_peak_read(buf.data_ptr(), buf.numel(), 256 * 16, sink.data_ptr(), sp) == 0
+    ms_r = timed(read)
+    read_gbs = buf.numel() / (ms_r * 1e-3) / 1e9
+    src, dst = buf[:2 << 30], buf[2 << 30:]
+    ms_c = timed(lambda: dst.copy_(src))
+    copy_gbs = 2.0 * src.numel() / (ms_c * 1e-3) / 1e9
+    del buf, src, dst
+    torch.cuda.empty_cache()
+    return {"bf16_mfma_TFLOPs": round(mfma_tf, 1), "hbm_read_GBs": round(read_gbs, 1),
+            "hbm_copy_GBs": round(copy_gbs, 1),
+            "method": "register-operand MFMA chains (512 workgroups x 4 waves x 8 chains); 4 GiB streaming "
+                      "read; 2 GiB device copy counted as read + write"}
+
+
+def kernel_split_entry(step, names, steps: int = 3):
+    """Mean device time per launch of each kernel of the step, from a
+    torch.profiler trace of `steps` steps (kernel names matched by
+    substring). None when the profiler records no device activity."""
+    import torch
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+        acc = {}
+        for e in prof.events():
+            if e.device_type != torch.autograd.DeviceType.CUDA:
+                continue
+            for key, pat in names.items():
+                if pat in e.name:
+                    t = e.device_time if hasattr(e, "device_time") else e.cuda_time
+                    acc.setdefault(key, []).append(t)
+        if not acc:
+            return None
+        return {k: round(sum(v) / len(v) / 1e3, 4) for k, v in acc.items()}
+    except Exception as ex:  # the profiler is a measurement aid only
+        return {"error": str(ex)[:200]}
+
+
+def captured_mass(qd, kd, idx, scale: float, qblocks):
+    """Mean share of the dense softmax mass that falls on the exact blocks S_i
+    (the coverage measure of the vector-quantized attention review, Table 6),
+    over the rows of the sampled query blocks of every head; fp32 logits on
+    the device."""
+    import torch
+    B, H, L, d = qd.shape
+    T = idx.shape[2]
+    kblock = torch.arange(L, device=qd.device) // 64
+    tot, cnt = 0.0, 0
+    for b in range(B):
+        for h in range(H):
+            rows = torch.cat([torch.arange(64 * i, min(64 * i + 64, L), device=qd.device) for i in qblocks])
+            lg = (qd[b, h, rows].float() @ kd[b, h].float().t().contiguous()) * scale
+            p = torch.softmax(lg, dim=-1)
+            member = torch.zeros(T, T, dtype=torch.bool, device=qd.device)
+            member.scatter_(1, idx[b, h].long(), True)
+            mask = member[rows // 64][:, kblock]
+            share = (p * mask).sum(-1)
+            tot += float(share.sum())
+            cnt += share.numel()
+    return tot / cnt
 
 
 def cpu_baseline(w, q, k, v, nq: int, nheads: int):
@@ -446,6 +582,9 @@ def main():
 
     idx_cpu = idx.cpu().numpy()
     attn_flops, exact_flops = attention_flops(w, idx_cpu, with_exact=True)
+    split = None if a.no_split else kernel_split_entry(step, {
+        "block_stats": "k_block_stats", "hbar_reduce": "k_hbar_reduce", "spectral": "k_block_spectral",
+        "route": "k_route", "centroids_bf16": "k_centroids_bf16", "attention": "k_attn_bf16"})
 
     # the exact phase on this workload: the same kernel with U_i dropped
     # (keep-or-drop mode), exact FLOPs over its time
@@ -527,6 +666,29 @@ def main():
         "cold_ms_per_step": round(sorted(cold)[1], 4),
         "input_generation_s": round(t_gen, 1),
     }
+    if split and "error" not in split:
+        pk = {"kernels_ms_per_launch": split}
+        if "block_stats" in split:
+            gbs = kv_bytes / (split["block_stats"] * 1e-3) / 1e9
+            pk["block_stats"] = {"algorithmic_GBs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        if "spectral" in split:
+            # nominal work: 8 Lanczos steps of A^T A per block (A x and A^T y, 2 d^2 FMAs each)
+            fl = 8 * 4.0 * w.d * w.d * w.B * w.H * w.T
+            tf = fl / (split["spectral"] * 1e-3) / 1e12
+            pk["spectral"] = {"nominal_flops": fl, "TFLOPs": round(tf, 2),
+                              "frac_of_fp32_valu_peak": round(tf / PEAK_FP32_VALU_TFLOPS, 4),
+                              "note": "fp32 VALU peak without packed-fp32 instructions (78.6 TFLOP/s)"}
+        res["precompute_kernels"] = pk
+    elif split:
+        res["precompute_kernels"] = split
+    if not a.no_peaks:
+        peaks = peaks_entry()
+        res["measured_peaks"] = peaks
+        res["roofline"]["frac_of_measured_peak"] = round(achieved / peaks["bf16_mfma_TFLOPs"], 4)
+        res["precompute_hbm"]["frac_of_measured_read"] = round(kv_bytes / (pre_ms * 1e-3) / 1e9 /
+                                                              peaks["hbm_read_GBs"], 4)
+        res["route_hbm"]["frac_of_measured_read"] = round(route_bytes / (route_ms * 1e-3) / 1e9 /
+                                                         peaks["hbm_read_GBs"], 4)
     if not a.no_exact_phase:
         del qd, kd, vd, stats, idx, out
         torch.cuda.empty_cache()

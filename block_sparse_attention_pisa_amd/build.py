@@ -1,7 +1,9 @@
 """Build libparo.so (the C-ABI library) in-tree for gfx950 with hipcc.
 
 Every HIP source under csrc/ is compiled to an object in _build/ and linked
-into block_sparse_attention_pisa_amd/libparo.so. Run: python -m
+into block_sparse_attention_pisa_amd/libparo.so; peaks/paro_peaks.hip (the
+practical-peak measurement kernels, include/paro_peaks.h) becomes
+libparo_peaks.so. Run: python -m
 block_sparse_attention_pisa_amd.build
 """
 from __future__ import annotations
@@ -16,6 +18,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libparo.so")
+# measurement helpers (practical peaks), a library of their own: not part of the PISA path
+PEAKS_SRC = os.path.join(PKG, "peaks", "paro_peaks.hip")
+LIB_PEAKS = os.path.join(PKG, "libparo_peaks.so")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -41,19 +46,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = _sources()
-    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = _sources()
+    with ThreadPoolExecutor(min(8, len(srcs) + 1)) as ex:
+        objs = list(ex.map(_compile, srcs + [PEAKS_SRC]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], LIB_PEAKS)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} from {len(srcs)} sources and {LIB_PEAKS}")
     return LIB
 
 
