@@ -345,22 +345,22 @@ __global__ __launch_bounds__(256) void k_hbar_reduce(const float* __restrict__ w
 // identical data, so the waves take identical decisions without further
 // synchronisation.
 //   * Vectors: fp32, lane l holds entries 16 tj + c (tj < D / 16); dot
-//     products are 16-lane DPP sums. Classical Gram-Schmidt against the
-//     whole basis (kept in LDS, one copy per wave).
-//   * After kLanczosCheck and after kLanczosK steps the Ritz pair of the
-//     tridiagonal is computed (64-point Sturm multisection across the lanes,
-//     then inverse iteration); the block stops when the residual bound
-//     res^2 / (gap * theta) < kLanczosTol, otherwise the process restarts
-//     from the Ritz vector after kLanczosK steps.
+//     products are 16-lane DPP sums.
+//   * Three-term recurrence (the basis is kept in LDS only to form the Ritz
+//     vector). From kLanczosCheck steps on, after every step, the Ritz pair
+//     of the tridiagonal is computed (64-point Sturm multisection across the
+//     lanes, then inverse iteration); the block stops when the residual
+//     bound res^2 / (gap * theta) < kLanczosTol, otherwise the process
+//     restarts from the Ritz vector after kLanczosK steps.
 //   * M_j = ||A x|| / ||x|| is then evaluated in fp64 from the fp32 Ritz
 //     vector, so its error is quadratic in the angle of x.
 // Power iteration alone needs thousands of steps when sigma_2 / sigma_1 is
 // close to 1 (blocks of i.i.d. keys); Lanczos converges in 5 to 8 steps for
 // almost every block of the video workloads.
 constexpr int kLanczosK = 8;
-constexpr int kLanczosCheck = 6;
+constexpr int kLanczosCheck = 5;     // first step count at which convergence is tested (then every step)
 constexpr int kLanczosCycles = 16;
-constexpr double kLanczosTol = 1e-9;
+constexpr double kLanczosTol = 3e-9;
 constexpr int kPairThreads = 128;
 
 __device__ __forceinline__ float start_sign(int row) {
@@ -423,6 +423,15 @@ __device__ __forceinline__ void pair_ax(const PairA<D>& A, const float (&x)[D / 
       y[ti][r] = row_sum16(p);
     }
 }
+// Sum over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48);
+// the two additions are commutative pairs, so all four lanes get bitwise the
+// same total. (Not the cross-row swaps of CDNA4: the compiler takes both
+// results of its two-result swap builtin from one register.)
+__device__ __forceinline__ float sum_over_rows4(float q) {
+  q += __shfl_xor(q, 16);
+  return q + __shfl_xor(q, 32);
+}
+
 // z = (partial over this wave's rows of) A^T y, summed over the 4 lane groups.
 template <int D>
 __device__ __forceinline__ void pair_aty(const PairA<D>& A, const float (&y)[D / 32][4], float (&z)[D / 16]) {
@@ -433,10 +442,43 @@ __device__ __forceinline__ void pair_aty(const PairA<D>& A, const float (&y)[D /
     for (int ti = 0; ti < PairA<D>::MT; ++ti)
 #pragma unroll
       for (int r = 0; r < 4; ++r) q += A.v[ti][tj][r] * y[ti][r];
-    q += __shfl_xor(q, 16);
-    q += __shfl_xor(q, 32);
-    z[tj] = q;
+    z[tj] = sum_over_rows4(q);
   }
+}
+
+// 64-bit DPP move (both halves with the same control).
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double v) {
+  int2 x = __builtin_bit_cast(int2, v);
+  x.x = __builtin_amdgcn_update_dpp(0, x.x, CTRL, 0xF, 0xF, false);
+  x.y = __builtin_amdgcn_update_dpp(0, x.y, CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, x);
+}
+// One level of the reduce-scatter: lanes whose bit `bit` is set keep the
+// upper half of `in` and send the lower half, the others the reverse; the
+// partner (given by the DPP control, a lane with that bit flipped and the
+// same higher bits) sends back the half this lane keeps.
+template <int N, int CTRL>
+__device__ __forceinline__ void rs_level(const double (&in)[2 * N], double (&out)[N], bool bit) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const double keep = bit ? in[N + i] : in[i];
+    const double send = bit ? in[i] : in[N + i];
+    out[i] = keep + dpp64<CTRL>(send);
+  }
+}
+// Sum over the 16 lanes of a DPP row of 16 values per lane; returns, in lane
+// c of the row, the total of value c. Partners: row_mirror (c, 15 - c),
+// row_half_mirror (c, c ^ 7 within each 8), quad_perm (c ^ 2), quad_perm
+// (c ^ 1): each pairs lanes that differ in the level's bit and share the
+// bits above it, so after four levels every lane has summed all 16 lanes.
+__device__ __forceinline__ double butterfly16(const double (&p)[16], int c) {
+  double a[8], b[4], d[2], e[1];
+  rs_level<8, 0x140>(p, a, (c & 8) != 0);
+  rs_level<4, 0x141>(a, b, (c & 4) != 0);
+  rs_level<2, 0x4E>(b, d, (c & 2) != 0);
+  rs_level<1, 0xB1>(d, e, (c & 1) != 0);
+  return e[0];
 }
 
 // Number of eigenvalues below x of the tridiagonal (al, be): sign changes of
@@ -473,13 +515,18 @@ __device__ __forceinline__ void multisect(const float (&al)[m], const float (&be
   }
 }
 
-// Ritz pair of the m-step tridiagonal of this wave: writes the (unnormalised)
-// Ritz vector to x and returns whether the residual bound is met. Computed in
-// fp32 on T / ||T|| (the Lanczos coefficients are fp32 quantities; M_j itself
-// is evaluated afterwards in fp64 from the vector).
+// Ritz pair of the m-step tridiagonal of this wave: returns whether the
+// residual bound is met, and writes the (unnormalised) Ritz vector to x when
+// it is or when `form` is set (a restart needs it). Computed in fp32 on
+// T / ||T|| (the Lanczos coefficients are fp32 quantities; M_j itself is
+// evaluated afterwards in fp64 from the vector): the top eigenvalue to fp32
+// precision by four rounds of 64-point multisection, the second one only to
+// a conservative bracket (two rounds; the test uses its upper end, so the
+// gap is never overestimated), the eigenvector by two passes of inverse
+// iteration just above the top eigenvalue.
 template <int m, int D>
 __device__ __forceinline__ bool ritz_step(const float* al_s, const float* be_s, const float (*basis)[D], int l,
-                                          int c, float (&x)[D / 16]) {
+                                          int c, bool form, float (&x)[D / 16]) {
   constexpr int NT = D / 16;
   float al[m], be[m];
   float lo = 0.f, hi = 0.f;
@@ -505,9 +552,10 @@ __device__ __forceinline__ bool ritz_step(const float* al_s, const float* be_s, 
     al[i] *= inv_scale;
     be[i] *= inv_scale;
   }
-  float lo1 = lo * inv_scale, hi1 = hi * inv_scale, lo2 = lo1, hi2 = hi1;
+  float lo1 = lo * inv_scale, hi1 = hi * inv_scale;
   multisect<m>(al, be, 1, 4, lo1, hi1, l);
-  multisect<m>(al, be, 2, 3, lo2, hi2, l);
+  float lo2 = lo * inv_scale, hi2 = hi1;
+  multisect<m>(al, be, 2, 2, lo2, hi2, l);
   const float theta = 0.5f * (lo1 + hi1);
   // inverse iteration with (mu I - T), mu just above theta: positive definite
   const float mu = hi1 + fmaxf(fabsf(theta) * 1e-6f, 1e-30f);
@@ -515,7 +563,7 @@ __device__ __forceinline__ bool ritz_step(const float* al_s, const float* be_s, 
 #pragma unroll
   for (int i = 0; i < m; ++i) sv[i] = 1.f;
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
+  for (int pass = 0; pass < 2; ++pass) {
     float cp[m], bp[m];
     float rden = __builtin_amdgcn_rcpf(fmaxf(mu - al[0], 1e-30f));
     cp[0] = -be[0] * rden;
@@ -541,14 +589,16 @@ __device__ __forceinline__ bool ritz_step(const float* al_s, const float* be_s, 
   const float gap = theta - hi2;
   const bool conv = res == 0.f || (gap > 0.f && theta > 0.f &&
                                    static_cast<double>(res) * res < kLanczosTol * gap * theta);
+  if (conv || form) {
 #pragma unroll
-  for (int tj = 0; tj < NT; ++tj) x[tj] = 0.f;
+    for (int tj = 0; tj < NT; ++tj) x[tj] = 0.f;
 #pragma unroll
-  for (int i = 0; i < m; ++i) {
-    float b[NT];
-    load_vec<NT>(basis[i], c, b);
+    for (int i = 0; i < m; ++i) {
+      float b[NT];
+      load_vec<NT>(basis[i], c, b);
 #pragma unroll
-    for (int tj = 0; tj < NT; ++tj) x[tj] += sv[i] * b[tj];
+      for (int tj = 0; tj < NT; ++tj) x[tj] += sv[i] * b[tj];
+    }
   }
   return conv;
 }
@@ -661,14 +711,21 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2)
   }
   bool done = false;
   for (int cyc = 0; cyc < kLanczosCycles && !done; ++cyc) {
-    float v[NT];
+    float v[NT], vp[NT];
     {
       const float n2 = vdot<NT>(x, x);
       const float inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
 #pragma unroll
-      for (int tj = 0; tj < NT; ++tj) v[tj] = x[tj] * inv;
+      for (int tj = 0; tj < NT; ++tj) {
+        v[tj] = x[tj] * inv;
+        vp[tj] = 0.f;
+      }
     }
+    float beta_prev = 0.f;
     if (g == 0) store_vec<NT>(basis[0], c, v);
+    // three-term recurrence: within kLanczosK steps the basis stays
+    // orthogonal enough for the top Ritz pair (the Ritz value is then
+    // re-evaluated from A itself)
     for (int k = 0; k < kLanczosK; ++k) {
       float z[NT];
       {
@@ -677,54 +734,57 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2)
         pair_aty<D>(A, y, z);
       }
       exchange(z);
+      const float alpha = vdot<NT>(z, v);
       float wv[NT];
 #pragma unroll
-      for (int tj = 0; tj < NT; ++tj) wv[tj] = z[tj];
-      float alpha = 0.f;
-      for (int kk = 0; kk <= k; ++kk) {
-        float b[NT];
-        if (kk == k) {
-#pragma unroll
-          for (int tj = 0; tj < NT; ++tj) b[tj] = v[tj];
-        } else {
-          load_vec<NT>(basis[kk], c, b);
-        }
-        const float cc = vdot<NT>(z, b);
-        if (kk == k) alpha = cc;
-#pragma unroll
-        for (int tj = 0; tj < NT; ++tj) wv[tj] -= cc * b[tj];
-      }
+      for (int tj = 0; tj < NT; ++tj) wv[tj] = z[tj] - alpha * v[tj] - beta_prev * vp[tj];
       const float beta = sqrtf(vdot<NT>(wv, wv));
       const float binv = beta > 0.f ? __builtin_amdgcn_rcpf(beta) : 0.f;
 #pragma unroll
-      for (int tj = 0; tj < NT; ++tj) v[tj] = wv[tj] * binv;
+      for (int tj = 0; tj < NT; ++tj) {
+        vp[tj] = v[tj];
+        v[tj] = wv[tj] * binv;
+      }
+      beta_prev = beta;
       if (g == 0) store_vec<NT>(basis[k + 1], c, v);
       if (l == 0) {
         s.al[w][k] = alpha;
         s.be[w][k] = beta;
       }
-      if (k + 1 == kLanczosCheck) {
-        if (ritz_step<kLanczosCheck, D>(s.al[w], s.be[w], basis, l, c, x)) {
+      if (k + 1 >= kLanczosCheck) {
+        bool conv;
+        switch (k + 1) {
+          case 5: conv = ritz_step<5, D>(s.al[w], s.be[w], basis, l, c, false, x); break;
+          case 6: conv = ritz_step<6, D>(s.al[w], s.be[w], basis, l, c, false, x); break;
+          case 7: conv = ritz_step<7, D>(s.al[w], s.be[w], basis, l, c, false, x); break;
+          default: conv = ritz_step<kLanczosK, D>(s.al[w], s.be[w], basis, l, c, true, x); break;
+        }
+        if (conv) {
           done = true;
           break;
         }
-      } else if (k + 1 == kLanczosK) {
-        done = ritz_step<kLanczosK, D>(s.al[w], s.be[w], basis, l, c, x);
       }
     }
   }
-  // M_j = ||A x|| / ||x|| in fp64 from the fp32 Ritz vector.
-  double ysq = 0.0;
+  // M_j = ||A x|| / ||x|| in fp64 from the fp32 Ritz vector. Each lane's 16
+  // row partials are summed over the 16 lanes of its DPP row by a butterfly
+  // reduce-scatter (after it lane c holds the whole of its row c), so the
+  // 64-bit values cross lanes 15 times instead of 64.
+  static_assert(4 * MT <= 16, "at most 16 rows per lane");
+  double p[16];  // rows 4 ti + r of this lane (4 MT of them; the rest are zero for D = 64)
+#pragma unroll
+  for (int i = 4 * MT; i < 16; ++i) p[i] = 0.0;
 #pragma unroll
   for (int ti = 0; ti < MT; ++ti)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      double p = 0.0;
+      double q = 0.0;
 #pragma unroll
-      for (int tj = 0; tj < NT; ++tj) p += static_cast<double>(A.v[ti][tj][r]) * x[tj];
-      p = row_sum16(p);
-      ysq += p * p;
+      for (int tj = 0; tj < NT; ++tj) q += static_cast<double>(A.v[ti][tj][r]) * x[tj];
+      p[4 * ti + r] = q;
     }
+  const double yrow = butterfly16(p, c);
+  const double ysq = row_sum16(yrow * yrow);
   double x2 = 0.0;
 #pragma unroll
   for (int tj = 0; tj < NT; ++tj) x2 += static_cast<double>(x[tj]) * x[tj];
