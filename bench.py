@@ -472,6 +472,48 @@ def captured_mass(qd, kd, idx, scale: float, qblocks):
     return tot / cnt
 
 
+def budget_ablation_entry(H: int = 8, L: int = 64 * 512, d: int = 128, permille=(50, 100, 125, 250)):
+    """Per-query-block budgets where they matter: error against dense
+    attention of the method with a fixed k per query block and with the same
+    total shared out by need (paro_route_budget, at least one block per row),
+    on the varying-need input (workloads.varying_need_inputs: some query
+    blocks attend sharply, others broadly). Dense = the fp32 path with every
+    block exact; error = relative Frobenius norm over all heads and rows."""
+    import torch
+    from block_sparse_attention_pisa_amd import paro
+    from workloads import varying_need_inputs
+    q, k, v = varying_need_inputs(1, H, L, d)
+    T = -(-L // 64)
+    q32, k32, v32 = (x.float().cuda() for x in (q, k, v))
+    st32 = paro.precompute(k32, v32)
+    dense = paro.attention(q32, k32, v32, st32[0], st32[1], st32[2], paro.route(q32, st32[0], st32[3], T, 0.1), T)
+    del q32, k32, v32, st32
+    nd = float(dense.norm())
+    qd, kd, vd = (x.cuda() for x in (q, k, v))
+    stats = paro.precompute(kd, vd)
+    rows = []
+    for pm in permille:
+        kk = -(-pm * T // 1000)
+        idx = paro.route(qd, stats[0], stats[3], kk, 0.1)
+        o = paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, kk)
+        e_fixed = float((o.float() - dense).norm()) / nd
+        offs, idx_b, _ = paro.route_budget(qd, stats[0], stats[3], kk * T, 1, 0.1)
+        o = paro.attention_csr(qd, kd, vd, stats[0], stats[1], stats[2], offs, idx_b, kk * T)
+        e_budget = float((o.float() - dense).norm()) / nd
+        # keep-or-drop (tail dropped) with the same two allocations
+        o = paro.attention(qd, kd, vd, stats[0], stats[1], stats[2], idx, kk, drop_tail=True)
+        d_fixed = float((o.float() - dense).norm()) / nd
+        o = paro.attention_csr(qd, kd, vd, stats[0], stats[1], stats[2], offs, idx_b, kk * T, drop_tail=True)
+        d_budget = float((o.float() - dense).norm()) / nd
+        ki = torch.diff(offs.to(torch.int64), dim=-1)
+        rows.append({"keep_permille": pm, "k": kk, "fixed_k": round(e_fixed, 6), "budget": round(e_budget, 6),
+                     "drop_fixed_k": round(d_fixed, 6), "drop_budget": round(d_budget, 6),
+                     "k_i_min": int(ki.min()), "k_i_max": int(ki.max())})
+    torch.cuda.synchronize()
+    return {"workload": f"varying need, B=1, H={H}, L={L}, d={d}, bf16", "total_per_head": "k T (same as fixed k)",
+            "error": "relative Frobenius norm of O - O_dense over all heads", "rows": rows}
+
+
 def cpu_baseline(w, q, k, v, nq: int, nheads: int):
     """Time the fp64 oracle on host cores on a bounded sample of the workload.
 
@@ -695,6 +737,7 @@ def main():
         res["exact_phase"] = exact_phase_entry()
     if not a.no_ablation:
         res["ablation"] = ablation_entry()
+        res["budget_ablation"] = budget_ablation_entry()
     if not a.no_configs:
         res["other_configs"] = configs_entry()
     if not a.no_cpu_baseline:

@@ -128,23 +128,14 @@ def test_uniform_budget_is_the_fixed_k_path():
 
 @pytest.mark.parametrize("per_row", [10, 30])
 def test_budget_with_strongly_varying_need(per_row):
-    """Keys of block j offset by a random mu_j (so centroid logits vary), and
-    queries pointing along one direction with a strength of 0.2, 1 or 5 by
-    block: sharper rows spread over fewer blocks, so the sharing is far from
-    uniform. With 30 blocks per row on average (T = 41) the neediest rows
+    """The varying-need input (workloads.varying_need_inputs: keys of block j
+    offset by a random mu_j, so centroid logits vary, and queries pointing
+    along one direction with a strength of 0.2, 1 or 5 by block): sharper
+    rows spread over fewer blocks, so the sharing is far from uniform. With 30 blocks per row on average (T = 41) the neediest rows
     reach T and what they cannot take is shared again among the others."""
-    from workloads import random_uniform_inputs
+    from workloads import varying_need_inputs
     B, H, L, d = 1, 2, 64 * 40 + 9, 128
-    q, k, v = random_uniform_inputs(B, H, L, d, dtype=torch.float32, seed=17, scale=0.8)
-    g = torch.Generator().manual_seed(3)
-    T0 = -(-L // 64)
-    mu = torch.randn(B, H, T0, d, generator=g) * 3.0
-    k = (k + mu.repeat_interleave(64, dim=2)[:, :, :L]).to(torch.bfloat16)
-    u = torch.randn(d, generator=g)
-    u = 3.0 * u / u.norm()
-    f = torch.tensor([0.2, 1.0, 5.0]).repeat_interleave(64).repeat(-(-L // 192))[:L]
-    q = (0.1 * q + f[None, None, :, None] * u).to(torch.bfloat16)
-    v = v.to(torch.bfloat16)
+    q, k, v = varying_need_inputs(B, H, L, d)
     T, scale = -(-L // 64), 1 / np.sqrt(d)
     K = per_row * T
     (qd, kd, vd), stats, _ = run_gpu(q, k, v, 1, 0.1)

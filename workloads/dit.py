@@ -205,3 +205,32 @@ def random_uniform_inputs(B, H, L, d, dtype=torch.float32, seed=0, scale=1.0):
         a = g.standard_normal((B, H, L, d)).astype(np.float32) * np.float32(scale)
         out.append(torch.from_numpy(a).to(dtype))
     return tuple(out)
+
+
+def varying_need_inputs(B, H, L, d, dtype=torch.bfloat16, seed=17):
+    """Inputs whose query blocks need very different numbers of exact blocks
+    (a stand-in for DiT attention in which some outputs attend sharply and
+    others broadly, the situation the ALLOT review's per-output budgets are
+    for). Recipe, numpy ``default_rng(seed)``:
+      * base q, k, v iid N(0, 0.8^2), shape [B, H, L, d];
+      * every key of block j is offset by mu_j ~ N(0, 3^2 I) (drawn per
+        (b, h, j)), so block centroids are far apart and the centroid logits
+        vary across blocks;
+      * a unit direction u (drawn per (b, h)) scaled to norm 3; the queries of
+        block i are 0.1 q + f_i u with f_i = 0.2, 1, 5 repeating over the
+        blocks, so blocks with a small f spread their attention over many
+        blocks and blocks with a large f concentrate it on a few.
+    v is left as drawn. Values are rounded to ``dtype`` at the end."""
+    g = np.random.default_rng(seed)
+    f32 = np.float32
+    T = -(-L // 64)
+    q = g.standard_normal((B, H, L, d), dtype=f32) * f32(0.8)
+    k = g.standard_normal((B, H, L, d), dtype=f32) * f32(0.8)
+    v = g.standard_normal((B, H, L, d), dtype=f32) * f32(0.8)
+    mu = g.standard_normal((B, H, T, d), dtype=f32) * f32(3.0)
+    k += np.repeat(mu, 64, axis=2)[:, :, :L]
+    u = g.standard_normal((B, H, 1, d), dtype=f32)
+    u *= f32(3.0) / np.linalg.norm(u, axis=-1, keepdims=True)
+    f = np.tile(np.repeat(np.array([0.2, 1.0, 5.0], dtype=f32), 64), -(-L // 192))[:L]
+    q = f32(0.1) * q + f[None, None, :, None] * u
+    return tuple(torch.from_numpy(np.ascontiguousarray(x)).to(dtype) for x in (q, k, v))
