@@ -84,8 +84,14 @@ __device__ __forceinline__ void add_piece<float>(double* acc, uint4 raw) {
 // offsets[i + 1] - offsets[i] best blocks at idx + offsets[i]).
 constexpr int kRouteFixed = 0, kRouteWeights = 1, kRouteRagged = 2;
 
+// Rows of more than 1280 blocks (NI >= 24) take over 80 KB of LDS for the
+// dots of 16 rows, so only one workgroup fits on a CU: those instantiations
+// may use 256 registers (two waves per SIMD) instead of spilling the keys.
+template <int NI>
+constexpr int route_waves_per_eu() { return NI >= 24 ? 2 : 4; }
+
 template <typename E, int D, int NI, int kMode>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_route(const E* __restrict__ Q, const float* __restrict__ kbar,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(route_waves_per_eu<NI>()))) void k_route(const E* __restrict__ Q, const float* __restrict__ kbar,
                                                     const double* __restrict__ M, int32_t* __restrict__ idx,
                                                     int L, int T, int R, int keep_k, double scale,
                                                     double lambda, float* __restrict__ qbar_ws,
@@ -180,18 +186,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     __syncthreads();  // qs is overwritten by the dots from here on
     const int nblk = ceil_div(T, 16);
+    // the centroids of the next block of 16 are loaded while the current
+    // ones are multiplied (one register set in flight)
+    auto load_kv = [&](int c, float4 (&kv4)[NQ]) {
+      const int n = min(16 * c + n16, T - 1);
+      const float4* kr = reinterpret_cast<const float4*>(kb + static_cast<size_t>(n) * D) + g;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) kv4[q] = kr[4 * q];
+    };
+    float4 nxt[NQ];
+    if (w < nblk) load_kv(w, nxt);
     for (int c = w; c < nblk; c += kWaves) {
       const int n = 16 * c + n16;
-      const float4* kr = reinterpret_cast<const float4*>(kb + static_cast<size_t>(min(n, T - 1)) * D) + g;
       float kv[4 * NQ];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        const float4 x = kr[4 * q];
-        kv[4 * q] = x.x;
-        kv[4 * q + 1] = x.y;
-        kv[4 * q + 2] = x.z;
-        kv[4 * q + 3] = x.w;
+        kv[4 * q] = nxt[q].x;
+        kv[4 * q + 1] = nxt[q].y;
+        kv[4 * q + 2] = nxt[q].z;
+        kv[4 * q + 3] = nxt[q].w;
       }
+      if (c + kWaves < nblk) load_kv(c + kWaves, nxt);
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4 * NQ; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[ks], kv[ks], acc, 0, 0, 0);
