@@ -32,6 +32,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxRows = 16;   // query blocks per workgroup = rows of the 16x16 MFMA tile
 constexpr int kMaxKeyRegs = 32;  // keys per lane kept in registers: rows of T <= 2048 never re-read LDS
+constexpr int kCompactRegs = 4;  // registers per lane of the selection's late bits (up to 256 keys)
 constexpr size_t kLdsBudget = 152 * 1024;
 
 // Order-preserving map of a double onto uint64 (larger score -> larger key);
@@ -306,7 +307,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(route_
       mask = top == 63 ? 0ull : ~0ull << (top + 1);
       prefix = kmax & mask;
       int match = T;
-      for (int b = top; b >= 0 && match != rem; --b) {
+      // decide bit b from the count c1 of keys (among those equal to prefix
+      // under mask, the only ones that can match want) that have it set
+      auto decide = [&](int b, int c1) {
+        if (rem <= c1) {
+          prefix = prefix | (1ull << b);
+          match = c1;
+        } else {
+          rem -= c1;
+          match -= c1;
+        }
+        mask |= 1ull << b;
+      };
+      int b = top;
+      // Once few keys still equal prefix under mask (`match` of them), they
+      // are gathered into kCompactRegs registers per lane and the remaining
+      // bits are counted over those alone: a key that differs from prefix
+      // under mask never matches again (mask only grows), so every count,
+      // and with it the result, is the same. The gather goes through this
+      // row's slice of `dots`, dead once the keys are in registers (T <=
+      // tail0), 8-byte aligned inside it.
+      // (dots is 16-byte aligned, so the slice's base is 8-byte aligned when r T is even)
+      uint64_t* gathered = reinterpret_cast<uint64_t*>(dots + r * T + ((r * T) & 1));
+      const int cap = T <= tail0 ? min(64 * kCompactRegs, (4 * T - 4) / 8) : 0;
+      for (; b >= 0 && match != rem && match > cap; --b) {
         const uint64_t m2 = mask | (1ull << b), want = prefix | (1ull << b);
         int c1 = 0;
 #pragma unroll
@@ -315,14 +339,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(route_
           const int j = base + l;
           c1 += count_lanes(j < T && (score_key(score_at(j)) & m2) == want);
         }
-        if (rem <= c1) {
-          prefix = want;
-          match = c1;
-        } else {
-          rem -= c1;
-          match -= c1;
+        decide(b, c1);
+      }
+      if (b >= 0 && match != rem) {
+        // (here T <= tail0: every key is in key[], padding keys are 0)
+        int pos = 0;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const bool alive = 64 * i + l < T && (key[i] & mask) == prefix;
+          const uint64_t bal = __ballot(alive);
+          if (alive) gathered[pos + lanes_below(bal)] = key[i];
+          pos += __builtin_popcountll(bal);
         }
-        mask = m2;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        // pos == match <= cap; lanes past it hold 0, which never equals a
+        // want (bit b is set in every want)
+        uint64_t ck[kCompactRegs];
+#pragma unroll
+        for (int c = 0; c < kCompactRegs; ++c) ck[c] = 64 * c + l < pos ? gathered[64 * c + l] : 0ull;
+        for (; b >= 0 && match != rem; --b) {
+          const uint64_t m2 = mask | (1ull << b), want = prefix | (1ull << b);
+          int c1 = 0;
+#pragma unroll
+          for (int c = 0; c < kCompactRegs; ++c) c1 += count_lanes((ck[c] & m2) == want);
+          decide(b, c1);
+        }
       }
     }
     // Take every key above prefix under mask and the first rem (in ascending
