@@ -233,6 +233,40 @@ def test_route_exact_ties_and_equal_scores(keep):
         assert (idx.cpu().numpy()[0, 0] == ir).all()
 
 
+@pytest.mark.parametrize("keep", [37, 300, 560])
+def test_route_ties_through_the_gathered_search(keep):
+    """T = 601 kv blocks made of 15 distinct blocks repeated about 40 times
+    each in a shuffled order: every row has tie groups of ~40 exactly equal
+    scores, so the threshold search narrows to a few hundred candidate keys
+    (gathered into a few registers per lane through the row's LDS slice of
+    dots, which for odd T starts 4 bytes into the slice on every other row)
+    and then runs out of bits inside a tie, where the lower block indices
+    must win."""
+    d, nb, nd = 64, 601, 15
+    g = np.random.default_rng(keep)
+    base = torch.from_numpy(g.standard_normal((nd, 64, d)).astype(np.float32))
+    order = g.permutation(np.arange(nb) % nd)
+    L = 64 * nb - 17
+    k = torch.cat([base[i] for i in order])[:L][None, None].to(torch.bfloat16)
+    v = torch.cat([base[(i + 3) % nd] for i in order])[:L][None, None].to(torch.bfloat16)
+    q = torch.from_numpy(g.standard_normal((1, 1, L, d)).astype(np.float32)).to(torch.bfloat16)
+    (qd, kd, vd), stats, idx = run_gpu(q, k, v, keep, 0.1)
+    qn, kn, vn = (x[0, 0].double().numpy() for x in (q, k, v))
+    st = pisa.block_stats(kn, vn, 64)
+    ir, sc = pisa.route(qn, st["kbar"], st["M"], keep, 0.1, 1 / np.sqrt(d), 64)
+    ig = idx.cpu().numpy()[0, 0]
+    check_route(ig, ir, sc)
+    # the duplicated full blocks tie exactly on the GPU too: within a row, a
+    # taken copy of a block means every lower-indexed copy is taken as well
+    full = order[: nb - 1]
+    for i in range(0, nb, 7):
+        taken = set(ig[i].tolist())
+        for blk in range(nd):
+            copies = [j for j in range(nb - 1) if full[j] == blk]
+            flags = [j in taken for j in copies]
+            assert flags == sorted(flags, reverse=True), (i, blk)
+
+
 @pytest.mark.parametrize("keep", [300, 2060])
 def test_route_rows_longer_than_register_keys(keep):
     """T = 2100 > 2048 kv blocks: the keys past the first 2048 of a row are
