@@ -347,19 +347,23 @@ __global__ __launch_bounds__(256) void k_hbar_reduce(const float* __restrict__ w
 //   * Vectors: fp32, lane l holds entries 16 tj + c (tj < D / 16); dot
 //     products are 16-lane DPP sums.
 //   * Three-term recurrence (the basis is kept in LDS only to form the Ritz
-//     vector). From kLanczosCheck steps on, after every step, the Ritz pair
-//     of the tridiagonal is computed (64-point Sturm multisection across the
-//     lanes, then inverse iteration); the block stops when the residual
-//     bound res^2 / (gap * theta) < kLanczosTol, otherwise the process
-//     restarts from the Ritz vector after kLanczosK steps.
+//     vector). After steps 5, 6, 7 and 8, then every second step to 16, then
+//     after 20 and 24, the Ritz pair of the tridiagonal is computed (64-point
+//     Sturm multisection across the lanes, then inverse iteration); the block
+//     stops when the residual bound res^2 / (gap * theta) < kLanczosTol,
+//     otherwise the process restarts from the Ritz vector after kLanczosK
+//     steps. Almost every block of the video workloads stops within 8 steps;
+//     the long cycle is for blocks of i.i.d. keys (the text tokens of the
+//     image shape: sigma_2 / sigma_1 about 0.9-0.99), which restarted every 8
+//     steps needed up to 37 and with 24-step cycles about 20.
 //   * M_j = ||A x|| / ||x|| is then evaluated in fp64 from the fp32 Ritz
 //     vector, so its error is quadratic in the angle of x.
 // Power iteration alone needs thousands of steps when sigma_2 / sigma_1 is
 // close to 1 (blocks of i.i.d. keys); Lanczos converges in 5 to 8 steps for
 // almost every block of the video workloads.
-constexpr int kLanczosK = 8;
-constexpr int kLanczosCheck = 5;     // first step count at which convergence is tested (then every step)
-constexpr int kLanczosCycles = 16;
+constexpr int kLanczosK = 24;        // steps per cycle before a restart
+constexpr int kLanczosCheck = 5;     // first step count at which convergence is tested
+constexpr int kLanczosCycles = 6;
 constexpr double kLanczosTol = 3e-9;
 constexpr int kPairThreads = 128;
 
@@ -383,6 +387,7 @@ struct PairLds {
   float vsum[D];
   float al[2][kLanczosK];
   float be[2][kLanczosK];
+  float rz[2][3][kLanczosK];  // per wave: sv, cp, bp of ritz_step_long
   double red[2][4];
 };
 
@@ -487,6 +492,7 @@ __device__ __forceinline__ double butterfly16(const double (&p)[16], int c) {
 // every p_i far from the fp32 range limits for m <= 8.
 template <int m>
 __device__ __forceinline__ int sturm_below(const float (&al)[m], const float (&be)[m], float x) {
+  static_assert(m <= 8, "longer tridiagonals go through sturm_below_long");
   float p0 = 1.f, p1 = al[0] - x;
   int changes = p1 < 0.f ? 1 : 0;
 #pragma unroll
@@ -495,6 +501,25 @@ __device__ __forceinline__ int sturm_below(const float (&al)[m], const float (&b
     changes += ((p2 < 0.f) != (p1 < 0.f)) ? 1 : 0;
     p0 = p1;
     p1 = p2;
+  }
+  return changes;
+}
+// The same count for a tridiagonal of m <= kLanczosK terms read from LDS
+// (al, be unscaled; sc = 1 / ||T||). Past 8 terms the pair (p_{i-1}, p_i) is
+// rescaled by 2^64 or 2^-64 whenever it has become tiny or huge: the
+// recurrence is linear in the pair, so a common positive factor leaves
+// every sign, and so the count, as it is.
+__device__ __forceinline__ int sturm_below_long(const float* al, const float* be, int m, float sc, float x) {
+  float p0 = 1.f, p1 = al[0] * sc - x;
+  int changes = p1 < 0.f ? 1 : 0;
+  for (int i = 1; i < m; ++i) {
+    const float b = be[i - 1] * sc;
+    float p2 = (al[i] * sc - x) * p1 - b * b * p0;
+    changes += ((p2 < 0.f) != (p1 < 0.f)) ? 1 : 0;
+    const float big = fmaxf(fabsf(p1), fabsf(p2));
+    const float f = big < 0x1p-64f ? 0x1p64f : (big > 0x1p64f ? 0x1p-64f : 1.f);
+    p0 = p1 * f;
+    p1 = p2 * f;
   }
   return changes;
 }
@@ -598,6 +623,89 @@ __device__ __forceinline__ bool ritz_step(const float* al_s, const float* be_s, 
       load_vec<NT>(basis[i], c, b);
 #pragma unroll
       for (int tj = 0; tj < NT; ++tj) x[tj] += sv[i] * b[tj];
+    }
+  }
+  return conv;
+}
+
+// ritz_step for m > 8 steps, with the tridiagonal (al_s, be_s) and the
+// vectors of the inverse iteration (sv, cp, bp: kLanczosK floats each, this
+// wave's) kept in LDS and loops left rolled, so that the long, rarely taken
+// checks hold no registers beside A. Every lane computes the same values;
+// the LDS writes of those values race only with themselves.
+template <int D>
+__device__ __forceinline__ bool ritz_step_long(const float* al_s, const float* be_s, int m, float* sv, float* cp,
+                                               float* bp, const float (*basis)[D], int l, int c, bool form,
+                                               float (&x)[D / 16]) {
+  constexpr int NT = D / 16;
+  float lo = 0.f, hi = 0.f;
+  for (int i = 0; i < m; ++i) {
+    const float rr = (i > 0 ? fabsf(be_s[i - 1]) : 0.f) + (i < m - 1 ? fabsf(be_s[i]) : 0.f);
+    lo = i == 0 ? al_s[0] - rr : fminf(lo, al_s[i] - rr);
+    hi = i == 0 ? al_s[0] + rr : fmaxf(hi, al_s[i] + rr);
+  }
+  const float scale = fmaxf(fabsf(lo), fabsf(hi));
+  if (!(scale > 0.f)) {
+    load_vec<NT>(basis[0], c, x);
+    return true;
+  }
+  const float sc = 1.f / scale;
+  auto section = [&](int q, int rounds, float& a, float& b) {
+    for (int rd = 0; rd < rounds; ++rd) {
+      const float step = (b - a) * (1.f / 65.f);
+      const float xx = a + step * static_cast<float>(l + 1);
+      const bool above = m - sturm_below_long(al_s, be_s, m, sc, xx) >= q;
+      const int cnt = __builtin_popcountll(__ballot(above));
+      const float na = cnt > 0 ? a + step * static_cast<float>(cnt) : a;
+      const float nb = cnt < 64 ? a + step * static_cast<float>(cnt + 1) : b;
+      a = na;
+      b = nb;
+    }
+  };
+  float lo1 = lo * sc, hi1 = hi * sc;
+  section(1, 4, lo1, hi1);
+  float lo2 = lo * sc, hi2 = hi1;
+  section(2, 2, lo2, hi2);
+  const float theta = 0.5f * (lo1 + hi1);
+  const float mu = hi1 + fmaxf(fabsf(theta) * 1e-6f, 1e-30f);
+  for (int i = 0; i < m; ++i) sv[i] = 1.f;
+  for (int pass = 0; pass < 2; ++pass) {
+    float rden = __builtin_amdgcn_rcpf(fmaxf(mu - al_s[0] * sc, 1e-30f));
+    float cprev = -be_s[0] * sc * rden, bprev = sv[0] * rden;
+    cp[0] = cprev;
+    bp[0] = bprev;
+    for (int i = 1; i < m; ++i) {
+      const float bi1 = be_s[i - 1] * sc;
+      rden = __builtin_amdgcn_rcpf(fmaxf((mu - al_s[i] * sc) + bi1 * cprev, 1e-30f));
+      cprev = -be_s[i] * sc * rden;
+      bprev = (sv[i] + bi1 * bprev) * rden;
+      cp[i] = cprev;
+      bp[i] = bprev;
+    }
+    float nxt = bp[m - 1];
+    sv[m - 1] = nxt;
+    float n = nxt * nxt;
+    for (int i = m - 2; i >= 0; --i) {
+      nxt = bp[i] - cp[i] * nxt;
+      sv[i] = nxt;
+      n += nxt * nxt;
+    }
+    const float inv = __builtin_amdgcn_rsqf(n);
+    for (int i = 0; i < m; ++i) sv[i] *= inv;
+  }
+  const float res = fabsf(be_s[m - 1] * sc * sv[m - 1]);
+  const float gap = theta - hi2;
+  const bool conv = res == 0.f || (gap > 0.f && theta > 0.f &&
+                                   static_cast<double>(res) * res < kLanczosTol * gap * theta);
+  if (conv || form) {
+#pragma unroll
+    for (int tj = 0; tj < NT; ++tj) x[tj] = 0.f;
+    for (int i = 0; i < m; ++i) {
+      float b[NT];
+      load_vec<NT>(basis[i], c, b);
+      const float si = sv[i];
+#pragma unroll
+      for (int tj = 0; tj < NT; ++tj) x[tj] += si * b[tj];
     }
   }
   return conv;
@@ -723,9 +831,10 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2)
     }
     float beta_prev = 0.f;
     if (g == 0) store_vec<NT>(basis[0], c, v);
-    // three-term recurrence: within kLanczosK steps the basis stays
-    // orthogonal enough for the top Ritz pair (the Ritz value is then
-    // re-evaluated from A itself)
+    // three-term recurrence with no reorthogonalisation: once the top Ritz
+    // pair converges the basis loses orthogonality (copies of it appear in
+    // the tridiagonal, the gap test then fails and the cycle ends with a
+    // restart from the Ritz vector), and M_j is re-evaluated from A itself
     for (int k = 0; k < kLanczosK; ++k) {
       float z[NT];
       {
@@ -757,7 +866,12 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2)
           case 5: conv = ritz_step<5, D>(s.al[w], s.be[w], basis, l, c, false, x); break;
           case 6: conv = ritz_step<6, D>(s.al[w], s.be[w], basis, l, c, false, x); break;
           case 7: conv = ritz_step<7, D>(s.al[w], s.be[w], basis, l, c, false, x); break;
-          default: conv = ritz_step<kLanczosK, D>(s.al[w], s.be[w], basis, l, c, true, x); break;
+          case 8: conv = ritz_step<8, D>(s.al[w], s.be[w], basis, l, c, false, x); break;
+          case 10: case 12: case 14: case 16: case 20: case kLanczosK:
+            conv = ritz_step_long<D>(s.al[w], s.be[w], k + 1, s.rz[w][0], s.rz[w][1], s.rz[w][2], basis, l, c,
+                                     k + 1 == kLanczosK, x);
+            break;
+          default: conv = false; break;
         }
         if (conv) {
           done = true;
