@@ -347,12 +347,12 @@ __global__ __launch_bounds__(256) void k_hbar_reduce(const float* __restrict__ w
 //   * Vectors: fp32, lane l holds entries 16 tj + c (tj < D / 16); dot
 //     products are 16-lane DPP sums.
 //   * Three-term recurrence (the basis is kept in LDS only to form the Ritz
-//     vector). After steps 5, 6, 7 and 8, then every second step to 16, then
-//     after 20 and 24, the Ritz pair of the tridiagonal is computed (64-point
-//     Sturm multisection across the lanes, then inverse iteration); the block
-//     stops when the residual bound res^2 / (gap * theta) < kLanczosTol,
-//     otherwise the process restarts from the Ritz vector after kLanczosK
-//     steps. Almost every block of the video workloads stops within 8 steps;
+//     vector). After steps 5, 6, 7 and 8, then at steps predicted from the
+//     decay of the residual bound between the last two checks, the Ritz pair
+//     of the tridiagonal is computed (64-point Sturm multisection across the
+//     lanes, then inverse iteration); the block stops when the residual
+//     bound res^2 / (gap * theta) < kLanczosTol, otherwise the process
+//     restarts from the Ritz vector after kLanczosK steps. Almost every block of the video workloads stops within 8 steps;
 //     the long cycle is for blocks of i.i.d. keys (the text tokens of the
 //     image shape: sigma_2 / sigma_1 about 0.9-0.99), which restarted every 8
 //     steps needed up to 37 and with 24-step cycles about 20.
@@ -551,7 +551,7 @@ __device__ __forceinline__ void multisect(const float (&al)[m], const float (&be
 // iteration just above the top eigenvalue.
 template <int m, int D>
 __device__ __forceinline__ bool ritz_step(const float* al_s, const float* be_s, const float (*basis)[D], int l,
-                                          int c, bool form, float (&x)[D / 16]) {
+                                          int c, bool form, float (&x)[D / 16], float& need) {
   constexpr int NT = D / 16;
   float al[m], be[m];
   float lo = 0.f, hi = 0.f;
@@ -614,6 +614,8 @@ __device__ __forceinline__ bool ritz_step(const float* al_s, const float* be_s, 
   const float gap = theta - hi2;
   const bool conv = res == 0.f || (gap > 0.f && theta > 0.f &&
                                    static_cast<double>(res) * res < kLanczosTol * gap * theta);
+  need = gap > 0.f && theta > 0.f ? static_cast<float>(static_cast<double>(res) * res / (kLanczosTol * gap * theta))
+                                  : INFINITY;
   if (conv || form) {
 #pragma unroll
     for (int tj = 0; tj < NT; ++tj) x[tj] = 0.f;
@@ -636,7 +638,7 @@ __device__ __forceinline__ bool ritz_step(const float* al_s, const float* be_s, 
 template <int D>
 __device__ __forceinline__ bool ritz_step_long(const float* al_s, const float* be_s, int m, float* sv, float* cp,
                                                float* bp, const float (*basis)[D], int l, int c, bool form,
-                                               float (&x)[D / 16]) {
+                                               float (&x)[D / 16], float& need) {
   constexpr int NT = D / 16;
   float lo = 0.f, hi = 0.f;
   for (int i = 0; i < m; ++i) {
@@ -697,6 +699,8 @@ __device__ __forceinline__ bool ritz_step_long(const float* al_s, const float* b
   const float gap = theta - hi2;
   const bool conv = res == 0.f || (gap > 0.f && theta > 0.f &&
                                    static_cast<double>(res) * res < kLanczosTol * gap * theta);
+  need = gap > 0.f && theta > 0.f ? static_cast<float>(static_cast<double>(res) * res / (kLanczosTol * gap * theta))
+                                  : INFINITY;
   if (conv || form) {
 #pragma unroll
     for (int tj = 0; tj < NT; ++tj) x[tj] = 0.f;
@@ -830,6 +834,8 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2)
       }
     }
     float beta_prev = 0.f;
+    int next = kLanczosCheck, m_prev = 0;  // the step of the next convergence check, and of the last one
+    float need_prev = 0.f;
     if (g == 0) store_vec<NT>(basis[0], c, v);
     // three-term recurrence with no reorthogonalisation: once the top Ritz
     // pair converges the basis loses orthogonality (copies of it appear in
@@ -860,23 +866,40 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2)
         s.al[w][k] = alpha;
         s.be[w][k] = beta;
       }
-      if (k + 1 >= kLanczosCheck) {
+      const int m = k + 1;
+      if (m == next) {
         bool conv;
-        switch (k + 1) {
-          case 5: conv = ritz_step<5, D>(s.al[w], s.be[w], basis, l, c, false, x); break;
-          case 6: conv = ritz_step<6, D>(s.al[w], s.be[w], basis, l, c, false, x); break;
-          case 7: conv = ritz_step<7, D>(s.al[w], s.be[w], basis, l, c, false, x); break;
-          case 8: conv = ritz_step<8, D>(s.al[w], s.be[w], basis, l, c, false, x); break;
-          case 10: case 12: case 14: case 16: case 20: case kLanczosK:
-            conv = ritz_step_long<D>(s.al[w], s.be[w], k + 1, s.rz[w][0], s.rz[w][1], s.rz[w][2], basis, l, c,
-                                     k + 1 == kLanczosK, x);
+        float need;
+        switch (m) {
+          case 5: conv = ritz_step<5, D>(s.al[w], s.be[w], basis, l, c, false, x, need); break;
+          case 6: conv = ritz_step<6, D>(s.al[w], s.be[w], basis, l, c, false, x, need); break;
+          case 7: conv = ritz_step<7, D>(s.al[w], s.be[w], basis, l, c, false, x, need); break;
+          case 8: conv = ritz_step<8, D>(s.al[w], s.be[w], basis, l, c, false, x, need); break;
+          default:
+            conv = ritz_step_long<D>(s.al[w], s.be[w], m, s.rz[w][0], s.rz[w][1], s.rz[w][2], basis, l, c,
+                                     m == kLanczosK, x, need);
             break;
-          default: conv = false; break;
         }
         if (conv) {
           done = true;
           break;
         }
+        // next check: after every step to 8; then where the decay of the
+        // residual bound since the last check (need falls geometrically with
+        // the steps) predicts need < 1, at most 8 steps on, 4 without a
+        // usable rate. need is the same value in both waves (computed from
+        // the same tridiagonal), so both keep the same schedule.
+        int ahead = 1;
+        if (m >= 8) {
+          ahead = 4;
+          if (m_prev > 0 && need < INFINITY && need_prev > need) {
+            const float rate = (__log2f(need_prev) - __log2f(need)) / static_cast<float>(m - m_prev);
+            ahead = min(8, max(1, static_cast<int>(ceilf(__log2f(need) / rate))));
+          }
+        }
+        next = min(m + ahead, kLanczosK);
+        need_prev = need;
+        m_prev = m;
       }
     }
   }
