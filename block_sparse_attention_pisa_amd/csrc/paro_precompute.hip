@@ -941,8 +941,14 @@ int stats_chunks(const paro_problem& p, int* G) {
   const int bh = p.B * p.H;
   // about 1024 workgroups in all, rounded down: two full rounds of the 512
   // that fit at once (256 CUs x 2), rather than two and a sliver whose
-  // workgroups each walk a whole chunk alone
-  int nchunk = max(1, min(T, 1024 / bh));
+  // workgroups each walk a whole chunk alone. For bf16, chunks of at least
+  // 8 blocks: every chunk writes a D x D partial sum (64 KB at d = 128) that
+  // k_hbar_reduce reads back, which for chunks of 2 blocks (the image shape)
+  // is as much traffic as K and V themselves (precompute 0.163 -> 0.152 ms
+  // there, 0.227 -> 0.214 ms at 480p; the fp32 path's per-block staging is
+  // slower, so it keeps the finer split).
+  const int gmin = sizeof(E) == 2 ? 8 : 1;
+  int nchunk = max(1, min(T / gmin, 1024 / bh));
   *G = ceil_div(T, nchunk);
   return ceil_div(T, *G);
 }
@@ -982,7 +988,7 @@ hipError_t launch_typed(const paro_problem& p, const E* K, const E* V, float* kb
 
 size_t precompute_workspace_bytes(const paro_problem& p) {
   int G = 1;
-  const int nchunk = stats_chunks<float, 64>(p, &G);
+  const int nchunk = p.dtype == PARO_DTYPE_BF16 ? stats_chunks<uint16_t, 64>(p, &G) : stats_chunks<float, 64>(p, &G);
   // per (b, h): nchunk partial H sums, then Hbar in PairA order
   return static_cast<size_t>(p.B) * p.H * (nchunk + 1) * p.d * p.d * sizeof(float);
 }
