@@ -763,21 +763,54 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int t = threadIdx.x, w = t / 64, l = t % 64, g = l / 16, c = l % 16;
   const int row0 = j * kBlock, nvalid = min(kBlock, L - row0);
 
-  // A starts as -Hbar (this lane's entries, 16-byte loads of the permuted copy)
+  // A starts as -Hbar (this lane's entries, 16-byte loads of the permuted
+  // copy). For bf16 all the K_j and V_j staging items and kbar_j, vsum_j are
+  // in flight before the first is waited on (instead of one round trip per
+  // staging item), and the Hbar loads (from L2) follow the LDS writes that
+  // free the staging registers.
   PairA<D> A;
-  {
-    const f32x4* hp = reinterpret_cast<const f32x4*>(hperm + static_cast<size_t>(bh) * D * D) + (w * 64 + l) * MT * NT;
+  const f32x4* hp = reinterpret_cast<const f32x4*>(hperm + static_cast<size_t>(bh) * D * D) + (w * 64 + l) * MT * NT;
+  const E* Kh = K + static_cast<size_t>(bh) * L * D;
+  const E* Vh = V + static_cast<size_t>(bh) * L * D;
+  const size_t o_kv = (static_cast<size_t>(bh) * T + j) * D + t;
+  if constexpr (sizeof(E) == 2) {
+    constexpr int IPT = 2 * D / kPairThreads;  // staging items per thread
+    static_assert(2 * D % kPairThreads == 0, "staging items per thread");
+    uint4 rk[IPT][4], rv[IPT][4];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      load_item<D>(Kh, row0, nvalid, t + kPairThreads * i, rk[i]);
+      load_item<D>(Vh, row0, nvalid, t + kPairThreads * i, rv[i]);
+    }
+    float kb = 0.f, vs = 0.f;
+    if (t < D) {
+      kb = kbar[o_kv];
+      vs = vsum[o_kv];
+    }
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      store_item(s.u.tile.kt, t + kPairThreads * i, rk[i]);
+      store_item(s.u.tile.vt, t + kPairThreads * i, rv[i]);
+    }
+    if (t < D) {
+      s.kbar[t] = kb;
+      s.vsum[t] = vs;
+    }
 #pragma unroll
     for (int ti = 0; ti < MT; ++ti)
 #pragma unroll
       for (int tj = 0; tj < NT; ++tj) A.v[ti][tj] = -hp[ti * NT + tj];
-  }
-  stage_transposed<D, kPairThreads>(K + static_cast<size_t>(bh) * L * D, row0, nvalid, s.u.tile.kt);
-  stage_transposed<D, kPairThreads>(V + static_cast<size_t>(bh) * L * D, row0, nvalid, s.u.tile.vt);
-  if (t < D) {
-    const size_t o = (static_cast<size_t>(bh) * T + j) * D + t;
-    s.kbar[t] = kbar[o];
-    s.vsum[t] = vsum[o];
+  } else {
+#pragma unroll
+    for (int ti = 0; ti < MT; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < NT; ++tj) A.v[ti][tj] = -hp[ti * NT + tj];
+    stage_transposed<D, kPairThreads>(Kh, row0, nvalid, s.u.tile.kt);
+    stage_transposed<D, kPairThreads>(Vh, row0, nvalid, s.u.tile.vt);
+    if (t < D) {
+      s.kbar[t] = kbar[o_kv];
+      s.vsum[t] = vsum[o_kv];
+    }
   }
   __syncthreads();
   // A = K_j^T V_j - kbar_j^T vsum_j - Hbar
