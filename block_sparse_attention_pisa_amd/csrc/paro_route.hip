@@ -220,6 +220,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(route_
       }
     }
   }
+  // lambda M_j of the keys each lane holds in registers (blocks 64 i + l):
+  // the same for every row of the group, so loaded once per wave, and here,
+  // where their latency hides behind the barrier that ends the dots
+  double lm[NI];
+  if constexpr (kMode != kRouteWeights) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) lm[i] = 64 * i + l < T ? lambda * Mh[64 * i + l] : 0.0;
+  }
   __syncthreads();
 
   // 3. selection, one wave per row
@@ -280,7 +288,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(route_
       const int j = 64 * i + l;
       key[i] = 0;
       if (j < T) {
-        const double s = score_at(j);
+        const double s = scale * static_cast<double>(dr[j]) + lm[i];  // = score_at(j)
         key[i] = score_key(s);
         smin = fmin(smin, s);
         smax = fmax(smax, s);
