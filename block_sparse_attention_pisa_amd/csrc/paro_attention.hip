@@ -46,6 +46,7 @@
 // fp32 kernel (k_attn_f32): the same three stages in plain fp32 arithmetic,
 // one key at a time; used for fp32 problems.
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "paro_common.h"
@@ -622,9 +623,17 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   int* sh = reinterpret_cast<int*>(ubits + kQB * nw);                               // nu, rerun flags
   uint16_t* ulist = reinterpret_cast<uint16_t*>(sh + 12);                           // [T]
 
-  // XCD-aware order: consecutive workgroup ids go to different XCDs, so hand
-  // each XCD a contiguous run of (head, query-block group) items.
-  int wg = blockIdx.x;
+  // bf16 is persistent: the grid (a multiple of 8 workgroups, at most one
+  // per CU) walks the nwg (head, query-block group) items, workgroup b taking
+  // items b, b + gridDim.x, ..., so a CU moves from one item straight to the
+  // next (no workgroup launch between them) and an item's set-up overlaps
+  // the previous item's last stores. fp8 keeps one workgroup per item (the
+  // loop is left after one pass; as a loop the fp8 tile spills more). XCD-
+  // aware order: consecutive item ids go to different XCDs (item % 8 = b % 8
+  // for a grid that is a multiple of 8), so hand each XCD a contiguous run
+  // of items.
+  for (int item = blockIdx.x; item < nwg; item += gridDim.x) {
+  int wg = item;
   const int n8 = (nwg / 8) * 8;
   if (wg < n8) wg = (wg % 8) * (nwg / 8) + wg / 8;
   const int ngrp = ceil_div(T, kQB);
@@ -1048,6 +1057,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       }
     }
   }
+  if constexpr (F8) break;
+  lds_barrier();  // every wave is done with this item's LDS before the next item writes it
+  }
 }
 
 // ------------------------------------------------------------------ fp32
@@ -1167,6 +1179,23 @@ __host__ inline WsLayout ws_layout(const paro_problem& p, bool fp8) {
   return w;
 }
 
+// Workgroups of the persistent attention grid: one per CU of the current
+// device (its LDS holds one), rounded down to a multiple of 8 so that every
+// workgroup stays on one XCD's run of items; looked up once per device.
+int persistent_workgroups() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) cus = 256;
+    n = cus / 8 * 8;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int D, bool F8>
 hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, const void* V, const float* kbar,
                        const float* vsum, const float* Hbar, const int32_t* idx, int keep_k, void* O, int mode,
@@ -1200,7 +1229,8 @@ hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, cons
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_al));
   if (e != hipSuccess) return e;
   const int nwg = ceil_div(T, kQB) * p.B * p.H;
-  hipLaunchKernelGGL((k_attn_bf16<D, F8>), dim3(nwg), dim3(kAttnThreads), lds_al, s,
+  const int grid = F8 ? nwg : std::min(nwg, persistent_workgroups());
+  hipLaunchKernelGGL((k_attn_bf16<D, F8>), dim3(grid), dim3(kAttnThreads), lds_al, s,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), kb16, vs16, Hbar, idx, static_cast<uint16_t*>(O), p.L, T,
                      keep_k, static_cast<float>(p.scale), nwg, mode, k8, ke, kb8, kbe, offs);
