@@ -65,6 +65,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kQB = 4;                    // query blocks per workgroup
 constexpr int kWaves = 2 * kQB;           // two 32-row waves per query block
 constexpr int kAttnThreads = 64 * kWaves;
+constexpr int kQueueStride = 16;          // ints between the item queues' counters (64 bytes)
+constexpr int kQueueInts = 8 * kQueueStride;
 // tail modes (the PARO_TAIL_* codes of the ABI; 2 = zeroth order only: tail on, correction off)
 constexpr int kModePisa = 0, kModeDrop = 1;
 
@@ -226,11 +228,13 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-// kbar and vsum (fp32 [BH][T][D]) rounded to bf16 for the matrix cores.
+// kbar and vsum (fp32 [BH][T][D]) rounded to bf16 for the matrix cores; also
+// clears the item queues of the attention launch that follows (when given).
 __global__ __launch_bounds__(256) void k_centroids_bf16(const float* __restrict__ kbar, const float* __restrict__ vsum,
                                                         uint16_t* __restrict__ kb16, uint16_t* __restrict__ vs16,
-                                                        size_t n8) {
+                                                        size_t n8, int* __restrict__ queues) {
   const size_t e = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (queues && e < kQueueInts) queues[e] = 0;
   if (e >= n8) return;
   const float4* v4 = reinterpret_cast<const float4*>(vsum) + 2 * e;
   reinterpret_cast<uint4*>(vs16)[e] = to_bf16x8(v4[0], v4[1]);
@@ -612,7 +616,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     const uint16_t* __restrict__ kb16, const uint16_t* __restrict__ vs16, const float* __restrict__ Hbar,
     const int32_t* __restrict__ idx, uint16_t* __restrict__ O, int L, int T, int keep_k, float scale, int nwg,
     int mode, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ ke, const uint8_t* __restrict__ kb8,
-    const uint8_t* __restrict__ kbe, const int32_t* __restrict__ offs) {
+    const uint8_t* __restrict__ kbe, const int32_t* __restrict__ offs, int* __restrict__ queues) {
   const bool tail = mode != kModeDrop, corr = mode == kModePisa;
   constexpr int BUF = Geo<D, F8>::BUF, KS = Geo<D>::KS, KSB = Geo<D>::KSB, VSR = Geo<D>::VSR, HS = Geo<D>::HS;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -620,22 +624,65 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   const int nw = ceil_div(T, 32);
   uint32_t* masks = reinterpret_cast<uint32_t*>(smem + sizeof(uint16_t) * 2 * BUF);  // [kQB][nw]
   uint32_t* ubits = masks + kQB * nw;  // [kQB][nw]: bit e = union tile e belongs to S_i of q-block qi
-  int* sh = reinterpret_cast<int*>(ubits + kQB * nw);                               // nu, rerun flags
+  int* sh = reinterpret_cast<int*>(ubits + kQB * nw);  // nu, rerun flags, next item (10)
   uint16_t* ulist = reinterpret_cast<uint16_t*>(sh + 12);                           // [T]
 
-  // bf16 is persistent: the grid (a multiple of 8 workgroups, at most one
-  // per CU) walks the nwg (head, query-block group) items, workgroup b taking
-  // items b, b + gridDim.x, ..., so a CU moves from one item straight to the
-  // next (no workgroup launch between them) and an item's set-up overlaps
-  // the previous item's last stores. fp8 keeps one workgroup per item (the
-  // loop is left after one pass; as a loop the fp8 tile spills more). XCD-
-  // aware order: consecutive item ids go to different XCDs (item % 8 = b % 8
-  // for a grid that is a multiple of 8), so hand each XCD a contiguous run
-  // of items.
-  for (int item = blockIdx.x; item < nwg; item += gridDim.x) {
-  int wg = item;
-  const int n8 = (nwg / 8) * 8;
-  if (wg < n8) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  // bf16 is persistent: the grid (at most one workgroup per CU) takes the
+  // nwg (head, query-block group) items from 8 queues, so a CU moves from
+  // one item straight to the next (no workgroup launch between them) and an
+  // item's set-up overlaps the previous item's last stores. Workgroups go to
+  // the XCDs round robin (b % 8), and queue x holds a contiguous run of
+  // items (whole heads), served in order to the workgroups b % 8 = x: the
+  // items in flight on one XCD stay neighbours, whose exact lists share most
+  // key blocks in that XCD's L2, however unevenly the items run. The first
+  // gridDim.x / 8 items of each queue are handed out by position (workgroup
+  // 8 i + x takes item i of queue x), the rest by an atomic counter per
+  // queue; a workgroup whose queue is empty serves the others. The next
+  // item is claimed during the current one (stage 3) and passed on in LDS.
+  // fp8 keeps one workgroup per item (the loop is left after one pass; as a
+  // loop the fp8 tile spills more), in the same XCD-aware order.
+  const int per_q = nwg / 8, g8 = static_cast<int>(gridDim.x) / 8;
+  auto queue_len = [&](int x) { return per_q + (x < nwg - 8 * per_q ? 1 : 0); };
+  auto queue_item = [&](int x, int i) { return i < per_q ? x * per_q + i : 8 * per_q + x; };
+  int* const own_queue = queues + kQueueStride * (blockIdx.x & 7);
+  // the claimed item, given this workgroup's take from its own queue. Once
+  // that queue is empty the other seven counters are read together (one
+  // round trip, however many are empty) and the first queue seen with items
+  // left is taken from; a take that lost the race for its last item reads
+  // again. Counters only grow, so each pass that fails has seen a queue run
+  // empty, and after at most 8 passes every queue reads empty.
+  auto claim = [&](int own) -> int {
+    const int x0 = blockIdx.x & 7;
+    if (g8 + own < queue_len(x0)) return queue_item(x0, g8 + own);
+    for (;;) {
+      int seen[7];
+#pragma unroll
+      for (int t = 0; t < 7; ++t)
+        seen[t] = __hip_atomic_load(queues + kQueueStride * ((x0 + 1 + t) & 7), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+      int x = -1;
+#pragma unroll
+      for (int t = 6; t >= 0; --t)
+        if (g8 + seen[t] < queue_len((x0 + 1 + t) & 7)) x = (x0 + 1 + t) & 7;
+      if (x < 0) return -1;
+      const int i = g8 + atomicAdd(queues + kQueueStride * x, 1);
+      if (i < queue_len(x)) return queue_item(x, i);
+    }
+  };
+  int wg = blockIdx.x;
+  if constexpr (F8) {
+    if (wg < 8 * per_q) wg = (wg % 8) * per_q + wg / 8;
+  } else {
+    const int x0 = wg & 7, i0 = wg >> 3;
+    if (wg < 8 * g8 && i0 < queue_len(x0)) {
+      wg = queue_item(x0, i0);
+    } else {
+      if (threadIdx.x == 0) sh[10] = claim(atomicAdd(own_queue, 1));
+      lds_barrier();
+      wg = sh[10];
+    }
+  }
+  for (; wg >= 0;) {
   const int ngrp = ceil_div(T, kQB);
   const int grp = wg % ngrp, bh = wg / ngrp;
 
@@ -1012,6 +1059,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   asm volatile("" : "+v"(t3));
   const int g3 = (t3 >> 5) & 1, ql3 = t3 & 31;
   const int row3 = (grp * kQB + (t3 >> 7)) * 64 + 32 * ((t3 >> 6) & 1) + ql3;
+  // the next item: the take from the own queue is issued here and returns
+  // ahead of the Hbar loads below (memory returns in order), so waiting for
+  // those loads covers it; every wave read the slot sh[10] before this
+  // item's first barrier. (The address goes through an opaque zero so the
+  // compiler's wave aggregation of atomics, which reads the result back at
+  // once, leaves this one alone.)
+  int own = 0;
+  if constexpr (!F8) {
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    if (t3 == 0) own = atomicAdd(own_queue + z, 1);
+  }
   if (nch > 0 && corr) {
     // Hbar^T in bf16: ht[v][k] = Hbar[k][v], rows padded to HS
     const float* Hh = Hbar + static_cast<size_t>(bh) * D * D;
@@ -1032,6 +1091,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     }
     lds_barrier();
   }
+  if constexpr (!F8)
+    if (t3 == 0) sh[10] = claim(own);
   // MFMAs need the whole wave: only the stores are guarded per lane.
   if (qvalid) {
     const uint16_t* hrow = buf + ql3 * HS + 8 * g3;
@@ -1059,6 +1120,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   }
   if constexpr (F8) break;
   lds_barrier();  // every wave is done with this item's LDS before the next item writes it
+  wg = sh[10];
   }
 }
 
@@ -1154,11 +1216,12 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
 }
 
 // Workspace of the bf16 problems (byte offsets, each region 256-byte aligned).
-// bf16 path: [kb16 | vs16], kbar and vsum in bf16, each [B H][T][D].
+// bf16 path: [kb16 | vs16 | queues], kbar and vsum in bf16, each [B H][T][D],
+// and the 8 item-queue counters of the persistent grid (kQueueInts ints).
 // fp8 path: [k8 | ke | kb8 | kbe | vs16]: K in e4m3 [B H][L][D] and its row
 // scale codes [B H][L], kbar likewise ([B H][T][D], [B H][T]), vsum in bf16.
 struct WsLayout {
-  size_t k8, ke, kb8, kbe, vs16, kb16, total;
+  size_t k8, ke, kb8, kbe, vs16, kb16, queues, total;
 };
 __host__ inline size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 __host__ inline WsLayout ws_layout(const paro_problem& p, bool fp8) {
@@ -1174,7 +1237,8 @@ __host__ inline WsLayout ws_layout(const paro_problem& p, bool fp8) {
   } else {
     w.kb16 = 0;
     w.vs16 = up256(bh * T * d * 2);
-    w.total = w.vs16 + up256(bh * T * d * 2);
+    w.queues = w.vs16 + up256(bh * T * d * 2);
+    w.total = w.queues + up256(sizeof(int) * kQueueInts);
   }
   return w;
 }
@@ -1207,9 +1271,10 @@ hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, cons
   unsigned char* wb = static_cast<unsigned char*>(ws);
   uint16_t* kb16 = F8 ? nullptr : reinterpret_cast<uint16_t*>(wb + lay.kb16);
   uint16_t* vs16 = reinterpret_cast<uint16_t*>(wb + lay.vs16);
+  int* queues = F8 ? nullptr : reinterpret_cast<int*>(wb + lay.queues);
   uint8_t *k8 = nullptr, *ke = nullptr, *kb8 = nullptr, *kbe = nullptr;
   hipLaunchKernelGGL(k_centroids_bf16, dim3(static_cast<unsigned>((n / 8 + 255) / 256)), dim3(256), 0, s, kbar, vsum,
-                     kb16, vs16, n / 8);
+                     kb16, vs16, n / 8, queues);
   if (F8) {
     k8 = wb + lay.k8;
     ke = wb + lay.ke;
@@ -1233,7 +1298,7 @@ hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, cons
   hipLaunchKernelGGL((k_attn_bf16<D, F8>), dim3(grid), dim3(kAttnThreads), lds_al, s,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), kb16, vs16, Hbar, idx, static_cast<uint16_t*>(O), p.L, T,
-                     keep_k, static_cast<float>(p.scale), nwg, mode, k8, ke, kb8, kbe, offs);
+                     keep_k, static_cast<float>(p.scale), nwg, mode, k8, ke, kb8, kbe, offs, queues);
   return hipGetLastError();
 }
 

@@ -108,7 +108,7 @@ def test_pointer_and_argument_validation():
     assert L.paro_route(pp, FAKE, FAKE, FAKE, 2, 0.1, None, None) == -1
     assert L.paro_route(pp, FAKE, FAKE + 4, FAKE, 2, 0.1, FAKE, None) == -4
     wa = L.paro_attention_workspace_bytes(pp)
-    assert wa == 2 * 1 * 2 * T * 128 * 2   # bf16 copies of kbar and vsum
+    assert wa == 2 * 1 * 2 * T * 128 * 2 + 512   # bf16 copies of kbar and vsum, 8 item-queue counters
     assert L.paro_attention_workspace_bytes(ctypes.byref(_p(dtype=1))) == 0
     assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 2, FAKE, FAKE, wa, None) == -1
     assert L.paro_attention(pp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T + 1, FAKE, FAKE, wa, None) == -2
