@@ -135,9 +135,11 @@ int paro_route(const paro_problem* p, const void* Q, const float* kbar, const do
  *      0 <= keep_k <= T.
  * out: O [B, H, L, d] (dtype; rows >= L of the last block are not written).
  * workspace: device scratch of at least paro_attention_workspace_bytes(p)
- *            bytes (bf16 copies of kbar and vsum for the matrix cores; 0
- *            bytes, so NULL is allowed, for fp32 problems); contents on entry
- *            are ignored and undefined on return.
+ *            bytes (bf16 copies of kbar and vsum for the matrix cores and
+ *            512 bytes of work-queue counters; 0 bytes, so NULL is allowed,
+ *            for fp32 problems); contents on entry are ignored and undefined
+ *            on return. Two calls that run at once must not share one
+ *            workspace.
  * bf16 problems use bf16 MFMA products with fp32 accumulation (tail
  * centroids, value sums and Hbar rounded to bf16 for the matrix cores);
  * fp32 problems use fp32 arithmetic throughout. An idx row that breaks the
@@ -178,9 +180,10 @@ int paro_attention_mode(const paro_problem* p, const void* Q, const void* K, con
  * paro_attention_noalloc - paro_attention_mode for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): the workspace of paro_attention_mode
- * (the bf16 copies of kbar and vsum) lives in a static device array of
- * PARO_NOALLOC_SCRATCH_BYTES bytes inside the library instead of a caller
- * buffer. Nothing is allocated or freed by the call.
+ * (the bf16 copies of kbar and vsum, the work-queue counters) lives in a
+ * static device array of PARO_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library instead of a caller buffer. Nothing is allocated or freed by the
+ * call.
  *   - Same arguments, results and errors as paro_attention_mode, minus the
  *     workspace. A problem whose paro_attention_workspace_bytes() exceeds
  *     PARO_NOALLOC_SCRATCH_BYTES returns PARO_ERR_WORKSPACE (the 720p video
