@@ -70,31 +70,58 @@ constexpr int kQueueInts = 8 * kQueueStride;
 // tail modes (the PARO_TAIL_* codes of the ABI; 2 = zeroth order only: tail on, correction off)
 constexpr int kModePisa = 0, kModeDrop = 1;
 
-// Tile geometry. F8: K (and the centroid keys) are staged as fp8 e4m3 rows
-// of D bytes plus one power-of-two (E8M0) scale byte per row; V stays bf16.
+// Tile geometry.
+// bf16: a staged tile (64 K rows, then 64 V rows) lives in LDS as 1 KB
+// regions, each filled by one wave-wide direct global-to-LDS load (lane i
+// writes bytes 16 i .. 16 i + 16 of the region): region r of the K (V) part
+// holds tile rows r, r + NREG, r + 2 NREG, ... as whole rows of 2 D bytes, so
+// every such load reads RR complete rows of the tensor. Regions are KREG
+// (VREG) bytes apart; the 16 (64) bytes beyond the 1 KB shift each region's
+// LDS banks, so that the K operand reads of 16 consecutive rows (one 16-lane
+// group of ds_read_b128, same dims) fall in 16 regions on 16 different bank
+// quads, and the transposing V reads of 4 consecutive rows (64 bytes each)
+// fall in 4 regions 64 bytes apart: no bank conflicts, and every operand
+// address is a per-lane base plus constants.
+// F8: K (and the centroid keys) are staged through registers as fp8 e4m3
+// rows of D bytes (row stride KSB) plus one power-of-two (E8M0) scale byte
+// per row; V stays bf16, row-major with row stride VSR.
 template <int D, bool F8 = false>
 struct Geo {
   static constexpr int CG = D / 8;                         // 16-byte chunks in a bf16 K row
-  static constexpr int KS = D + 24;                        // bf16 K tile row stride (elements): D dims and padding
   static constexpr int KSB = D + 16;                       // fp8 K tile row stride (bytes): D dims and padding
-  static constexpr int VSR = D + 32;                       // V tile row stride (row-major, read transposed)
+  static constexpr int VSR = D + 32;                       // fp8 path: V tile row stride (row-major, read transposed)
   static constexpr int HS = D + 8;                         // Hbar^T row stride
+  static constexpr int RR = 512 / D;                       // bf16: tile rows per 1 KB region
+  static constexpr int NREG = 64 / RR;                     // bf16: regions per 64 rows
+  static constexpr int KREG = 1024 + 16, VREG = 1024 + 64; // bf16: bytes from one region to the next
   // K tile (elements of 2 bytes); fp8: 64 rows, then the 64 row-scale bytes
-  static constexpr int KTILE = F8 ? (64 * KSB + 64) / 2 : 64 * KS;
-  static constexpr int VTILE = 64 * VSR;
+  static constexpr int KTILE = F8 ? (64 * KSB + 64) / 2 : NREG * KREG / 2;
+  static constexpr int VTILE = F8 ? 64 * VSR : NREG * VREG / 2;
   static constexpr int BUF = KTILE + VTILE;                // one staging buffer (elements)
+  static constexpr int NBUF = F8 ? 2 : 3;                  // staging buffers in LDS
+  // element offsets, from a lane's operand address, of the same dims 32 key
+  // rows on (K, bf16), and 4, 16 and 32 key rows on (V)
+  static constexpr int K32 = 32 / NREG * D;
+  static constexpr int V4 = F8 ? 4 * VSR : 4 * VREG / 2;
+  static constexpr int V16 = F8 ? 16 * VSR : 16 / NREG * D;
+  static constexpr int V32 = F8 ? 32 * VSR : 32 / NREG * D;
+  static constexpr int DMA_OPS = 2 * NREG / kWaves;       // bf16: direct loads per wave and tile
   static constexpr int NK = D / 16;                        // bf16 k-steps of S^T = K Q^T over the D dims
   static constexpr int NK8 = D / 64;                       // fp8 k-steps
   static constexpr int NU = D / 32;                        // 32-dim output tiles
-  // K items (16 bytes) staged per thread and tile; fp8: 4 D items, threads < 4 D take one each
-  static constexpr int KPT = F8 ? 1 : 64 * CG / kAttnThreads;
+  // fp8 path, staged through registers: one K item (16 bytes) for threads
+  // < 4 D, VPT V chunks per thread, the row-scale bytes in threads 0-3
   static constexpr int VPT = 64 * CG / kAttnThreads;       // V chunks staged per thread and tile
-  static constexpr int VI = KPT;                           // first V register
-  static constexpr int EI = KPT + VPT;                     // fp8: the row-scale item (threads 0-3)
-  static constexpr int NR = KPT + VPT + (F8 ? 1 : 0);      // staging registers (16 B)
-  static_assert(D * HS <= 2 * BUF, "Hbar^T must fit in the staging buffers");
+  static constexpr int VI = 1;                             // first V register
+  static constexpr int EI = 1 + VPT;                       // the row-scale item (threads 0-3)
+  static constexpr int NR = 2 + VPT;                       // staging registers (16 B)
+  static_assert(D * HS <= NBUF * BUF, "Hbar^T must fit in the staging buffers");
+  // bf16: each wave loads whole regions; a lane's V rows 8 g + k (k < 4)
+  // and those 4 rows on stay in one row of regions; +16 and +32 key rows
+  // are whole rows of regions on
+  static_assert(F8 || (NREG % kWaves == 0 && 11 % NREG + 4 < NREG && 16 % NREG == 0), "bf16 region geometry");
   static_assert(64 * CG % kAttnThreads == 0, "V items per thread");
-  static_assert(!F8 || 4 * D <= kAttnThreads, "fp8 K items per thread");
+  static_assert(4 * D <= kAttnThreads, "fp8 K items per thread");
   static_assert(KTILE % 8 == 0, "V tile alignment");
 };
 
@@ -127,87 +154,107 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// One step's data in flight, NR registers of 16 bytes per thread:
-// r[0..KPT) = K chunks; r[VI..VI+VPT) = V chunks, laid out as the K chunks
-// (8 dims of one key each, consecutive lanes on consecutive chunks of a row).
-template <int D, bool F8 = false>
-struct Stage {
-  uint4 r[Geo<D, F8>::NR];
+// fp8 path: one step's data in flight, NR registers of 16 bytes per thread:
+// r[0] = a K item (16 e4m3 bytes of a row, threads < 4 D); r[VI..VI+VPT) = V
+// chunks (8 dims of one key each, consecutive lanes on consecutive chunks of
+// a row); r[EI] = row-scale bytes (threads 0-3).
+template <int D>
+struct Stage8 {
+  uint4 r[Geo<D, true>::NR];
 };
 
-// Per-thread byte offsets of the staging loads inside a tile (constant).
-template <int D, bool F8 = false>
-struct StageOffs {
-  uint32_t k[Geo<D, F8>::KPT];  // K chunk i: row q / CG, chunk q % CG (q = tid + threads * i);
-                                // fp8: row tid / (D / 16), chunk tid % (D / 16)
-  uint32_t v[Geo<D, F8>::VPT];  // V chunk i: row q / CG, chunk q % CG (q = tid + threads * i)
+// fp8 path: per-thread byte offsets of the staging loads inside a tile (constant).
+template <int D>
+struct StageOffs8 {
+  uint32_t k;                         // fp8 K: row tid / (D / 16), 16-byte chunk tid % (D / 16)
+  uint32_t v[Geo<D, true>::VPT];      // V chunk i: row q / CG, chunk q % CG (q = tid + threads * i)
   __device__ __forceinline__ void init() {
     constexpr int CG = Geo<D>::CG;
     const int tid = threadIdx.x;
-    if (F8) {
-      k[0] = static_cast<uint32_t>((tid / (D / 16)) * D + 16 * (tid % (D / 16)));
-    } else {
+    k = static_cast<uint32_t>((tid / (D / 16)) * D + 16 * (tid % (D / 16)));
 #pragma unroll
-      for (int i = 0; i < Geo<D, F8>::KPT; ++i) {
-        const int q = tid + kAttnThreads * i;
-        k[i] = static_cast<uint32_t>((q / CG) * D * 2 + 16 * (q % CG));
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < Geo<D, F8>::VPT; ++i) {
+    for (int i = 0; i < Geo<D, true>::VPT; ++i) {
       const int q = tid + kAttnThreads * i;
       v[i] = static_cast<uint32_t>((q / CG) * D * 2 + 16 * (q % CG));
     }
   }
 };
 
-// 64 rows of keys (from kr) and values (from vr), both bf16 [rows][D] with
-// `bytes` valid bytes from the base on (uniform): an exact tile (the K and V
-// rows of kv-block j) or a centroid chunk (kbar and vsum rows of 64
-// centroids, rounded to bf16 beforehand).
-// fp8 (F8): kr holds rows of D bytes and ke one scale byte per row.
-template <int D, bool F8 = false>
-__device__ __forceinline__ void load_rows(const void* kr, const uint16_t* vr, const uint8_t* ke, int rows,
-                                          const StageOffs<D, F8>& of, Stage<D, F8>& st) {
-  constexpr int KPT = Geo<D, F8>::KPT, VI = Geo<D, F8>::VI;
-  const auto rk = make_rsrc(kr, static_cast<uint32_t>(rows * D * (F8 ? 1 : 2)));
+// fp8 path: 64 rows of e4m3 keys (kr, D bytes each, scale bytes in ke) and
+// bf16 values (vr, [rows][D]), `rows` valid rows from the base on (uniform):
+// an exact tile (the rows of kv-block j) or a centroid chunk (64 centroids).
+template <int D>
+__device__ __forceinline__ void load_rows8(const uint8_t* kr, const uint16_t* vr, const uint8_t* ke, int rows,
+                                           const StageOffs8<D>& of, Stage8<D>& st) {
+  const auto rk = make_rsrc(kr, static_cast<uint32_t>(rows * D));
   const auto rv = make_rsrc(vr, static_cast<uint32_t>(rows * D * 2));
-  if (F8) {
-    if (threadIdx.x < 4 * D) st.r[0] = bload(rk, of.k[0]);
-    // the range check of a raw buffer load is per dword, so the scale bytes'
-    // range is rounded up to whole dwords (the bytes past the last row belong
-    // to masked keys; they lie inside the caller's workspace)
-    if (threadIdx.x < 4)
-      st.r[Geo<D, F8>::EI] = bload(make_rsrc(ke, static_cast<uint32_t>((rows + 3) & ~3)), 16 * threadIdx.x);
-  } else {
+  if (threadIdx.x < 4 * D) st.r[0] = bload(rk, of.k);
+  // the range check of a raw buffer load is per dword, so the scale bytes'
+  // range is rounded up to whole dwords (the bytes past the last row belong
+  // to masked keys; they lie inside the caller's workspace)
+  if (threadIdx.x < 4)
+    st.r[Geo<D, true>::EI] = bload(make_rsrc(ke, static_cast<uint32_t>((rows + 3) & ~3)), 16 * threadIdx.x);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) st.r[i] = bload(rk, of.k[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < Geo<D, F8>::VPT; ++i) st.r[VI + i] = bload(rv, of.v[i]);
+  for (int i = 0; i < Geo<D, true>::VPT; ++i) st.r[Geo<D, true>::VI + i] = bload(rv, of.v[i]);
 }
-template <int D, bool F8 = false>
-__device__ __forceinline__ void store_exact(const Stage<D, F8>& st, uint16_t* buf) {
-  constexpr int CG = Geo<D>::CG, KPT = Geo<D, F8>::KPT, KS = Geo<D>::KS, VSR = Geo<D>::VSR, VI = Geo<D, F8>::VI;
-  uint16_t* vt = buf + Geo<D, F8>::KTILE;
-  if (F8) {
-    constexpr int KSB = Geo<D>::KSB;
-    uint8_t* kb = reinterpret_cast<uint8_t*>(buf);
-    const int q = threadIdx.x;
-    if (q < 4 * D) *reinterpret_cast<uint4*>(kb + (q / (D / 16)) * KSB + 16 * (q % (D / 16))) = st.r[0];
-    if (q < 4) *reinterpret_cast<uint4*>(kb + 64 * KSB + 16 * q) = st.r[Geo<D, F8>::EI];
-  } else {
+template <int D>
+__device__ __forceinline__ void store8(const Stage8<D>& st, uint16_t* buf) {
+  constexpr int CG = Geo<D>::CG, KSB = Geo<D>::KSB, VSR = Geo<D>::VSR;
+  uint16_t* vt = buf + Geo<D, true>::KTILE;
+  uint8_t* kb = reinterpret_cast<uint8_t*>(buf);
+  const int q = threadIdx.x;
+  if (q < 4 * D) *reinterpret_cast<uint4*>(kb + (q / (D / 16)) * KSB + 16 * (q % (D / 16))) = st.r[0];
+  if (q < 4) *reinterpret_cast<uint4*>(kb + 64 * KSB + 16 * q) = st.r[Geo<D, true>::EI];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int q = threadIdx.x + kAttnThreads * i;
-      *reinterpret_cast<uint4*>(buf + (q / CG) * KS + 8 * (q % CG)) = st.r[i];
-    }
+  for (int i = 0; i < Geo<D, true>::VPT; ++i) {
+    const int qq = threadIdx.x + kAttnThreads * i;
+    *reinterpret_cast<uint4*>(vt + (qq / CG) * VSR + 8 * (qq % CG)) = st.r[Geo<D, true>::VI + i];
   }
+}
+
+// bf16 path: per-lane source offsets (bytes, constant) of this wave's direct
+// loads. Wave w loads regions PW w .. PW w + PW - 1 of the K and the V part;
+// lane i of the load of region r supplies tile row r + NREG (i / (D / 8)),
+// bytes 16 (i % (D / 8)) .. + 16, which lands at byte 16 i of the region.
+typedef __attribute__((address_space(3))) void lds_void;
+template <int D>
+struct DmaOffs {
+  static constexpr int PW = Geo<D>::NREG / kWaves;
+  uint32_t off[PW];
+  int reg0;  // this wave's first region (uniform)
+  __device__ __forceinline__ void init() {
+    constexpr int NREG = Geo<D>::NREG;
+    reg0 = PW * __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int i = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < Geo<D, F8>::VPT; ++i) {
-    const int q = threadIdx.x + kAttnThreads * i;
-    *reinterpret_cast<uint4*>(vt + (q / CG) * VSR + 8 * (q % CG)) = st.r[VI + i];
+    for (int p = 0; p < PW; ++p)
+      off[p] = static_cast<uint32_t>((reg0 + p + NREG * (i / (D / 8))) * 2 * D + 16 * (i % (D / 8)));
   }
+};
+// bf16 path: one tile (keys kr, values vr, both bf16 [rows][D], `rows` valid
+// rows from the base on; the rest read as zeros) into staging buffer b by
+// direct global-to-LDS loads, DMA_OPS per wave. Their LDS writes land
+// asynchronously: they are counted by vmcnt, which the caller waits on
+// before the barrier that publishes the tile.
+template <int D>
+__device__ __forceinline__ void dma_rows(const uint16_t* kr, const uint16_t* vr, int rows, uint16_t* b,
+                                         const DmaOffs<D>& of) {
+  const auto rk = make_rsrc(kr, static_cast<uint32_t>(rows * D * 2));
+  const auto rv = make_rsrc(vr, static_cast<uint32_t>(rows * D * 2));
+  unsigned char* kb = reinterpret_cast<unsigned char*>(b);
+  unsigned char* vb = kb + 2 * Geo<D>::KTILE;
+#pragma unroll
+  for (int p = 0; p < DmaOffs<D>::PW; ++p) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kb + (of.reg0 + p) * Geo<D>::KREG), 16, of.off[p], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vb + (of.reg0 + p) * Geo<D>::VREG), 16, of.off[p], 0, 0, 0);
+  }
+}
+// Wait until at most N of this wave's global loads (direct loads included)
+// are outstanding (N < 16; expcnt and lgkmcnt left alone).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 // ------------------------------------------------------------ fp8
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -330,23 +377,28 @@ __device__ __forceinline__ f32x16 qk_half8(const uint8_t* kt, int sa, const Acc<
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-// V^T operand (8 keys x 1 dim per lane) from the row-major V tile: two
-// transposing reads, keys key0 .. key0 + 3 and key0 + 4 .. key0 + 7, where
-// p is the lane's supplier address (see voff in the kernel).
-template <int D>
-__device__ __forceinline__ bf16x8 v_op(const uint16_t* p) {
+// V^T operand (8 keys x 1 dim per lane) from the V tile (rows of V as
+// loaded): two transposing reads, keys key0 .. key0 + 3 and key0 + 4 ..
+// key0 + 7, where p is the lane's supplier address (see voff in the kernel).
+// (p is restrict-qualified so that the reads carry alias-scope information:
+// without it the compiler makes every LDS read that lacks such information
+// wait for all direct global-to-LDS loads in flight, including those of the
+// tiles still being prefetched; the kernel's own waits before each barrier
+// order the direct loads with the reads.)
+template <int D, bool F8>
+__device__ __forceinline__ bf16x8 v_op(const uint16_t* __restrict__ p) {
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const_cast<uint16_t*>(p)));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const_cast<uint16_t*>(p + 4 * Geo<D>::VSR)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const_cast<uint16_t*>(p + Geo<D, F8>::V4)));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // O^T += V^T P^T for 32 keys (vt: the lane's supplier base plus the key offset).
-template <int D>
+template <int D, bool F8>
 __device__ __forceinline__ void pv_half(const uint16_t* vt, const bf16x8 (&pb)[2], Acc<D>& a) {
 #pragma unroll
   for (int u = 0; u < Geo<D>::NU; ++u)
 #pragma unroll
-    for (int s = 0; s < 2; ++s) a.o[u] = mfma32x32x16(v_op<D>(vt + 16 * s * Geo<D>::VSR + 32 * u), pb[s], a.o[u]);
+    for (int s = 0; s < 2; ++s) a.o[u] = mfma32x32x16(v_op<D, F8>(vt + s * Geo<D, F8>::V16 + 32 * u), pb[s], a.o[u]);
 }
 
 // Lane predicate for accumulator register i of a 32-key S^T half: whether the
@@ -431,7 +483,7 @@ constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
 template <int D, bool kMask, bool kLast = false>
 __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int voff, Acc<D>& a, uint64_t km,
                                             uint64_t kl, float& pl) {
-  constexpr int NK = Geo<D>::NK, NU = Geo<D>::NU, KS = Geo<D>::KS, VSR = Geo<D>::VSR;
+  constexpr int NK = Geo<D>::NK, NU = Geo<D>::NU, K32 = Geo<D>::K32, V16 = Geo<D>::V16, V32 = Geo<D>::V32;
   constexpr int NV = 2 * NU;
   constexpr int kValu = kMask ? 52 : 36;  // VALU instructions of one softmax half (approximate)
   const uint16_t* kp = bc + koff;
@@ -444,7 +496,7 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
   __builtin_amdgcn_sched_barrier(0);
   // region 2: S^T half 0 | K operands of half 1
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) k1[ks] = *reinterpret_cast<const bf16x8*>(kp + 32 * KS + 16 * ks);
+  for (int ks = 0; ks < NK; ++ks) k1[ks] = *reinterpret_cast<const bf16x8*>(kp + K32 + 16 * ks);
   f32x16 s0 = a.nm, s1 = a.nm;
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks) s0 = mfma32x32x16(k0[ks], a.qb[ks], s0);
@@ -458,7 +510,7 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) v0[2 * u + h] = v_op<D>(vp + 16 * h * VSR + 32 * u);
+    for (int h = 0; h < 2; ++h) v0[2 * u + h] = v_op<D, false>(vp + h * V16 + 32 * u);
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks) s1 = mfma32x32x16(k1[ks], a.qb[ks], s1);
   float pl0 = 0.f, pl1 = 0.f;
@@ -475,7 +527,7 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) v1[2 * u + h] = v_op<D>(vp + (32 + 16 * h) * VSR + 32 * u);
+    for (int h = 0; h < 2; ++h) v1[2 * u + h] = v_op<D, false>(vp + V32 + h * V16 + 32 * u);
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
@@ -540,7 +592,7 @@ __device__ __forceinline__ float exact_tile8(const uint8_t* kb, const uint8_t* s
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) v0[2 * u + h] = v_op<D>(vp + 16 * h * VSR + 32 * u);
+    for (int h = 0; h < 2; ++h) v0[2 * u + h] = v_op<D, true>(vp + 16 * h * VSR + 32 * u);
 #pragma unroll
   for (int st = 0; st < NK8; ++st)
     s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k1[st], a.q8[st], s1, 0, 0, 0, sa1, 0, a.qe);
@@ -558,7 +610,7 @@ __device__ __forceinline__ float exact_tile8(const uint8_t* kb, const uint8_t* s
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) v1[2 * u + h] = v_op<D>(vp + (32 + 16 * h) * VSR + 32 * u);
+    for (int h = 0; h < 2; ++h) v1[2 * u + h] = v_op<D, true>(vp + (32 + 16 * h) * VSR + 32 * u);
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
@@ -618,11 +670,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     int mode, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ ke, const uint8_t* __restrict__ kb8,
     const uint8_t* __restrict__ kbe, const int32_t* __restrict__ offs, int* __restrict__ queues) {
   const bool tail = mode != kModeDrop, corr = mode == kModePisa;
-  constexpr int BUF = Geo<D, F8>::BUF, KS = Geo<D>::KS, KSB = Geo<D>::KSB, VSR = Geo<D>::VSR, HS = Geo<D>::HS;
+  constexpr int BUF = Geo<D, F8>::BUF, NBUF = Geo<D, F8>::NBUF, KSB = Geo<D>::KSB, VSR = Geo<D>::VSR;
+  constexpr int HS = Geo<D>::HS, NREG = Geo<D>::NREG;
   extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* buf = reinterpret_cast<uint16_t*>(smem);  // 2 staging buffers
+  uint16_t* buf = reinterpret_cast<uint16_t*>(smem);  // NBUF staging buffers
   const int nw = ceil_div(T, 32);
-  uint32_t* masks = reinterpret_cast<uint32_t*>(smem + sizeof(uint16_t) * 2 * BUF);  // [kQB][nw]
+  uint32_t* masks = reinterpret_cast<uint32_t*>(smem + sizeof(uint16_t) * NBUF * BUF);  // [kQB][nw]
   uint32_t* ubits = masks + kQB * nw;  // [kQB][nw]: bit e = union tile e belongs to S_i of q-block qi
   int* sh = reinterpret_cast<int*>(ubits + kQB * nw);  // nu, rerun flags, next item (10)
   uint16_t* ulist = reinterpret_cast<uint16_t*>(sh + 12);                           // [T]
@@ -697,12 +750,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   const float cl2 = scale * kLog2e;
   const int nlast = L - 64 * (T - 1);
   // per-lane operand offsets inside a staging buffer
-  const int koff = perm_key(0, ql) * KS + 8 * g;              // K rows of sub-tile 0 (+32 KS for 1)
-  const int koff8 = perm_key(0, ql) * KSB + 32 * g;           // fp8: bytes, (+32 KSB for sub-tile 1)
+  // bf16: the lane's K row of sub-tile 0, dims 8 g .. + 8 (+K32 for sub-tile 1)
+  const int krow = perm_key(0, ql);
+  const int koff = (krow % NREG) * (Geo<D>::KREG / 2) + (krow / NREG) * D + 8 * g;
+  const int koff8 = krow * KSB + 32 * g;                      // fp8: bytes, (+32 KSB for sub-tile 1)
   // supplier address of the transposing V reads: in 16-lane group G = l / 16,
   // lane 4 k + j reads row (key) 8 g + k, dims 16 (G % 2) + 4 j .. + 4, so
   // that the group's output lane i gets dim 16 (G % 2) + i of keys .. + 3
-  const int voff = Geo<D, F8>::KTILE + (8 * g + (l & 15) / 4) * VSR + 16 * ((l >> 4) & 1) + 4 * (l & 3);
+  const int vrow = 8 * g + (l & 15) / 4, vdim = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+  const int voff = Geo<D, F8>::KTILE + vdim +
+                   (F8 ? vrow * VSR : (vrow % NREG) * (Geo<D>::VREG / 2) + (vrow / NREG) * D);
 
   Acc<D> a;
   {
@@ -764,8 +821,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
                                                       pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7])));
     }
   }
-  StageOffs<D, F8> of;
-  of.init();
+  StageOffs8<D> of8;
+  DmaOffs<D> ofd;
+  if constexpr (F8)
+    of8.init();
+  else
+    ofd.init();
 
   // ---- membership masks of the 4 exact lists and their sorted union
   for (int e = tid; e < kQB * nw; e += kAttnThreads) masks[e] = 0u;
@@ -845,46 +906,80 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   // softmax reference), steps 1..nu = the exact tiles of the union, then
   // centroid chunks 1..nch-1. Chunk c covers blocks [64 c, 64 c + 64).
   const int nsteps = 1 + nu + (nch > 1 ? nch - 1 : 0);
-  Stage<D, F8> st;
-  auto fetch = [&](int step) {
+  // staging buffer of the current step (step % NBUF, kept by rotation)
+  int slot = 0;
+  auto slot_after = [&](int k) { return slot + k < NBUF ? slot + k : slot + k - NBUF; };
+  auto cur = [&]() -> uint16_t* { return buf + slot * BUF; };
+  Stage8<D> st;  // fp8: the step in flight
+  // start the loads of a step: fp8 into registers (st), bf16 straight into
+  // LDS buffer dst
+  auto fetch = [&](int step, uint16_t* dst) {
     if (step >= 1 && step <= nu) {
       const int j = __builtin_amdgcn_readfirstlane(ulist[step - 1]);
       const size_t base = static_cast<size_t>(64 * j) * D;
-      if (F8)
-        load_rows<D, F8>(k8 + head + base, Vh + base, ke + static_cast<size_t>(bh) * L + 64 * j, min(64, L - 64 * j), of,
-                         st);
+      if constexpr (F8)
+        load_rows8<D>(k8 + head + base, Vh + base, ke + static_cast<size_t>(bh) * L + 64 * j, min(64, L - 64 * j), of8,
+                      st);
       else
-        load_rows<D, F8>(Kh + base, Vh + base, nullptr, min(64, L - 64 * j), of, st);
+        dma_rows<D>(Kh + base, Vh + base, min(64, L - 64 * j), dst, ofd);
     } else {
       const int c = step == 0 ? 0 : step - nu;
       const size_t base = static_cast<size_t>(64 * c) * D;
-      if (F8)
-        load_rows<D, F8>(kb8 + static_cast<size_t>(bh) * T * D + base, vs + base,
-                         kbe + static_cast<size_t>(bh) * T + 64 * c, min(64, T - 64 * c), of, st);
+      if constexpr (F8)
+        load_rows8<D>(kb8 + static_cast<size_t>(bh) * T * D + base, vs + base,
+                      kbe + static_cast<size_t>(bh) * T + 64 * c, min(64, T - 64 * c), of8, st);
       else
-        load_rows<D, F8>(kb + base, vs + base, nullptr, min(64, T - 64 * c), of, st);
+        dma_rows<D>(kb + base, vs + base, min(64, T - 64 * c), dst, ofd);
     }
   };
-  auto put = [&](int step, uint16_t* b) { store_exact<D, F8>(st, b); };
   // S^T of sub-tile t (keys 32 t ..) of a staged tile, either path
   auto s_half = [&](const uint16_t* bc, int t) -> f32x16 {
     if constexpr (F8) {
       const uint8_t* b8 = reinterpret_cast<const uint8_t*>(bc);
       return qk_half8<D>(b8 + koff8 + 32 * t * KSB, b8[64 * KSB + perm_key(t, ql)], a);
     } else {
-      return qk_half<D>(bc + koff + 32 * t * KS, a);
+      return qk_half<D>(bc + koff + t * Geo<D>::K32, a);
     }
   };
+  // after step: publish step + 1 in LDS. fp8: store it from registers and
+  // load step + 2. bf16 (three buffers, loads two steps ahead): wait for
+  // this wave's loads of step + 1 (those of step + 2 may stay in flight),
+  // then, past the barrier, every wave is done with step's buffer, which
+  // takes step + 3.
   auto advance = [&](int step) {
-    if (step + 1 < nsteps) put(step + 1, buf + ((step + 1) & 1) * BUF);
-    if (step + 2 < nsteps) fetch(step + 2);
-    lds_barrier();
+    if constexpr (F8) {
+      if (step + 1 < nsteps) store8<D>(st, buf + slot_after(1) * BUF);
+      if (step + 2 < nsteps) fetch(step + 2, nullptr);
+      lds_barrier();
+    } else {
+      if (step + 2 < nsteps)
+        wait_vm<Geo<D>::DMA_OPS>();
+      else
+        wait_vm<0>();
+      lds_barrier();
+      if (step + 3 < nsteps) fetch(step + 3, cur());
+    }
+    slot = slot_after(1);
   };
   auto start = [&]() {
-    fetch(0);
-    put(0, buf);
-    lds_barrier();
-    if (nsteps > 1) fetch(1);
+    slot = 0;
+    if constexpr (F8) {
+      fetch(0, nullptr);
+      store8<D>(st, buf);
+      lds_barrier();
+      if (nsteps > 1) fetch(1, nullptr);
+    } else {
+      fetch(0, buf);
+      if (nsteps > 1) fetch(1, buf + BUF);
+      if (nsteps > 2) fetch(2, buf + 2 * BUF);
+      if (nsteps > 2)
+        wait_vm<2 * Geo<D>::DMA_OPS>();
+      else if (nsteps > 1)
+        wait_vm<Geo<D>::DMA_OPS>();
+      else
+        wait_vm<0>();
+      lds_barrier();
+    }
   };
   // whether this wave computes union tile `step`: one 64-bit word of its
   // bitmap per 64 tiles, held in scalar registers
@@ -926,7 +1021,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       float mx = -INFINITY;
       start();
       for (int step = 0; step < nsteps; ++step) {
-        const uint16_t* bc = buf + (step & 1) * BUF;
+        const uint16_t* bc = cur();
         if (step >= 1 && step <= nu) {
           if (mine_tile(step)) {
             const uint64_t km = step > nfull ? past_nlast : 0ull;
@@ -989,8 +1084,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
                                                        static_cast<uint32_t>(kl), p0, pl0);
           ps += softmax_half<D, true, true, true>(s1, a, shift, static_cast<uint32_t>(km >> 32),
                                                   static_cast<uint32_t>(kl >> 32), p1, pl1);
-          pv_half<D>(buf + voff, p0, a);
-          pv_half<D>(buf + voff + 32 * VSR, p1, a);
+          pv_half<D, F8>(buf + voff, p0, a);
+          pv_half<D, F8>(buf + voff + Geo<D, F8>::V32, p1, a);
           a.dsum += 64.f * ps + (static_cast<float>(nlast) - 64.f) * (pl0 + pl1);
           a.csum += ps;
         }
@@ -999,19 +1094,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     }
     // ---- exact tiles: full blocks, then the partial last block
     for (int step = 1; step <= nfull; ++step) {
-      const uint16_t* bc = buf + (step & 1) * BUF;
+      const uint16_t* bc = cur();
       if (mine_tile(step)) a.dsum += run_tile<D, F8, false>(bc, koff, koff8, ql, voff, a, 0ull, 0ull, pl);
       advance(step);
     }
     for (int step = nfull + 1; step <= nu; ++step) {
-      const uint16_t* bc = buf + (step & 1) * BUF;
+      const uint16_t* bc = cur();
       if (mine_tile(step)) a.dsum += run_tile<D, F8, true>(bc, koff, koff8, ql, voff, a, past_nlast, 0ull, pl);
       advance(step);
     }
     // ---- centroid chunks 1..nch-2, then the last chunk (block T - 1 with its
     // weight n_{T-1})
     for (int step = nu + 1; step < nsteps - 1; ++step) {
-      const uint16_t* bc = buf + (step & 1) * BUF;
+      const uint16_t* bc = cur();
       if (active) {
         const float ps = run_tile<D, F8, true>(bc, koff, koff8, ql, voff, a, chunk_mask(step - nu), 0ull, pl);
         a.dsum += 64.f * ps;
@@ -1020,8 +1115,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       advance(step);
     }
     if (nch > 1) {
-      const int step = nsteps - 1, c = nch - 1;
-      const uint16_t* bc = buf + (step & 1) * BUF;
+      const int c = nch - 1;  // step nsteps - 1
+      const uint16_t* bc = cur();
       if (active) {
         const float ps =
             run_tile<D, F8, true, true>(bc, koff, koff8, ql, voff, a, chunk_mask(c), 1ull << (T - 1 - 64 * c), pl);
@@ -1287,7 +1382,7 @@ hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, cons
                        s, kbar, crows, kb8, kbe);
   }
   const int nw = ceil_div(T, 32);
-  const size_t lds = sizeof(uint16_t) * 2 * Geo<D, F8>::BUF + 2 * sizeof(uint32_t) * kQB * nw + 12 * sizeof(int) +
+  const size_t lds = sizeof(uint16_t) * Geo<D, F8>::NBUF * Geo<D, F8>::BUF + 2 * sizeof(uint32_t) * kQB * nw + 12 * sizeof(int) +
                      sizeof(uint16_t) * T;
   const size_t lds_al = (lds + 15) / 16 * 16;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_bf16<D, F8>),
