@@ -823,18 +823,38 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   }
   StageOffs8<D> of8;
   DmaOffs<D> ofd;
-  if constexpr (F8)
+  const uint16_t* kb = kb16 + static_cast<size_t>(bh) * T * D;
+  const uint16_t* vs = vs16 + static_cast<size_t>(bh) * T * D;
+  if constexpr (F8) {
     of8.init();
-  else
+  } else {
     ofd.init();
+    // step 0 (centroid chunk 0) does not depend on the exact lists: its
+    // direct loads go out now and overlap the set-up below
+    dma_rows<D>(kb, vs, min(64, T), buf, ofd);
+  }
 
   // ---- membership masks of the 4 exact lists and their sorted union
+  // (the first entries of each list are loaded before the masks are
+  // cleared, so that round trip overlaps the clearing barrier)
+  constexpr int kPre = 3;
+  int cnt = 0, jpre[kPre];
+  const int32_t* irow = nullptr;
+  if (qvalid && (w & 1) == 0) {
+    irow = exact_list(idx, offs, bh, T, qblk, keep_k, cnt);
+#pragma unroll
+    for (int r = 0; r < kPre; ++r) jpre[r] = l + 64 * r < cnt ? irow[l + 64 * r] : 0;
+  }
   for (int e = tid; e < kQB * nw; e += kAttnThreads) masks[e] = 0u;
   lds_barrier();
   if (qvalid && (w & 1) == 0) {
-    int cnt;
-    const int32_t* irow = exact_list(idx, offs, bh, T, qblk, keep_k, cnt);
-    for (int e = l; e < cnt; e += 64) {
+#pragma unroll
+    for (int r = 0; r < kPre; ++r)
+      if (l + 64 * r < cnt) {
+        const int j = min(max(jpre[r], 0), T - 1);
+        atomicOr(&masks[qi * nw + (j >> 5)], 1u << (j & 31));
+      }
+    for (int e = l + 64 * kPre; e < cnt; e += 64) {
       const int j = min(max(irow[e], 0), T - 1);
       atomicOr(&masks[qi * nw + (j >> 5)], 1u << (j & 31));
     }
@@ -879,8 +899,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   lds_barrier();
   const uint32_t* mymask = masks + qi * nw;
   const uint32_t* mybits = ubits + qi * nw;
-  const uint16_t* kb = kb16 + static_cast<size_t>(bh) * T * D;
-  const uint16_t* vs = vs16 + static_cast<size_t>(bh) * T * D;
   // stage 2 chunks (none when U_i is empty or the tail is dropped; step 0
   // still stages centroid chunk 0 for the softmax reference)
   bool any_tail = keep_k < T;  // some query block of the group has a non-empty U_i
@@ -961,7 +979,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     }
     slot = slot_after(1);
   };
-  auto start = [&]() {
+  // (pre0: the bf16 loads of step 0 were issued already)
+  auto start = [&](bool pre0) {
     slot = 0;
     if constexpr (F8) {
       fetch(0, nullptr);
@@ -969,7 +988,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       lds_barrier();
       if (nsteps > 1) fetch(1, nullptr);
     } else {
-      fetch(0, buf);
+      if (!pre0) fetch(0, buf);
       if (nsteps > 1) fetch(1, buf + BUF);
       if (nsteps > 2) fetch(2, buf + 2 * BUF);
       if (nsteps > 2)
@@ -1019,7 +1038,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       // exact maximum of everything it weighs (exact keys, and centroids,
       // which never exceed the keys of their own block), then start over.
       float mx = -INFINITY;
-      start();
+      start(false);
       for (int step = 0; step < nsteps; ++step) {
         const uint16_t* bc = cur();
         if (step >= 1 && step <= nu) {
@@ -1052,7 +1071,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       }
     }
     a.over = false;
-    start();
+    start(pass == 0);
     float pl = 0.f;
     // ---- step 0: centroid chunk 0
     {
