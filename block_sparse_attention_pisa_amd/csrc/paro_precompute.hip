@@ -755,11 +755,16 @@ __global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(2)
                                                                  const float* __restrict__ kbar,
                                                                  const float* __restrict__ vsum,
                                                                  const float* __restrict__ hperm,
-                                                                 double* __restrict__ M, int L, int T) {
+                                                                 double* __restrict__ M, int L, int T, int nbh) {
   extern __shared__ __align__(16) unsigned char smem[];
   PairLds<E, D>& s = *reinterpret_cast<PairLds<E, D>*>(smem);
   constexpr int MT = PairA<D>::MT, NT = PairA<D>::NT;
-  const int j = blockIdx.x, bh = blockIdx.y;
+  // one workgroup per (head, block), heads fastest and blocks from the end
+  // of the sequence back: blocks of nearly i.i.d. keys (text tokens, which
+  // DiT layouts append after the image or video tokens) have the smallest
+  // spectral gaps and the longest Lanczos runs, and this order starts them
+  // first instead of leaving the last head's to run alone at the end
+  const int j = T - 1 - static_cast<int>(blockIdx.x / nbh), bh = static_cast<int>(blockIdx.x % nbh);
   const int t = threadIdx.x, w = t / 64, l = t % 64, g = l / 16, c = l % 16;
   const int row0 = j * kBlock, nvalid = min(kBlock, L - row0);
 
@@ -1012,8 +1017,8 @@ hipError_t launch_typed(const paro_problem& p, const E* K, const E* V, float* kb
   hipLaunchKernelGGL(k_hbar_reduce<D>, dim3(ceil_div(D * D, 256), bh), dim3(256), 0, st,
                      static_cast<const float*>(partials), Hbar, hperm, nchunk, T);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_block_spectral<E, D>), dim3(T, bh), dim3(kPairThreads), lds3, st, K, V, kbar, vsum,
-                     static_cast<const float*>(hperm), M, p.L, T);
+  hipLaunchKernelGGL((k_block_spectral<E, D>), dim3(static_cast<unsigned>(T * bh)), dim3(kPairThreads), lds3, st, K, V,
+                     kbar, vsum, static_cast<const float*>(hperm), M, p.L, T, static_cast<int>(bh));
   return hipGetLastError();
 }
 
