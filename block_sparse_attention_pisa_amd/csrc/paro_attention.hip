@@ -6,15 +6,17 @@
 // bf16 kernel (k_attn_bf16): a workgroup of 8 waves serves 4 consecutive
 // query blocks of one (batch, head); each block of 64 rows is split between
 // two waves of 32 rows, so every wave fits in 256 registers and each SIMD
-// runs two waves whose matrix and vector work interleave.
+// runs two waves whose matrix and vector work interleave. The grid is
+// persistent (one workgroup per CU) and takes these items from per-XCD
+// queues in the workspace.
 //  * The exact lists of the 4 blocks are merged into their sorted union; each
-//    union tile (64 keys x d) is staged once into LDS for all 8 waves (the
-//    global loads of the tile after next sit in registers while the current
-//    one is consumed; two LDS buffers; one LDS-only barrier per tile). K and
-//    V are both stored row-major, rows padded so that no operand read has a
-//    bank conflict: a K operand is one ds_read_b128, a V^T operand two
-//    transposing reads (ds_read_b64_tr_b16, new in CDNA4), each at a per-lane
-//    base plus a compile-time offset, so V needs no transpose on its way in.
+//    union tile (64 keys x d) is staged once into LDS for all 8 waves by
+//    direct global-to-LDS loads, two tiles ahead into three buffers, one
+//    LDS-only barrier per tile. K and V rows are stored whole, in 1 KB
+//    regions whose spacing keeps every operand read free of bank conflicts:
+//    a K operand is one ds_read_b128, a V^T operand two transposing reads
+//    (ds_read_b64_tr_b16, new in CDNA4), each at a per-lane base plus a
+//    compile-time offset, so V needs no transpose on its way in.
 //  * A wave computes S^T = K Q^T for its 32 queries on
 //    v_mfma_f32_32x32x16_bf16 with Q^T held in registers, the accumulators
 //    starting at -m (the softmax reference). In the C layout of S^T each
@@ -52,9 +54,10 @@
 #include "paro_common.h"
 
 // Device scratch of paro_attention_noalloc, for callers that cannot allocate:
-// it holds the bf16 copies of kbar and vsum that paro_attention otherwise
-// keeps in the caller's workspace. Every GPU the library runs on holds its
-// own copy until the process ends; calls on one GPU share it.
+// it holds the bf16 copies of kbar and vsum and the work-queue counters that
+// paro_attention otherwise keeps in the caller's workspace. Every GPU the
+// library runs on holds its own copy until the process ends; calls on one
+// GPU share it.
 static __device__ __align__(256) unsigned char scratch[PARO_NOALLOC_SCRATCH_BYTES];
 
 namespace paro {
