@@ -73,58 +73,56 @@ constexpr int kQueueInts = 8 * kQueueStride;
 // tail modes (the PARO_TAIL_* codes of the ABI; 2 = zeroth order only: tail on, correction off)
 constexpr int kModePisa = 0, kModeDrop = 1;
 
-// Tile geometry.
-// bf16: a staged tile (64 K rows, then 64 V rows) lives in LDS as 1 KB
-// regions, each filled by one wave-wide direct global-to-LDS load (lane i
-// writes bytes 16 i .. 16 i + 16 of the region): region r of the K (V) part
-// holds tile rows r, r + NREG, r + 2 NREG, ... as whole rows of 2 D bytes, so
-// every such load reads RR complete rows of the tensor. Regions are KREG
-// (VREG) bytes apart; the 16 (64) bytes beyond the 1 KB shift each region's
-// LDS banks, so that the K operand reads of 16 consecutive rows (one 16-lane
-// group of ds_read_b128, same dims) fall in 16 regions on 16 different bank
-// quads, and the transposing V reads of 4 consecutive rows (64 bytes each)
-// fall in 4 regions 64 bytes apart: no bank conflicts, and every operand
-// address is a per-lane base plus constants.
-// F8: K (and the centroid keys) are staged through registers as fp8 e4m3
-// rows of D bytes (row stride KSB) plus one power-of-two (E8M0) scale byte
-// per row; V stays bf16, row-major with row stride VSR.
+// Tile geometry. A staged tile (64 K rows, then 64 V rows) lives in LDS as
+// 1 KB regions, each filled by one wave-wide direct global-to-LDS load (lane
+// i writes bytes 16 i .. 16 i + 16 of the region): region r of the K (V)
+// part holds tile rows r, r + NREG, r + 2 NREG, ... as whole rows, so every
+// such load reads complete rows of the tensor. Regions are KREG (VREG) bytes
+// apart; the 16 (64) bytes beyond the 1 KB shift each region's LDS banks, so
+// that the K operand reads of 16 consecutive rows (one 16-lane group of
+// ds_read_b128, same dims) fall in 16 different bank quads, and the
+// transposing V reads of 4 consecutive rows (64 bytes each) fall in 4
+// regions 64 bytes apart: no bank conflicts, and every operand address is a
+// per-lane base plus constants.
+// bf16: K rows of 2 D bytes, NREG = 64 / RR regions of RR = 512 / D rows.
+// F8: K (and the centroid keys) as e4m3 rows of D bytes, NREG8 = D / 16
+// regions of 1024 / D rows, then the 64 row-scale (E8M0) bytes at KSC; V
+// as in bf16.
 template <int D, bool F8 = false>
 struct Geo {
-  static constexpr int CG = D / 8;                         // 16-byte chunks in a bf16 K row
-  static constexpr int KSB = D + 16;                       // fp8 K tile row stride (bytes): D dims and padding
-  static constexpr int VSR = D + 32;                       // fp8 path: V tile row stride (row-major, read transposed)
-  static constexpr int HS = D + 8;                         // Hbar^T row stride
-  static constexpr int RR = 512 / D;                       // bf16: tile rows per 1 KB region
-  static constexpr int NREG = 64 / RR;                     // bf16: regions per 64 rows
-  static constexpr int KREG = 1024 + 16, VREG = 1024 + 64; // bf16: bytes from one region to the next
-  // K tile (elements of 2 bytes); fp8: 64 rows, then the 64 row-scale bytes
-  static constexpr int KTILE = F8 ? (64 * KSB + 64) / 2 : NREG * KREG / 2;
-  static constexpr int VTILE = F8 ? 64 * VSR : NREG * VREG / 2;
+  static constexpr int CG = D / 8;                         // 16-byte chunks in a bf16 row
+  static constexpr int HS = D + 8;                         // fp8 stage 3: Hbar^T row stride
+  static constexpr int RR = 512 / D;                       // bf16 K and V: tile rows per 1 KB region
+  static constexpr int NREG = 64 / RR;                     // bf16 K and V: regions per 64 rows
+  static constexpr int NREG8 = D / 16;                     // e4m3 K: regions per 64 rows
+  static constexpr int KREG = 1024 + 16, VREG = 1024 + 64; // bytes from one region to the next
+  static constexpr int KSC = NREG8 * KREG;                 // fp8: byte offset of the row-scale bytes
+  // K part (elements of 2 bytes); fp8: the e4m3 regions, then the scales
+  static constexpr int KTILE = F8 ? (KSC + 64) / 2 : NREG * KREG / 2;
+  static constexpr int VTILE = NREG * VREG / 2;
   static constexpr int BUF = KTILE + VTILE;                // one staging buffer (elements)
-  static constexpr int NBUF = F8 ? 2 : 3;                  // staging buffers in LDS
+  static constexpr int NBUF = 3;                           // staging buffers in LDS
   // element offsets, from a lane's operand address, of the same dims 32 key
-  // rows on (K, bf16), and 4, 16 and 32 key rows on (V)
+  // rows on (bf16 K), and 4, 16 and 32 key rows on (V); fp8 K: 32 rows on
+  // are K32B bytes on
   static constexpr int K32 = 32 / NREG * D;
-  static constexpr int V4 = F8 ? 4 * VSR : 4 * VREG / 2;
-  static constexpr int V16 = F8 ? 16 * VSR : 16 / NREG * D;
-  static constexpr int V32 = F8 ? 32 * VSR : 32 / NREG * D;
-  static constexpr int DMA_OPS = 2 * NREG / kWaves;       // bf16: direct loads per wave and tile
+  static constexpr int K32B = 32 / NREG8 * D;
+  static constexpr int V4 = 4 * VREG / 2;
+  static constexpr int V16 = 16 / NREG * D;
+  static constexpr int V32 = 32 / NREG * D;
+  // direct loads per wave and tile: bf16 NREG / 8 K and V regions each;
+  // fp8 d = 128 one e4m3 region, two V regions and one load of scale bytes,
+  // d = 64 one V region and either the e4m3 region (waves 0-3) or scales
+  static constexpr int DMA_OPS = F8 ? (D == 128 ? 4 : 2) : 2 * NREG / kWaves;
   static constexpr int NK = D / 16;                        // bf16 k-steps of S^T = K Q^T over the D dims
   static constexpr int NK8 = D / 64;                       // fp8 k-steps
   static constexpr int NU = D / 32;                        // 32-dim output tiles
-  // fp8 path, staged through registers: one K item (16 bytes) for threads
-  // < 4 D, VPT V chunks per thread, the row-scale bytes in threads 0-3
-  static constexpr int VPT = 64 * CG / kAttnThreads;       // V chunks staged per thread and tile
-  static constexpr int VI = 1;                             // first V register
-  static constexpr int EI = 1 + VPT;                       // the row-scale item (threads 0-3)
-  static constexpr int NR = 2 + VPT;                       // staging registers (16 B)
   static_assert(D * HS <= NBUF * BUF, "Hbar^T must fit in the staging buffers");
-  // bf16: each wave loads whole regions; a lane's V rows 8 g + k (k < 4)
-  // and those 4 rows on stay in one row of regions; +16 and +32 key rows
-  // are whole rows of regions on
-  static_assert(F8 || (NREG % kWaves == 0 && 11 % NREG + 4 < NREG && 16 % NREG == 0), "bf16 region geometry");
-  static_assert(64 * CG % kAttnThreads == 0, "V items per thread");
-  static_assert(4 * D <= kAttnThreads, "fp8 K items per thread");
+  // each wave loads whole regions; a lane's V rows 8 g + k (k < 4) and those
+  // 4 rows on stay in one row of regions; +16 and +32 key rows are whole rows
+  // of regions on
+  static_assert(NREG % kWaves == 0 && 11 % NREG + 4 < NREG && 16 % NREG == 0, "region geometry");
+  static_assert((D == 128 && NREG8 == kWaves) || (D == 64 && 2 * NREG8 == kWaves), "fp8 regions per wave");
   static_assert(KTILE % 8 == 0, "V tile alignment");
 };
 
@@ -155,64 +153,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
-// fp8 path: one step's data in flight, NR registers of 16 bytes per thread:
-// r[0] = a K item (16 e4m3 bytes of a row, threads < 4 D); r[VI..VI+VPT) = V
-// chunks (8 dims of one key each, consecutive lanes on consecutive chunks of
-// a row); r[EI] = row-scale bytes (threads 0-3).
-template <int D>
-struct Stage8 {
-  uint4 r[Geo<D, true>::NR];
-};
-
-// fp8 path: per-thread byte offsets of the staging loads inside a tile (constant).
-template <int D>
-struct StageOffs8 {
-  uint32_t k;                         // fp8 K: row tid / (D / 16), 16-byte chunk tid % (D / 16)
-  uint32_t v[Geo<D, true>::VPT];      // V chunk i: row q / CG, chunk q % CG (q = tid + threads * i)
-  __device__ __forceinline__ void init() {
-    constexpr int CG = Geo<D>::CG;
-    const int tid = threadIdx.x;
-    k = static_cast<uint32_t>((tid / (D / 16)) * D + 16 * (tid % (D / 16)));
-#pragma unroll
-    for (int i = 0; i < Geo<D, true>::VPT; ++i) {
-      const int q = tid + kAttnThreads * i;
-      v[i] = static_cast<uint32_t>((q / CG) * D * 2 + 16 * (q % CG));
-    }
-  }
-};
-
-// fp8 path: 64 rows of e4m3 keys (kr, D bytes each, scale bytes in ke) and
-// bf16 values (vr, [rows][D]), `rows` valid rows from the base on (uniform):
-// an exact tile (the rows of kv-block j) or a centroid chunk (64 centroids).
-template <int D>
-__device__ __forceinline__ void load_rows8(const uint8_t* kr, const uint16_t* vr, const uint8_t* ke, int rows,
-                                           const StageOffs8<D>& of, Stage8<D>& st) {
-  const auto rk = make_rsrc(kr, static_cast<uint32_t>(rows * D));
-  const auto rv = make_rsrc(vr, static_cast<uint32_t>(rows * D * 2));
-  if (threadIdx.x < 4 * D) st.r[0] = bload(rk, of.k);
-  // the range check of a raw buffer load is per dword, so the scale bytes'
-  // range is rounded up to whole dwords (the bytes past the last row belong
-  // to masked keys; they lie inside the caller's workspace)
-  if (threadIdx.x < 4)
-    st.r[Geo<D, true>::EI] = bload(make_rsrc(ke, static_cast<uint32_t>((rows + 3) & ~3)), 16 * threadIdx.x);
-#pragma unroll
-  for (int i = 0; i < Geo<D, true>::VPT; ++i) st.r[Geo<D, true>::VI + i] = bload(rv, of.v[i]);
-}
-template <int D>
-__device__ __forceinline__ void store8(const Stage8<D>& st, uint16_t* buf) {
-  constexpr int CG = Geo<D>::CG, KSB = Geo<D>::KSB, VSR = Geo<D>::VSR;
-  uint16_t* vt = buf + Geo<D, true>::KTILE;
-  uint8_t* kb = reinterpret_cast<uint8_t*>(buf);
-  const int q = threadIdx.x;
-  if (q < 4 * D) *reinterpret_cast<uint4*>(kb + (q / (D / 16)) * KSB + 16 * (q % (D / 16))) = st.r[0];
-  if (q < 4) *reinterpret_cast<uint4*>(kb + 64 * KSB + 16 * q) = st.r[Geo<D, true>::EI];
-#pragma unroll
-  for (int i = 0; i < Geo<D, true>::VPT; ++i) {
-    const int qq = threadIdx.x + kAttnThreads * i;
-    *reinterpret_cast<uint4*>(vt + (qq / CG) * VSR + 8 * (qq % CG)) = st.r[Geo<D, true>::VI + i];
-  }
 }
 
 // bf16 path: per-lane source offsets (bytes, constant) of this wave's direct
@@ -250,6 +190,53 @@ __device__ __forceinline__ void dma_rows(const uint16_t* kr, const uint16_t* vr,
   for (int p = 0; p < DmaOffs<D>::PW; ++p) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kb + (of.reg0 + p) * Geo<D>::KREG), 16, of.off[p], 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vb + (of.reg0 + p) * Geo<D>::VREG), 16, of.off[p], 0, 0, 0);
+  }
+}
+// fp8 path: this wave's direct loads of a tile (DMA_OPS of them): V regions
+// as DmaOffs; d = 128: e4m3 region w and scale bytes 8 w .. + 8 (lanes 0-1);
+// d = 64: e4m3 region w (waves 0-3) or scale bytes 16 (w - 4) .. + 16 (waves
+// 4-7, lanes 0-3). Lane i of an e4m3 load supplies tile row r + NREG8 (i / (D
+// / 16)), bytes 16 (i % (D / 16)) .. + 16; a scale load writes 4 bytes per lane.
+template <int D>
+struct DmaOffs8 {
+  DmaOffs<D> v;
+  uint32_t koff, soff;
+  int w;                    // this wave (uniform)
+  bool has_k;               // loads an e4m3 region (else scale bytes, d = 64)
+  int sbase, slanes;        // scale bytes of this wave: first byte, lanes
+  __device__ __forceinline__ void init() {
+    constexpr int NREG8 = Geo<D, true>::NREG8;
+    v.init();
+    w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int i = threadIdx.x & 63;
+    has_k = D == 128 || w < 4;
+    koff = static_cast<uint32_t>((w + NREG8 * (i / (D / 16))) * D + 16 * (i % (D / 16)));
+    sbase = D == 128 ? 8 * w : 16 * (w - 4);
+    slanes = D == 128 ? 2 : 4;
+    soff = static_cast<uint32_t>(sbase + 4 * i);
+  }
+};
+template <int D>
+__device__ __forceinline__ void dma_rows8(const uint8_t* kr, const uint16_t* vr, const uint8_t* ke, int rows,
+                                          uint16_t* b, const DmaOffs8<D>& of) {
+  constexpr int KREG = Geo<D, true>::KREG, VREG = Geo<D, true>::VREG;
+  unsigned char* kb = reinterpret_cast<unsigned char*>(b);
+  unsigned char* vb = kb + 2 * Geo<D, true>::KTILE;
+  const auto rv = make_rsrc(vr, static_cast<uint32_t>(rows * D * 2));
+#pragma unroll
+  for (int p = 0; p < DmaOffs<D>::PW; ++p)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vb + (of.v.reg0 + p) * VREG), 16, of.v.off[p], 0, 0, 0);
+  if (of.has_k) {
+    const auto rk = make_rsrc(kr, static_cast<uint32_t>(rows * D));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kb + of.w * KREG), 16, of.koff, 0, 0, 0);
+  }
+  if (D == 128 || !of.has_k) {
+    // the range check of a raw buffer load is per dword, so the scale bytes'
+    // range is rounded up to whole dwords (the bytes past the last row belong
+    // to masked keys; they lie inside the caller's workspace)
+    const auto rs = make_rsrc(ke, static_cast<uint32_t>((rows + 3) & ~3));
+    if ((threadIdx.x & 63) < of.slanes)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(kb + Geo<D, true>::KSC + of.sbase), 4, of.soff, 0, 0, 0);
   }
 }
 // Wait until at most N of this wave's global loads (direct loads included)
@@ -361,6 +348,18 @@ __device__ __forceinline__ f32x16 qk_half(const uint16_t* kt, const Acc<D>& a) {
   return s;
 }
 
+// 32 bytes of a staged e4m3 K row as an fp8 MFMA operand. (p is
+// restrict-qualified so that the reads carry alias-scope information:
+// without it the compiler makes them wait for every direct global-to-LDS
+// load in flight; the kernel's own waits before each barrier order those
+// loads with the reads.)
+__device__ __forceinline__ i32x8 k8_op(const uint8_t* __restrict__ p) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(p);
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
+  return i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+               static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+}
+
 // fp8 path: S^T of 32 keys (kt: the lane's permuted fp8 K row plus 32 g
 // bytes; sa: the E8M0 code of that row's scale). The two operands carry
 // their power-of-two scales into the MFMA, which applies them.
@@ -368,13 +367,8 @@ template <int D>
 __device__ __forceinline__ f32x16 qk_half8(const uint8_t* kt, int sa, const Acc<D>& a) {
   f32x16 s = a.nm;
 #pragma unroll
-  for (int st = 0; st < Geo<D>::NK8; ++st) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(kt + 64 * st);
-    const uint4 hi = *reinterpret_cast<const uint4*>(kt + 64 * st + 16);
-    const i32x8 kk = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-                      static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
-    s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kk, a.q8[st], s, 0, 0, 0, sa, 0, a.qe);
-  }
+  for (int st = 0; st < Geo<D>::NK8; ++st)
+    s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k8_op(kt + 64 * st), a.q8[st], s, 0, 0, 0, sa, 0, a.qe);
   return s;
 }
 
@@ -560,27 +554,22 @@ __device__ __forceinline__ float exact_tile(const uint16_t* bc, int koff, int vo
 template <int D, bool kMask, bool kLast = false>
 __device__ __forceinline__ float exact_tile8(const uint8_t* kb, const uint8_t* sc, int ql, const uint16_t* bc,
                                              int voff, Acc<D>& a, uint64_t km, uint64_t kl, float& pl) {
-  constexpr int NK8 = Geo<D>::NK8, NU = Geo<D>::NU, KSB = Geo<D>::KSB, VSR = Geo<D>::VSR;
+  constexpr int NK8 = Geo<D>::NK8, NU = Geo<D>::NU, K32B = Geo<D, true>::K32B, V16 = Geo<D, true>::V16,
+                V32 = Geo<D, true>::V32;
   constexpr int NV = 2 * NU;
   constexpr int kValu = kMask ? 52 : 36;
   constexpr int NKX = NK8;
   const uint16_t* vp = bc + voff;
   i32x8 k0[NK8], k1[NK8];
   bf16x8 v0[NV], v1[NV];
-  auto ld = [&](const uint8_t* p) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(p);
-    const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-    return i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-                 static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
-  };
   // region 1: K operands of half 0, the row scales of both halves
 #pragma unroll
-  for (int st = 0; st < NK8; ++st) k0[st] = ld(kb + 64 * st);
+  for (int st = 0; st < NK8; ++st) k0[st] = k8_op(kb + 64 * st);
   const int sa0 = sc[perm_key(0, ql)], sa1 = sc[perm_key(1, ql)];
   __builtin_amdgcn_sched_barrier(0);
   // region 2: S^T half 0 | K operands of half 1
 #pragma unroll
-  for (int st = 0; st < NK8; ++st) k1[st] = ld(kb + 32 * KSB + 64 * st);
+  for (int st = 0; st < NK8; ++st) k1[st] = k8_op(kb + K32B + 64 * st);
   f32x16 s0 = a.nm, s1 = a.nm;
 #pragma unroll
   for (int st = 0; st < NK8; ++st)
@@ -595,7 +584,7 @@ __device__ __forceinline__ float exact_tile8(const uint8_t* kb, const uint8_t* s
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) v0[2 * u + h] = v_op<D, true>(vp + 16 * h * VSR + 32 * u);
+    for (int h = 0; h < 2; ++h) v0[2 * u + h] = v_op<D, true>(vp + h * V16 + 32 * u);
 #pragma unroll
   for (int st = 0; st < NK8; ++st)
     s1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k1[st], a.q8[st], s1, 0, 0, 0, sa1, 0, a.qe);
@@ -613,7 +602,7 @@ __device__ __forceinline__ float exact_tile8(const uint8_t* kb, const uint8_t* s
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) v1[2 * u + h] = v_op<D, true>(vp + (32 + 16 * h) * VSR + 32 * u);
+    for (int h = 0; h < 2; ++h) v1[2 * u + h] = v_op<D, true>(vp + V32 + h * V16 + 32 * u);
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
@@ -657,7 +646,7 @@ __device__ __forceinline__ float run_tile(const uint16_t* bc, int koff, int koff
                                           uint64_t km, uint64_t kl, float& pl) {
   if constexpr (F8) {
     const uint8_t* b8 = reinterpret_cast<const uint8_t*>(bc);
-    return exact_tile8<D, kMask, kLast>(b8 + koff8, b8 + 64 * Geo<D>::KSB, ql, bc, voff, a, km, kl, pl);
+    return exact_tile8<D, kMask, kLast>(b8 + koff8, b8 + Geo<D, true>::KSC, ql, bc, voff, a, km, kl, pl);
   } else {
     return exact_tile<D, kMask, kLast>(bc, koff, voff, a, km, kl, pl);
   }
@@ -673,7 +662,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     int mode, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ ke, const uint8_t* __restrict__ kb8,
     const uint8_t* __restrict__ kbe, const int32_t* __restrict__ offs, int* __restrict__ queues) {
   const bool tail = mode != kModeDrop, corr = mode == kModePisa;
-  constexpr int BUF = Geo<D, F8>::BUF, NBUF = Geo<D, F8>::NBUF, KSB = Geo<D>::KSB, VSR = Geo<D>::VSR;
+  constexpr int BUF = Geo<D, F8>::BUF, NBUF = Geo<D, F8>::NBUF, NREG8 = Geo<D>::NREG8;
   constexpr int HS = Geo<D>::HS, NREG = Geo<D>::NREG;
   extern __shared__ __align__(16) unsigned char smem[];
   uint16_t* buf = reinterpret_cast<uint16_t*>(smem);  // NBUF staging buffers
@@ -756,13 +745,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   // bf16: the lane's K row of sub-tile 0, dims 8 g .. + 8 (+K32 for sub-tile 1)
   const int krow = perm_key(0, ql);
   const int koff = (krow % NREG) * (Geo<D>::KREG / 2) + (krow / NREG) * D + 8 * g;
-  const int koff8 = krow * KSB + 32 * g;                      // fp8: bytes, (+32 KSB for sub-tile 1)
+  // fp8: bytes, the lane's e4m3 row of sub-tile 0, dims 32 g .. (+K32B for sub-tile 1)
+  const int koff8 = (krow % NREG8) * Geo<D>::KREG + (krow / NREG8) * D + 32 * g;
   // supplier address of the transposing V reads: in 16-lane group G = l / 16,
   // lane 4 k + j reads row (key) 8 g + k, dims 16 (G % 2) + 4 j .. + 4, so
   // that the group's output lane i gets dim 16 (G % 2) + i of keys .. + 3
   const int vrow = 8 * g + (l & 15) / 4, vdim = 16 * ((l >> 4) & 1) + 4 * (l & 3);
   const int voff = Geo<D, F8>::KTILE + vdim +
-                   (F8 ? vrow * VSR : (vrow % NREG) * (Geo<D>::VREG / 2) + (vrow / NREG) * D);
+                   (vrow % NREG) * (Geo<D>::VREG / 2) + (vrow / NREG) * D;
 
   Acc<D> a;
   {
@@ -824,16 +814,17 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
                                                       pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7])));
     }
   }
-  StageOffs8<D> of8;
+  DmaOffs8<D> of8;
   DmaOffs<D> ofd;
   const uint16_t* kb = kb16 + static_cast<size_t>(bh) * T * D;
   const uint16_t* vs = vs16 + static_cast<size_t>(bh) * T * D;
+  // step 0 (centroid chunk 0) does not depend on the exact lists: its direct
+  // loads go out now and overlap the set-up below
   if constexpr (F8) {
     of8.init();
+    dma_rows8<D>(kb8 + static_cast<size_t>(bh) * T * D, vs, kbe + static_cast<size_t>(bh) * T, min(64, T), buf, of8);
   } else {
     ofd.init();
-    // step 0 (centroid chunk 0) does not depend on the exact lists: its
-    // direct loads go out now and overlap the set-up below
     dma_rows<D>(kb, vs, min(64, T), buf, ofd);
   }
 
@@ -931,24 +922,22 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   int slot = 0;
   auto slot_after = [&](int k) { return slot + k < NBUF ? slot + k : slot + k - NBUF; };
   auto cur = [&]() -> uint16_t* { return buf + slot * BUF; };
-  Stage8<D> st;  // fp8: the step in flight
-  // start the loads of a step: fp8 into registers (st), bf16 straight into
-  // LDS buffer dst
+  // start the direct loads of a step into LDS buffer dst
   auto fetch = [&](int step, uint16_t* dst) {
     if (step >= 1 && step <= nu) {
       const int j = __builtin_amdgcn_readfirstlane(ulist[step - 1]);
       const size_t base = static_cast<size_t>(64 * j) * D;
       if constexpr (F8)
-        load_rows8<D>(k8 + head + base, Vh + base, ke + static_cast<size_t>(bh) * L + 64 * j, min(64, L - 64 * j), of8,
-                      st);
+        dma_rows8<D>(k8 + head + base, Vh + base, ke + static_cast<size_t>(bh) * L + 64 * j, min(64, L - 64 * j), dst,
+                     of8);
       else
         dma_rows<D>(Kh + base, Vh + base, min(64, L - 64 * j), dst, ofd);
     } else {
       const int c = step == 0 ? 0 : step - nu;
       const size_t base = static_cast<size_t>(64 * c) * D;
       if constexpr (F8)
-        load_rows8<D>(kb8 + static_cast<size_t>(bh) * T * D + base, vs + base,
-                      kbe + static_cast<size_t>(bh) * T + 64 * c, min(64, T - 64 * c), of8, st);
+        dma_rows8<D>(kb8 + static_cast<size_t>(bh) * T * D + base, vs + base,
+                     kbe + static_cast<size_t>(bh) * T + 64 * c, min(64, T - 64 * c), dst, of8);
       else
         dma_rows<D>(kb + base, vs + base, min(64, T - 64 * c), dst, ofd);
     }
@@ -957,51 +946,38 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   auto s_half = [&](const uint16_t* bc, int t) -> f32x16 {
     if constexpr (F8) {
       const uint8_t* b8 = reinterpret_cast<const uint8_t*>(bc);
-      return qk_half8<D>(b8 + koff8 + 32 * t * KSB, b8[64 * KSB + perm_key(t, ql)], a);
+      return qk_half8<D>(b8 + koff8 + t * Geo<D>::K32B, b8[Geo<D, true>::KSC + perm_key(t, ql)], a);
     } else {
       return qk_half<D>(bc + koff + t * Geo<D>::K32, a);
     }
   };
-  // after step: publish step + 1 in LDS. fp8: store it from registers and
-  // load step + 2. bf16 (three buffers, loads two steps ahead): wait for
-  // this wave's loads of step + 1 (those of step + 2 may stay in flight),
-  // then, past the barrier, every wave is done with step's buffer, which
-  // takes step + 3.
+  // after step: publish step + 1 in LDS (three buffers, loads two steps
+  // ahead): wait for this wave's loads of step + 1 (those of step + 2 may
+  // stay in flight), then, past the barrier, every wave is done with step's
+  // buffer, which takes step + 3.
+  constexpr int OPS = Geo<D, F8>::DMA_OPS;
   auto advance = [&](int step) {
-    if constexpr (F8) {
-      if (step + 1 < nsteps) store8<D>(st, buf + slot_after(1) * BUF);
-      if (step + 2 < nsteps) fetch(step + 2, nullptr);
-      lds_barrier();
-    } else {
-      if (step + 2 < nsteps)
-        wait_vm<Geo<D>::DMA_OPS>();
-      else
-        wait_vm<0>();
-      lds_barrier();
-      if (step + 3 < nsteps) fetch(step + 3, cur());
-    }
+    if (step + 2 < nsteps)
+      wait_vm<OPS>();
+    else
+      wait_vm<0>();
+    lds_barrier();
+    if (step + 3 < nsteps) fetch(step + 3, cur());
     slot = slot_after(1);
   };
-  // (pre0: the bf16 loads of step 0 were issued already)
+  // (pre0: the loads of step 0 were issued already)
   auto start = [&](bool pre0) {
     slot = 0;
-    if constexpr (F8) {
-      fetch(0, nullptr);
-      store8<D>(st, buf);
-      lds_barrier();
-      if (nsteps > 1) fetch(1, nullptr);
-    } else {
-      if (!pre0) fetch(0, buf);
-      if (nsteps > 1) fetch(1, buf + BUF);
-      if (nsteps > 2) fetch(2, buf + 2 * BUF);
-      if (nsteps > 2)
-        wait_vm<2 * Geo<D>::DMA_OPS>();
-      else if (nsteps > 1)
-        wait_vm<Geo<D>::DMA_OPS>();
-      else
-        wait_vm<0>();
-      lds_barrier();
-    }
+    if (!pre0) fetch(0, buf);
+    if (nsteps > 1) fetch(1, buf + BUF);
+    if (nsteps > 2) fetch(2, buf + 2 * BUF);
+    if (nsteps > 2)
+      wait_vm<2 * OPS>();
+    else if (nsteps > 1)
+      wait_vm<OPS>();
+    else
+      wait_vm<0>();
+    lds_barrier();
   };
   // whether this wave computes union tile `step`: one 64-bit word of its
   // bitmap per 64 tiles, held in scalar registers
