@@ -672,7 +672,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   int* sh = reinterpret_cast<int*>(ubits + kQB * nw);  // nu, rerun flags, next item (10)
   uint16_t* ulist = reinterpret_cast<uint16_t*>(sh + 12);                           // [T]
 
-  // bf16 is persistent: the grid (at most one workgroup per CU) takes the
+  // The grid is persistent (at most one workgroup per CU) and takes the
   // nwg (head, query-block group) items from 8 queues, so a CU moves from
   // one item straight to the next (no workgroup launch between them) and an
   // item's set-up overlaps the previous item's last stores. Workgroups go to
@@ -684,8 +684,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   // 8 i + x takes item i of queue x), the rest by an atomic counter per
   // queue; a workgroup whose queue is empty serves the others. The next
   // item is claimed during the current one (stage 3) and passed on in LDS.
-  // fp8 keeps one workgroup per item (the loop is left after one pass; as a
-  // loop the fp8 tile spills more), in the same XCD-aware order.
   const int per_q = nwg / 8, g8 = static_cast<int>(gridDim.x) / 8;
   auto queue_len = [&](int x) { return per_q + (x < nwg - 8 * per_q ? 1 : 0); };
   auto queue_item = [&](int x, int i) { return i < per_q ? x * per_q + i : 8 * per_q + x; };
@@ -715,9 +713,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     }
   };
   int wg = blockIdx.x;
-  if constexpr (F8) {
-    if (wg < 8 * per_q) wg = (wg % 8) * per_q + wg / 8;
-  } else {
+  {
     const int x0 = wg & 7, i0 = wg >> 3;
     if (wg < 8 * g8 && i0 < queue_len(x0)) {
       wg = queue_item(x0, i0);
@@ -1159,7 +1155,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
   // compiler's wave aggregation of atomics, which reads the result back at
   // once, leaves this one alone.)
   int own = 0;
-  if constexpr (!F8) {
+  {
     int z = 0;
     asm volatile("" : "+v"(z));
     if (t3 == 0) own = atomicAdd(own_queue + z, 1);
@@ -1184,8 +1180,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
     }
     lds_barrier();
   }
-  if constexpr (!F8)
-    if (t3 == 0) sh[10] = claim(own);
+  if (t3 == 0) sh[10] = claim(own);
   // MFMAs need the whole wave: only the stores are guarded per lane.
   if (qvalid) {
     const uint16_t* hrow = buf + ql3 * HS + 8 * g3;
@@ -1211,7 +1206,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_bf16(
       }
     }
   }
-  if constexpr (F8) break;
   lds_barrier();  // every wave is done with this item's LDS before the next item writes it
   wg = sh[10];
   }
@@ -1311,8 +1305,9 @@ __global__ __launch_bounds__(kF32Threads) void k_attn_f32(const float* __restric
 // Workspace of the bf16 problems (byte offsets, each region 256-byte aligned).
 // bf16 path: [kb16 | vs16 | queues], kbar and vsum in bf16, each [B H][T][D],
 // and the 8 item-queue counters of the persistent grid (kQueueInts ints).
-// fp8 path: [k8 | ke | kb8 | kbe | vs16]: K in e4m3 [B H][L][D] and its row
-// scale codes [B H][L], kbar likewise ([B H][T][D], [B H][T]), vsum in bf16.
+// fp8 path: [k8 | ke | kb8 | kbe | vs16 | queues]: K in e4m3 [B H][L][D] and
+// its row scale codes [B H][L], kbar likewise ([B H][T][D], [B H][T]), vsum
+// in bf16, and the 8 item-queue counters.
 struct WsLayout {
   size_t k8, ke, kb8, kbe, vs16, kb16, queues, total;
 };
@@ -1326,7 +1321,8 @@ __host__ inline WsLayout ws_layout(const paro_problem& p, bool fp8) {
     w.kb8 = w.ke + up256(bh * p.L);
     w.kbe = w.kb8 + up256(bh * T * d);
     w.vs16 = w.kbe + up256(bh * T);
-    w.total = w.vs16 + up256(bh * T * d * 2);
+    w.queues = w.vs16 + up256(bh * T * d * 2);
+    w.total = w.queues + up256(sizeof(int) * kQueueInts);
   } else {
     w.kb16 = 0;
     w.vs16 = up256(bh * T * d * 2);
@@ -1364,7 +1360,7 @@ hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, cons
   unsigned char* wb = static_cast<unsigned char*>(ws);
   uint16_t* kb16 = F8 ? nullptr : reinterpret_cast<uint16_t*>(wb + lay.kb16);
   uint16_t* vs16 = reinterpret_cast<uint16_t*>(wb + lay.vs16);
-  int* queues = F8 ? nullptr : reinterpret_cast<int*>(wb + lay.queues);
+  int* queues = reinterpret_cast<int*>(wb + lay.queues);
   uint8_t *k8 = nullptr, *ke = nullptr, *kb8 = nullptr, *kbe = nullptr;
   hipLaunchKernelGGL(k_centroids_bf16, dim3(static_cast<unsigned>((n / 8 + 255) / 256)), dim3(256), 0, s, kbar, vsum,
                      kb16, vs16, n / 8, queues);
@@ -1387,7 +1383,7 @@ hipError_t launch_bf16(const paro_problem& p, const void* Q, const void* K, cons
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_al));
   if (e != hipSuccess) return e;
   const int nwg = ceil_div(T, kQB) * p.B * p.H;
-  const int grid = F8 ? nwg : std::min(nwg, persistent_workgroups());
+  const int grid = std::min(nwg, persistent_workgroups());
   hipLaunchKernelGGL((k_attn_bf16<D, F8>), dim3(grid), dim3(kAttnThreads), lds_al, s,
                      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), kb16, vs16, Hbar, idx, static_cast<uint16_t*>(O), p.L, T,

@@ -308,7 +308,9 @@ int paro_attention_csr(const paro_problem* p, const void* Q, const void* K, cons
  * That is, the method evaluated on q', K and kbar rounded to e4m3 as stated.
  * Same arguments and contract as paro_attention_mode; fp32 problems return
  * PARO_ERR_DTYPE. workspace: at least paro_attention_fp8_workspace_bytes(p)
- * bytes (the e4m3 copies of K and kbar with their scales, and bf16 vsum).
+ * bytes (the e4m3 copies of K and kbar with their scales, bf16 vsum and 512
+ * bytes of work-queue counters); two calls that run at once must not share
+ * one workspace.
  */
 int paro_attention_fp8(const paro_problem* p, const void* Q, const void* K, const void* V,
                        const float* kbar, const float* vsum, const float* Hbar,

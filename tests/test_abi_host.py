@@ -175,9 +175,10 @@ def test_fp8_entry_points_validation():
     pp = ctypes.byref(p)
     T = L.paro_num_blocks(1000, 64)
     wf = L.paro_attention_fp8_workspace_bytes(pp)
-    # e4m3 K [2][1000][128] + its scales + e4m3 kbar [2][16][128] + scales + bf16 vsum, 256-byte aligned regions
+    # e4m3 K [2][1000][128] + its scales + e4m3 kbar [2][16][128] + scales + bf16 vsum + 8 item-queue
+    # counters, 256-byte aligned regions
     up = lambda x: (x + 255) // 256 * 256
-    assert wf == up(2 * 1000 * 128) + up(2 * 1000) + up(2 * T * 128) + up(2 * T) + up(2 * T * 128 * 2)
+    assert wf == up(2 * 1000 * 128) + up(2 * 1000) + up(2 * T * 128) + up(2 * T) + up(2 * T * 128 * 2) + 512
     assert L.paro_attention_fp8_workspace_bytes(ctypes.byref(_p(dtype=1))) == 0
     args = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
     assert L.paro_attention_fp8(ctypes.byref(_p(dtype=1)), *args, 2, 0, FAKE, FAKE, wf, None) == -3
