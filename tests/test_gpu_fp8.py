@@ -104,6 +104,39 @@ def test_fp8_edge_shapes(case, mode):
         log(f"[fp8] edge b{b}h{h} vs the oracle on e4m3 operands: max {mx:.3g} mean {mean:.3g}")
 
 
+@pytest.mark.parametrize("case", [
+    dict(B=1, H=2, L=64 * 300 + 11, d=64, keep=30),    # d = 64 over many tiles (scale bytes loaded by waves 4-7)
+    dict(B=2, H=1, L=64 * 600 - 5, d=128, keep=40),    # 300 items: more than one per persistent workgroup
+])
+def test_fp8_medium_shapes(case):
+    """The fp8 path at sizes between the edge cases and the DiT workloads,
+    on sampled query blocks, against the oracle on the e4m3-rounded operands."""
+    B, H, L, d, keep = (case[x] for x in ("B", "H", "L", "d", "keep"))
+    q, k, v = random_uniform_inputs(B, H, L, d, dtype=torch.bfloat16, seed=L + keep, scale=0.8)
+    scale = 1 / np.sqrt(d)
+    log(f"[fp8] medium {case}")
+    (qd, kd, vd), stats, idx = run_gpu(q, k, v, keep, 0.1)
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    idx_or = torch.empty_like(idx.cpu())
+    refs = {}
+    for b in range(B):
+        for h in range(H):
+            st = pisa.block_stats(kn[b, h], vn[b, h], 64)
+            ir, _ = pisa.route(qn[b, h], st["kbar"], st["M"], keep, 0.1, scale, 64)
+            idx_or[b, h] = torch.from_numpy(ir.astype(np.int32))
+            refs[(b, h)] = (st, ir)
+    o = paro.attention(qd, kd, vd, *stats[:3], idx_or.cuda(), keep, qk_fp8=True).float().cpu().numpy()
+    rng_ = pisa.block_ranges(L, 64)
+    for (b, h), (st, ir) in refs.items():
+        qbs = sample_qblocks(len(rng_), 8)
+        qq, kq, stq = fp8_operands(q[b, h], k[b, h], st["kbar"], st, scale)
+        oref = pisa.attention(qq, kq, vn[b, h], stq, ir, scale, 64, qblocks=qbs)
+        og = np.concatenate([o[b, h, rng_[i][0]:rng_[i][1]] for i in qbs])
+        orr = np.concatenate([oref[i] for i in qbs])
+        mx, mean = check_attention(og, orr, "bf16")
+        log(f"[fp8] medium b{b}h{h} vs the oracle on e4m3 operands: max {mx:.3g} mean {mean:.3g}")
+
+
 def test_fp8_rejects_fp32():
     q = torch.zeros(1, 1, 64, 64, device="cuda")
     stats = paro.precompute(q, q)
