@@ -28,19 +28,25 @@ from parity_util import ATTN_TOL, log
 pytestmark = pytest.mark.gpu
 
 
-def test_max_blocks_uniform_logits():
-    T, d, keep = 16384, 64, 5
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_max_blocks_uniform_logits(d, fp8):
+    """d = 128 is the largest LDS footprint of the attention kernel (three
+    staging buffers plus the lists of 16384 blocks). The fp8 key-query path
+    rounds q to e4m3, but with every key equal all logits of a row stay
+    equal, so its result is the same mean of V."""
+    T, keep = 16384, 5
     L = 64 * T - 7
     g = torch.Generator().manual_seed(11)
     q = torch.randn(1, 1, L, d, generator=g).to(torch.bfloat16)
     k0 = torch.randint(-2, 3, (d,), generator=g).to(torch.bfloat16)
     k = k0.expand(1, 1, L, d).contiguous()
     v = torch.randint(-2, 3, (1, 1, L, d), generator=g).to(torch.bfloat16)
-    log(f"[limits] T={T} L={L} d={d} keep={keep}")
+    log(f"[limits] T={T} L={L} d={d} keep={keep} fp8={fp8}")
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     kbar, vsum, Hbar, M = paro.precompute(kd, vd)
     idx = paro.route(qd, kbar, M, keep, 0.1)
-    o = paro.attention(qd, kd, vd, kbar, vsum, Hbar, idx, keep)
+    o = paro.attention(qd, kd, vd, kbar, vsum, Hbar, idx, keep, qk_fp8=fp8)
     torch.cuda.synchronize()
 
     # statistics
