@@ -15,9 +15,10 @@
 //   3. per row, one wave forms the fp64 scores scale * dot + lambda * M_j,
 //      maps them onto order-preserving 64-bit keys held in registers, and
 //      finds the keep_k-th largest key bit by bit, from the highest bit where
-//      the row's keys differ down, counting matches with wave ballots (no LDS
-//      traffic, no atomics); it stops as soon as the keys that agree with the
-//      prefix found so far are exactly the ones still needed. The winners are
+//      the row's keys differ down: for each bit it counts, with one 64-bit
+//      compare per key and wave ballots (no LDS traffic, no atomics), the keys
+//      at or above the candidate threshold; it stops as soon as the keys that
+//      agree with the prefix found so far are exactly the ones still needed. The winners are
 //      written in ascending j with a ballot / mbcnt compaction. Exact ties go
 //      to the lower j, so the result is a deterministic integer function of
 //      the scores.
@@ -57,6 +58,14 @@ __device__ __forceinline__ int lanes_below(uint64_t bal) {
 }
 
 __device__ __forceinline__ int count_lanes(bool p) { return __builtin_popcountll(__ballot(p)); }
+
+// A wave-uniform 64-bit value, moved to scalar registers (so that the
+// comparisons against it take a scalar operand).
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(v))));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(v >> 32))));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
 
 // acc[e] += element e of a 16-byte piece of a row (8 bf16 or 4 fp32 values)
 template <typename E>
@@ -304,10 +313,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(route_
       smin = fmin(smin, shfl_xor_f64(smin, o));
       smax = fmax(smax, shfl_xor_f64(smax, o));
     }
-    const uint64_t kmin = score_key(smin), kmax = score_key(smax);
+    const uint64_t kmin = uniform64(score_key(smin)), kmax = uniform64(score_key(smax));
     // Invariants: every key whose bits under `mask` exceed `prefix` is taken
     // (keep_k - rem of them); `match` keys equal prefix under mask and rem of
-    // them are still needed, so match >= rem.
+    // them are still needed, so match >= rem. `mask` covers bits 63 .. b + 1
+    // and prefix has no bits below them, so for want = prefix | 2^b a key is
+    // >= want exactly when it is above prefix under mask or equal to it with
+    // bit b set: the keys with bit b set among those that can still match
+    // are the ones >= want, less the keep_k - rem already taken.
     uint64_t mask = ~0ull, prefix = kmax;
     int rem = keep_k;
     if (kmin != kmax) {
@@ -339,15 +352,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(route_
       uint64_t* gathered = reinterpret_cast<uint64_t*>(dots + r * T + ((r * T) & 1));
       const int cap = T <= tail0 ? min(64 * kCompactRegs, (4 * T - 4) / 8) : 0;
       for (; b >= 0 && match != rem && match > cap; --b) {
-        const uint64_t m2 = mask | (1ull << b), want = prefix | (1ull << b);
-        int c1 = 0;
+        const uint64_t want = prefix | (1ull << b);
+        int ge = 0;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) c1 += count_lanes((key[i] & m2) == want);
+        for (int i = 0; i < NI; ++i) ge += count_lanes(key[i] >= want);
         for (int base = tail0; base < T; base += 64) {
           const int j = base + l;
-          c1 += count_lanes(j < T && (score_key(score_at(j)) & m2) == want);
+          ge += count_lanes(j < T && score_key(score_at(j)) >= want);
         }
-        decide(b, c1);
+        decide(b, ge - (keep_k - rem));
       }
       if (b >= 0 && match != rem) {
         // (here T <= tail0: every key is in key[], padding keys are 0)
@@ -365,23 +378,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(route_
         uint64_t ck[kCompactRegs];
 #pragma unroll
         for (int c = 0; c < kCompactRegs; ++c) ck[c] = 64 * c + l < pos ? gathered[64 * c + l] : 0ull;
+        // the keys taken from here on are all gathered ones (the others are
+        // above or below prefix under mask already)
+        const int taken0 = keep_k - rem;
         for (; b >= 0 && match != rem; --b) {
-          const uint64_t m2 = mask | (1ull << b), want = prefix | (1ull << b);
-          int c1 = 0;
+          const uint64_t want = prefix | (1ull << b);
+          int ge = 0;
 #pragma unroll
-          for (int c = 0; c < kCompactRegs; ++c) c1 += count_lanes((ck[c] & m2) == want);
-          decide(b, c1);
+          for (int c = 0; c < kCompactRegs; ++c) ge += count_lanes(ck[c] >= want);
+          decide(b, ge - (keep_k - rem - taken0));
         }
       }
     }
     // Take every key above prefix under mask and the first rem (in ascending
     // j) equal to it: exactly keep_k indices.
+    // (above prefix under mask: above its largest completion hi; padding
+    // keys are 0 and never above)
     int written = 0, eq_seen = 0;
+    const uint64_t hi = prefix | ~mask;
     auto emit = [&](int j, uint64_t k, bool valid) {
-      const uint64_t km = k & mask;
-      const bool eq = valid && km == prefix;
+      const bool gt = k > hi;
+      const bool eq = valid && !gt && k >= prefix;
       const uint64_t beq = __ballot(eq);
-      const bool sel = (valid && km > prefix) || (eq && eq_seen + lanes_below(beq) < rem);
+      const bool sel = gt || (eq && eq_seen + lanes_below(beq) < rem);
       const uint64_t bsel = __ballot(sel);
       const int pos = written + lanes_below(bsel);
       if (sel && pos < keep_k) out[pos] = j;
