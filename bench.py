@@ -48,6 +48,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP32_VALU_TFLOPS = 78.6   # MI355X fp32 vector FMA without packed-fp32 instructions (the build disables them)
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic_video720p_75600.json")
 ATTN_SRCS = [os.path.join(ROOT, "block_sparse_attention_pisa_amd", "csrc", f)
              for f in ("paro_attention.hip", "paro_common.h")]
@@ -245,12 +246,16 @@ def budget_entry(w, qd, kd, vd, stats, out, reps: int = 3):
             "k_i_min": int(kk.min()), "k_i_max": int(kk.max())}
 
 
-def configs_entry(names=("image_4608", "video480p_32760", "video_long_118800"), steps: int = 5):
+def configs_entry(names=("image_4608", "video480p_32760", "video_long_118800"), steps: int = 11,
+                  warm_s: float = 0.1):
     """The other DiT shapes (the 4.6k-token image, and the 32k and 119k-token
     videos the metric spans), timed like the headline step: precompute +
     route + attention on one stream, inputs resident, HIP events around each
-    phase after two warm-up steps (medians of `steps`); cold: the median of 3
-    steps each after a 512 MB write that evicts L2 and MALL."""
+    phase (medians of `steps`) after warm-up steps worth about `warm_s`
+    seconds (at least two): a step of a millisecond or less run after a few
+    warm-up steps finds the shader clock below its steady-state rate. Cold:
+    the median of 3 steps each after a 512 MB write that evicts L2 and
+    MALL."""
     import torch
     from block_sparse_attention_pisa_amd import paro
     from workloads import WORKLOADS, make_inputs
@@ -279,8 +284,12 @@ def configs_entry(names=("image_4608", "video480p_32760", "video_long_118800"), 
             if ev:
                 ev[3].record(stream)
 
-        for _ in range(2):
+        t_warm, n_warm = time.perf_counter(), 0
+        while n_warm < 2 or time.perf_counter() - t_warm < warm_s:
             step()
+            n_warm += 1
+            if n_warm % 4 == 0:
+                torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         for e in evs:
             step(e)
@@ -309,7 +318,8 @@ def configs_entry(names=("image_4608", "video480p_32760", "video_long_118800"), 
                      "attention_TFLOPs": round(flops / (att * 1e-3) / 1e12, 1),
                      "attention_frac_of_bf16_peak": round(flops / (att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "precompute_frac_of_hbm_peak": round(kv_bytes / (pre * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                     "cold_ms_per_step": round(sorted(cold)[1], 4)}
+                     "cold_ms_per_step": round(sorted(cold)[1], 4),
+                     "warmup_steps": n_warm, "timed_steps": steps}
         del qd, kd, vd, stats, idx, o, ws
         torch.cuda.empty_cache()
     return out
@@ -688,6 +698,12 @@ def main():
                            "frac_of_peak": round(kv_bytes / (pre_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "route_hbm": {"algorithmic_GBs": round(route_bytes / (route_ms * 1e-3) / 1e9, 1),
                       "frac_of_peak": round(route_bytes / (route_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        # the centroid dots q_bar . k_bar (2 B H T^2 d FLOPs on fp32 MFMA)
+        # over the whole routing time
+        "route_fp32_mfma": {"dots_flops": 2.0 * w.B * w.H * w.T * w.T * w.d,
+                            "TFLOPs": round(2.0 * w.B * w.H * w.T * w.T * w.d / (route_ms * 1e-3) / 1e12, 2),
+                            "frac_of_peak": round(2.0 * w.B * w.H * w.T * w.T * w.d / (route_ms * 1e-3) / 1e12 /
+                                                  PEAK_FP32_MFMA_TFLOPS, 4)},
         "roofline": {
             "kernel": "k_attn_bf16 (paro_attention)",
             "bound": "mfma",
