@@ -229,48 +229,68 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // the set is refilled with block j + 2 (the loop is unrolled by two so
     // that both sets stay in registers)
     uint4 rkA[4], rvA[4], rkB[4], rvB[4];
+    // (a block past the chunk is fetched as zero rows: its descriptor
+    // covers no bytes, so no memory is read, and the loads stay
+    // unconditional, which lets the compiler count them exactly instead of
+    // waiting for both register sets)
     auto fetch = [&](int j, uint4 (&rk)[4], uint4 (&rv)[4]) {
-      load_item<D>(Kh, j * kBlock, min(kBlock, L - j * kBlock), item, rk);
-      load_item<D>(Vh, j * kBlock, min(kBlock, L - j * kBlock), item, rv);
+      // (wave-uniform; said so, so that the descriptors stay scalar)
+      const int jj = __builtin_amdgcn_readfirstlane(j < j1 ? j : j0);
+      const int nv = __builtin_amdgcn_readfirstlane(j < j1 ? min(kBlock, L - j * kBlock) : 0);
+      load_item<D>(Kh, jj * kBlock, nv, item, rk);
+      load_item<D>(Vh, jj * kBlock, nv, item, rv);
     };
     if (has_item) {
       fetch(j0, rkA, rvA);
-      if (j0 + 1 < j1) fetch(j0 + 1, rkB, rvB);
+      fetch(j0 + 1, rkB, rvB);
     }
-    auto body = [&](int j, uint4 (&rk)[4], uint4 (&rv)[4]) {
-      const int row0 = j * kBlock, nvalid = min(kBlock, L - row0);
-      lds_barrier();  // the previous block's tiles have been consumed
-      if (has_item) {
-        store_item(s.kt, item, rk);
-        store_item(s.vt, item, rv);
-        float ks[8], vs[8];
-        item_colsum(rk, ks);
-        item_colsum(rv, vs);
-        if (item % 16 == 0) {
-          const int dg = item / 16;
-          const size_t o = (static_cast<size_t>(bh) * T + j) * D + 8 * dg;
-          const float fn = static_cast<float>(nvalid);
+    // Stage block j from its register set, write its column sums, and refill
+    // the set with block j + 2. The 16 lanes of a dim group hold the same
+    // sums, so all of them write them (same value, same address): no
+    // branch and no condition on any memory instruction of the loop, so
+    // the compiler counts the outstanding loads exactly and block j + 1
+    // stays in flight while block j is waited for.
+    auto stage = [&](int j, uint4 (&rk)[4], uint4 (&rv)[4]) {
+      const int nvalid = min(kBlock, L - j * kBlock);
+      store_item(s.kt, item, rk);
+      store_item(s.vt, item, rv);
+      float ks[8], vs[8];
+      item_colsum(rk, ks);
+      item_colsum(rv, vs);
+      const int dg = item / 16;
+      const size_t o = (static_cast<size_t>(bh) * T + j) * D + 8 * dg;
+      const float fn = static_cast<float>(nvalid);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            ks[e] = ks[e] / fn;
-            s.kbar[8 * dg + e] = ks[e];
-            s.vsum[8 * dg + e] = vs[e];
-          }
-          *reinterpret_cast<f32x4*>(kbar + o) = f32x4{ks[0], ks[1], ks[2], ks[3]};
-          *reinterpret_cast<f32x4*>(kbar + o + 4) = f32x4{ks[4], ks[5], ks[6], ks[7]};
-          *reinterpret_cast<f32x4*>(vsum + o) = f32x4{vs[0], vs[1], vs[2], vs[3]};
-          *reinterpret_cast<f32x4*>(vsum + o + 4) = f32x4{vs[4], vs[5], vs[6], vs[7]};
-        }
-        if (j + 2 < j1) fetch(j + 2, rk, rv);
+      for (int e = 0; e < 8; ++e) {
+        ks[e] = ks[e] / fn;
+        s.kbar[8 * dg + e] = ks[e];
+        s.vsum[8 * dg + e] = vs[e];
+      }
+      *reinterpret_cast<f32x4*>(kbar + o) = f32x4{ks[0], ks[1], ks[2], ks[3]};
+      *reinterpret_cast<f32x4*>(kbar + o + 4) = f32x4{ks[4], ks[5], ks[6], ks[7]};
+      *reinterpret_cast<f32x4*>(vsum + o) = f32x4{vs[0], vs[1], vs[2], vs[3]};
+      *reinterpret_cast<f32x4*>(vsum + o + 4) = f32x4{vs[4], vs[5], vs[6], vs[7]};
+      fetch(j + 2, rk, rv);
+    };
+    auto body = [&](int j, uint4 (&rk)[4], uint4 (&rv)[4]) {
+      lds_barrier();  // the previous block's tiles have been consumed
+      if constexpr (2 * D == kThreads) {
+        stage(j, rk, rv);  // every thread has an item
+      } else {
+        if (has_item) stage(j, rk, rv);
       }
       lds_barrier();
       accumulate_ktv<D>(s, acc);
       subtract_rank1(s, acc);
     };
-    for (int j = j0; j < j1; j += 2) {
+    // pairs of blocks, both bodies unconditional (so the loads of set B are
+    // always the newer ones where set A is waited for), then an odd last one
+    int j = j0;
+    for (; j + 1 < j1; j += 2) {
       body(j, rkA, rvA);
-      if (j + 1 < j1) body(j + 1, rkB, rvB);
+      body(j + 1, rkB, rvB);
     }
+    if (j < j1) body(j, rkA, rvA);
   } else {
     for (int j = j0; j < j1; ++j) {
       const int row0 = j * kBlock, nvalid = min(kBlock, L - row0);
