@@ -13,7 +13,7 @@ from oracle import pisa
 from workloads import WORKLOADS, Workload, make_inputs, random_uniform_inputs
 
 from parity_util import (check_attention, check_route, check_stats, full_parity, log, run_gpu,
-                         sample_qblocks)
+                         sample_qblocks, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +45,29 @@ def test_video_long_sampled():
     w = WORKLOADS["video_long_118800"]
     s = full_parity(w, heads=[(0, 0), (0, 23)], qblocks=lambda T: sample_qblocks(T, 24))
     log("[parity] long summary", s)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_precompute_every_head_of_a_batch(dtype):
+    """Precompute of B = 2 x H = 5 heads over 1700 blocks (ragged last
+    block, 17,000 blocks in all): every head against the oracle, so a wrong
+    (batch, head) offset anywhere in the three kernels fails, and two calls
+    bitwise equal."""
+    B, H, L, d = 2, 5, 64 * 1700 - 17, 64
+    _, k, v = random_uniform_inputs(B, H, L, d, dtype=dtype, seed=31)
+    kd, vd = to_dev(k, v)
+    s1 = paro.precompute(kd, vd)
+    s2 = paro.precompute(kd, vd)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(s1, s2))
+    kn, vn = k.double().numpy(), v.double().numpy()
+    worst = {}
+    for b in range(B):
+        for h in range(H):
+            st = pisa.block_stats(kn[b, h], vn[b, h], 64)
+            r = check_stats(s1, st, b, h)
+            worst = {n: max(worst.get(n, 0.0), x) for n, x in r.items()}
+    log("[parity] precompute, every head", dtype, worst)
 
 
 def test_long_dense_control_equals_softmax_attention():
