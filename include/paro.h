@@ -33,7 +33,9 @@
  *   outputs must not alias inputs.
  * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *   All work is enqueued on it asynchronously; the library never
- *   synchronizes. Device faults surface at the caller's next synchronization.
+ *   synchronizes, allocates or sets memory, so every call can be recorded
+ *   into a HIP graph by stream capture (the launches are its only work).
+ *   Device faults surface at the caller's next synchronization.
  * - Return value: PARO_OK (0) or a negative PARO_ERR_* code. Arguments are
  *   validated on the host before anything is launched; on an error nothing
  *   is launched and no output is touched. The library never prints or aborts.
