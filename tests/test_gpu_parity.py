@@ -117,6 +117,41 @@ def test_edge_shapes(case, dtype):
         check_attention(o[b, h], oref, dtype)
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64)])
+def test_custom_scale_and_negative_lambda(dtype, d):
+    """A softmax scale other than 1/sqrt(d) (it enters the routing score,
+    the exact logits, the tail logits and the correction) and a negative
+    lambda (routing then prefers blocks of small M_j): statistics, every
+    routing row and every query block against the oracle."""
+    B, H, L, keep, lam, scale = 1, 2, 64 * 150 + 9, 20, -0.3, 0.05
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q, k, v = random_uniform_inputs(B, H, L, d, dtype=tdt, seed=77, scale=0.8)
+    (qd, kd, vd), stats, idx = run_gpu(q, k, v, keep, lam, scale=scale)
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    idx_h = idx.cpu().numpy()
+    idx_or = torch.empty_like(idx.cpu())
+    refs = {}
+    for b in range(B):
+        for h in range(H):
+            st = pisa.block_stats(kn[b, h], vn[b, h], 64)
+            ir, sc = pisa.route(qn[b, h], st["kbar"], st["M"], keep, lam, scale, 64)
+            check_stats(stats, st, b, h)
+            check_route(idx_h[b, h], ir, sc)
+            idx_or[b, h] = torch.from_numpy(ir.astype(np.int32))
+            refs[(b, h)] = (st, ir)
+    o = paro.attention(qd, kd, vd, *stats[:3], idx_or.cuda(), keep, scale=scale).float().cpu().numpy()
+    worst = 0.0
+    for (b, h), (st, ir) in refs.items():
+        oref = pisa.attention(qn[b, h], kn[b, h], vn[b, h], st, ir, scale, 64)
+        mx, mean = check_attention(o[b, h], oref, dtype)
+        worst = max(worst, mx)
+        log(f"[parity] scale {scale} lambda {lam} {dtype} d={d} head {h}: max {mx:.3g} mean {mean:.3g}")
+    # the scale is used: the same call at the default 1/sqrt(d) lands far
+    # outside the error this one has against its reference
+    o_def = paro.attention(qd, kd, vd, *stats[:3], idx_or.cuda(), keep).float().cpu().numpy()
+    assert np.abs(o_def - o).max() > 10 * worst
+
+
 @pytest.mark.parametrize("case", [
     dict(B=1, H=2, L=64 * 300 + 11, d=64, keep=30, lam=0.1),     # d = 64 over many tiles, ragged tail
     dict(B=2, H=1, L=64 * 600 - 5, d=128, keep=599, lam=0.1),    # keep = T - 1: one tail block per row
