@@ -12,7 +12,7 @@ from block_sparse_attention_pisa_amd import paro
 from oracle import pisa
 from workloads import WORKLOADS, Workload, make_inputs, random_uniform_inputs
 
-from parity_util import (check_attention, check_route, check_stats, full_parity, log, run_gpu,
+from parity_util import (M_ABS_TOL, check_attention, check_route, check_stats, full_parity, log, run_gpu,
                          sample_qblocks, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -68,6 +68,58 @@ def test_precompute_every_head_of_a_batch(dtype):
             r = check_stats(s1, st, b, h)
             worst = {n: max(worst.get(n, 0.0), x) for n, x in r.items()}
     log("[parity] precompute, every head", dtype, worst)
+
+
+def _spectral_bounds(k, v, block=64, iters=24, seed=5):
+    """Lower and upper bounds on sigma_max(H_j - Hbar) for every block of one
+    head, in fp64 on the CPU from the inputs (k, v: [L, d] float64 tensors):
+    ||A x|| for x after `iters` power steps on A^T A from a seeded Gaussian
+    start (never above sigma_max, and equal to it once converged), and the
+    Frobenius norm (never below)."""
+    L, d = k.shape
+    T = -(-L // block)
+    pad = T * block - L
+    z = torch.zeros(pad, d, dtype=torch.float64)
+    kb = torch.cat([k, z]).reshape(T, block, d)
+    vb = torch.cat([v, z]).reshape(T, block, d)
+    n = torch.full((T,), block, dtype=torch.float64)
+    n[-1] = block - pad
+    valid = (torch.arange(block)[None, :] < n[:, None]).to(torch.float64)[:, :, None]
+    kbar = kb.sum(dim=1) / n[:, None]
+    H = torch.bmm(((kb - kbar[:, None, :]) * valid).transpose(1, 2).contiguous(), vb)
+    A = H - H.mean(dim=0, keepdim=True)
+    At = A.transpose(1, 2).contiguous()
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(T, d, 1, dtype=torch.float64, generator=g)
+    for _ in range(iters):
+        x = torch.bmm(At, torch.bmm(A, x))
+        x = x / x.norm(dim=1, keepdim=True)
+    lower = torch.bmm(A, x)[:, :, 0].norm(dim=1)
+    upper = A.flatten(1).norm(dim=1)
+    return lower.numpy(), upper.numpy()
+
+
+@pytest.mark.parametrize("name", ["video720p_75600", "video_long_118800"])
+def test_spectral_norm_of_every_block_within_bounds(name):
+    """At the full sizes, M_j of every block of every head lies between a
+    converged fp64 power-iteration estimate (a lower bound on sigma_max) and
+    the Frobenius norm: a Lanczos run that settled on a lower singular value
+    anywhere in the launch fails here, even in heads the sampled parity
+    tests do not look at."""
+    w = WORKLOADS[name]
+    q, k, v = make_inputs(w)
+    del q
+    stats = paro.precompute(k.cuda(), v.cuda())
+    M = stats[3].cpu().numpy()
+    tight = 0
+    for h in range(w.H):
+        lo, up = _spectral_bounds(k[0, h].double(), v[0, h].double())
+        m = M[0, h]
+        assert (m >= lo - M_ABS_TOL).all(), (name, h, int(np.argmax(lo - m)), float((lo - m).max()))
+        assert (m <= up + M_ABS_TOL).all(), (name, h, int(np.argmax(m - up)))
+        tight += int((np.abs(m - lo) <= M_ABS_TOL).sum())
+    log(f"[parity] {name}: M within [power estimate, Frobenius] for all {w.H * w.T} blocks; "
+        f"{tight} within {M_ABS_TOL} of the power estimate")
 
 
 def test_long_dense_control_equals_softmax_attention():
