@@ -99,7 +99,7 @@ def _spectral_bounds(k, v, block=64, iters=24, seed=5):
     return lower.numpy(), upper.numpy()
 
 
-@pytest.mark.parametrize("name", ["video720p_75600", "video_long_118800"])
+@pytest.mark.parametrize("name", ["image_4608", "video480p_32760", "video720p_75600", "video_long_118800"])
 def test_spectral_norm_of_every_block_within_bounds(name):
     """At the full sizes, M_j of every block of every head lies between a
     converged fp64 power-iteration estimate (a lower bound on sigma_max) and
