@@ -75,7 +75,8 @@ def _spectral_bounds(k, v, block=64, iters=24, seed=5):
     head, in fp64 on the CPU from the inputs (k, v: [L, d] float64 tensors):
     ||A x|| for x after `iters` power steps on A^T A from a seeded Gaussian
     start (never above sigma_max, and equal to it once converged), and the
-    Frobenius norm (never below)."""
+    Frobenius norm (never below); plus kbar, vsum and Hbar by their
+    definitions (mean and sum over a block's valid tokens, mean of the H_j)."""
     L, d = k.shape
     T = -(-L // block)
     pad = T * block - L
@@ -96,29 +97,36 @@ def _spectral_bounds(k, v, block=64, iters=24, seed=5):
         x = x / x.norm(dim=1, keepdim=True)
     lower = torch.bmm(A, x)[:, :, 0].norm(dim=1)
     upper = A.flatten(1).norm(dim=1)
-    return lower.numpy(), upper.numpy()
+    exact = {"kbar": kbar.numpy(), "vsum": vb.sum(dim=1).numpy(), "Hbar": H.mean(dim=0).numpy()}
+    return lower.numpy(), upper.numpy(), exact
 
 
 @pytest.mark.parametrize("name", ["image_4608", "video480p_32760", "video720p_75600", "video_long_118800"])
 def test_spectral_norm_of_every_block_within_bounds(name):
-    """At the full sizes, M_j of every block of every head lies between a
-    converged fp64 power-iteration estimate (a lower bound on sigma_max) and
-    the Frobenius norm: a Lanczos run that settled on a lower singular value
-    anywhere in the launch fails here, even in heads the sampled parity
-    tests do not look at."""
+    """At the full sizes, for every head: kbar, vsum and Hbar against their
+    fp64 definitions (the bars of the sampled tests), and M_j of every block
+    between a converged fp64 power-iteration estimate (a lower bound on
+    sigma_max) and the Frobenius norm: a Lanczos run that settled on a lower
+    singular value anywhere in the launch fails here, even in heads the
+    sampled parity tests do not look at."""
     w = WORKLOADS[name]
     q, k, v = make_inputs(w)
     del q
     stats = paro.precompute(k.cuda(), v.cuda())
     M = stats[3].cpu().numpy()
+    kbar, vsum, Hbar = (x.double().cpu().numpy() for x in stats[:3])
     tight = 0
     for h in range(w.H):
-        lo, up = _spectral_bounds(k[0, h].double(), v[0, h].double())
+        lo, up, ex = _spectral_bounds(k[0, h].double(), v[0, h].double())
+        for nm, got, tol in (("kbar", kbar[0, h], 2e-6), ("vsum", vsum[0, h], 2e-6), ("Hbar", Hbar[0, h], 2e-5)):
+            rel = np.abs(got - ex[nm]).max() / np.abs(ex[nm]).max()
+            assert rel < tol, (name, h, nm, rel)
         m = M[0, h]
         assert (m >= lo - M_ABS_TOL).all(), (name, h, int(np.argmax(lo - m)), float((lo - m).max()))
         assert (m <= up + M_ABS_TOL).all(), (name, h, int(np.argmax(m - up)))
         tight += int((np.abs(m - lo) <= M_ABS_TOL).sum())
-    log(f"[parity] {name}: M within [power estimate, Frobenius] for all {w.H * w.T} blocks; "
+    log(f"[parity] {name}: kbar, vsum, Hbar of all {w.H} heads; M within [power estimate, Frobenius] "
+        f"for all {w.H * w.T} blocks; "
         f"{tight} within {M_ABS_TOL} of the power estimate")
 
 
