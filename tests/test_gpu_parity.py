@@ -130,6 +130,34 @@ def test_spectral_norm_of_every_block_within_bounds(name):
         f"{tight} within {M_ABS_TOL} of the power estimate")
 
 
+@pytest.mark.parametrize("name", ["video720p_75600", "video_long_118800"])
+def test_route_every_row_at_full_size(name):
+    """The routing kernel as a unit, at the full sizes and in the launch
+    configuration of the step: the workload's queries, kbar from its
+    definition and a seeded synthetic M (any M is a valid input; the exact
+    one needs an SVD per block), every row of every head against the
+    oracle's top-k, differences excused only within the 1e-5 score gap."""
+    w = WORKLOADS[name]
+    q, k, _ = make_inputs(w)
+    T, d = w.T, w.d
+    kn = k[0].double()
+    pad = T * 64 - w.L
+    kb = torch.cat([kn, torch.zeros(w.H, pad, d, dtype=torch.float64)], dim=1).reshape(w.H, T, 64, d)
+    n = torch.full((T,), 64.0, dtype=torch.float64)
+    n[-1] = 64 - pad
+    kbar = (kb.sum(dim=2) / n[None, :, None]).numpy()
+    M = np.abs(np.random.default_rng(11).normal(300.0, 20.0, size=(w.H, T)))
+    idx = paro.route(q.cuda(), torch.from_numpy(kbar).float()[None].cuda(), torch.from_numpy(M)[None].cuda(),
+                     w.k, w.lam).cpu().numpy()
+    excused = 0
+    for h in range(w.H):
+        # the kernel reads kbar in fp32: the oracle scores use the same rounded values
+        kb32 = kbar[h].astype(np.float32).astype(np.float64)
+        ir, sc = pisa.route(q[0, h].double().numpy(), kb32, M[h], w.k, w.lam, w.scale, 64)
+        excused += check_route(idx[0, h], ir, sc)
+    log(f"[parity] {name}: routing of all {w.H * T} rows, {excused} excused within the gap")
+
+
 def test_long_dense_control_equals_softmax_attention():
     """keep = 100%: the path must reduce to plain softmax attention."""
     w = WORKLOADS["video_long_118800_dense"]
