@@ -63,7 +63,7 @@ def spectral_norm(A: np.ndarray) -> np.ndarray:
     return np.linalg.svd(A, compute_uv=False)[..., 0]
 
 
-def block_stats(k: np.ndarray, v: np.ndarray, block: int, keep_H: bool = False):
+def block_stats(k: np.ndarray, v: np.ndarray, block: int, keep_H: bool = False, spectral: bool = True):
     """Precompute stage for one (batch, head): k, v are [L, d] float64.
 
     Section 2, "hardware implementation", pre-computation step (block
@@ -72,6 +72,8 @@ def block_stats(k: np.ndarray, v: np.ndarray, block: int, keep_H: bool = False):
 
     Returns a dict with kbar [T, d], vsum [T, d], n [T] (valid tokens per
     block), Hbar [d, d] and M [T]; H [T, d, d] as well when ``keep_H``.
+    ``spectral=False`` leaves M out (None): attention needs only the other
+    statistics, and the SVDs dominate the cost.
     """
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -88,7 +90,7 @@ def block_stats(k: np.ndarray, v: np.ndarray, block: int, keep_H: bool = False):
         vsum[j] = vj.sum(axis=0)                     # block value sum
         H[j] = (kj - kbar[j]).T @ vj                 # block first-order matrix
     Hbar = H.sum(axis=0) / T                         # mean over all blocks
-    M = spectral_norm(H - Hbar[None])                # covariance norm per block
+    M = spectral_norm(H - Hbar[None]) if spectral else None   # covariance norm per block
     out = {"kbar": kbar, "vsum": vsum, "n": n, "Hbar": Hbar, "M": M}
     if keep_H:
         out["H"] = H

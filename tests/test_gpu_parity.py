@@ -158,6 +158,34 @@ def test_route_every_row_at_full_size(name):
     log(f"[parity] {name}: routing of all {w.H * T} rows, {excused} excused within the gap")
 
 
+def test_attention_every_head_at_full_size():
+    """The attention kernel as a unit at 720p, every one of the 40 heads (the
+    persistent grid spreads them over eight queues and all workgroups): a
+    seeded synthetic routing (148 distinct blocks per row) fed to both
+    sides, the first, the last and one seeded query block of each head
+    against the oracle."""
+    w = WORKLOADS["video720p_75600"]
+    q, k, v = make_inputs(w)
+    T, kk = w.T, w.k
+    g = np.random.default_rng(13)
+    idx = np.sort(np.argsort(g.random((w.H, T, T), dtype=np.float32), axis=2)[:, :, :kk], axis=2).astype(np.int32)
+    qd, kd, vd = to_dev(q, k, v)
+    stats = paro.precompute(kd, vd)
+    o = paro.attention(qd, kd, vd, *stats[:3], torch.from_numpy(idx)[None].cuda(), kk).float().cpu().numpy()
+    worst = (0.0, 0.0)
+    for h in range(w.H):
+        qn, kn, vn = (x[0, h].double().numpy() for x in (q, k, v))
+        st = pisa.block_stats(kn, vn, 64, spectral=False)
+        qbs = sorted({0, T - 1, int(g.integers(1, T - 1))})
+        ref = pisa.attention(qn, kn, vn, st, idx[h], w.scale, 64, qblocks=qbs)
+        for i in qbs:
+            rows = slice(64 * i, min(64 * i + 64, w.L))
+            mx, mean = check_attention(o[0, h, rows], ref[i], "bf16")
+            worst = (max(worst[0], mx), max(worst[1], mean))
+    log(f"[parity] 720p attention, 3 query blocks of every head, synthetic routing: max {worst[0]:.3g} "
+        f"mean {worst[1]:.3g}")
+
+
 def test_long_dense_control_equals_softmax_attention():
     """keep = 100%: the path must reduce to plain softmax attention."""
     w = WORKLOADS["video_long_118800_dense"]
