@@ -500,3 +500,14 @@ def test_dense_attention_and_block_ranges():
     assert np.abs(pisa.dense_attention(qs, ks, v, 0.4) - ref_s).max() < 1e-9
     assert pisa.block_ranges(150, 64) == [(0, 64), (64, 128), (128, 150)]
     assert pisa.block_ranges(64, 64) == [(0, 64)] and pisa.block_ranges(1, 64) == [(0, 1)]
+
+
+def test_block_stats_without_spectral_norms_keeps_the_other_statistics():
+    """block_stats(..., spectral=False) leaves M out and nothing else changes."""
+    g = np.random.default_rng(4)
+    k, v = g.standard_normal((64 * 5 + 9, 32)), g.standard_normal((64 * 5 + 9, 32))
+    full = pisa.block_stats(k, v, 64)
+    part = pisa.block_stats(k, v, 64, spectral=False)
+    assert part["M"] is None
+    for name in ("kbar", "vsum", "n", "Hbar"):
+        assert np.array_equal(full[name], part[name]), name
