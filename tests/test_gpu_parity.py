@@ -158,12 +158,14 @@ def test_route_every_row_at_full_size(name):
     log(f"[parity] {name}: routing of all {w.H * T} rows, {excused} excused within the gap")
 
 
-def test_attention_every_head_at_full_size():
+@pytest.mark.parametrize("fp8", [False, True])
+def test_attention_every_head_at_full_size(fp8):
     """The attention kernel as a unit at 720p, every one of the 40 heads (the
     persistent grid spreads them over eight queues and all workgroups): a
     seeded synthetic routing (148 distinct blocks per row) fed to both
     sides, the first, the last and one seeded query block of each head
-    against the oracle."""
+    against the exact oracle; also with the key-query products on the fp8
+    matrix cores, held to the same bf16 bar."""
     w = WORKLOADS["video720p_75600"]
     q, k, v = make_inputs(w)
     T, kk = w.T, w.k
@@ -171,7 +173,8 @@ def test_attention_every_head_at_full_size():
     idx = np.sort(np.argsort(g.random((w.H, T, T), dtype=np.float32), axis=2)[:, :, :kk], axis=2).astype(np.int32)
     qd, kd, vd = to_dev(q, k, v)
     stats = paro.precompute(kd, vd)
-    o = paro.attention(qd, kd, vd, *stats[:3], torch.from_numpy(idx)[None].cuda(), kk).float().cpu().numpy()
+    o = paro.attention(qd, kd, vd, *stats[:3], torch.from_numpy(idx)[None].cuda(), kk,
+                       qk_fp8=fp8).float().cpu().numpy()
     worst = (0.0, 0.0)
     for h in range(w.H):
         qn, kn, vn = (x[0, h].double().numpy() for x in (q, k, v))
@@ -182,7 +185,8 @@ def test_attention_every_head_at_full_size():
             rows = slice(64 * i, min(64 * i + 64, w.L))
             mx, mean = check_attention(o[0, h, rows], ref[i], "bf16")
             worst = (max(worst[0], mx), max(worst[1], mean))
-    log(f"[parity] 720p attention, 3 query blocks of every head, synthetic routing: max {worst[0]:.3g} "
+    log(f"[parity] 720p attention{' (fp8 key-query)' if fp8 else ''}, 3 query blocks of every head, "
+        f"synthetic routing: max {worst[0]:.3g} "
         f"mean {worst[1]:.3g}")
 
 
