@@ -348,8 +348,19 @@ __global__ __launch_bounds__(256) void k_hbar_reduce(const float* __restrict__ w
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= D * D) return;
+  // eight partials in flight at a time (unconditional loads, the index
+  // clamped to the last chunk), added in chunk order: the same sum as one
+  // load per chunk, without one memory round trip per chunk
+  constexpr int kBatch = 8;
+  const float* src = ws + static_cast<size_t>(bh) * nchunk * D * D + e;
   double sum = 0.0;
-  for (int c = 0; c < nchunk; ++c) sum += ws[(static_cast<size_t>(bh) * nchunk + c) * D * D + e];
+  for (int c0 = 0; c0 < nchunk; c0 += kBatch) {
+    float p[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) p[u] = src[static_cast<size_t>(min(c0 + u, nchunk - 1)) * D * D];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) sum = c0 + u < nchunk ? sum + p[u] : sum;
+  }
   const float h = static_cast<float>(sum / T);
   Hbar[static_cast<size_t>(bh) * D * D + e] = h;
   hperm[static_cast<size_t>(bh) * D * D + pair_perm_index<D>(e / D, e % D)] = h;
