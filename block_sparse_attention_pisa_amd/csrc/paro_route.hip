@@ -232,10 +232,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(route_
   // lambda M_j of the keys each lane holds in registers (blocks 64 i + l):
   // the same for every row of the group, so loaded once per wave, and here,
   // where their latency hides behind the barrier that ends the dots
+  // (unconditional loads, the index clamped to the last block, so all of
+  // them are in flight together; lanes past T then take 0 as before)
   double lm[NI];
   if constexpr (kMode != kRouteWeights) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) lm[i] = 64 * i + l < T ? lambda * Mh[64 * i + l] : 0.0;
+    for (int i = 0; i < NI; ++i) lm[i] = Mh[min(64 * i + l, T - 1)];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) lm[i] = 64 * i + l < T ? lambda * lm[i] : 0.0;
   }
   __syncthreads();
 
