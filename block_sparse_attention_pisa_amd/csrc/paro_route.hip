@@ -543,11 +543,33 @@ __global__ __launch_bounds__(kAllocThreads) void k_budget_alloc(const int64_t* _
   };
   unsigned long long thr = ~0ull;  // no extra block when left == 0
   if (left > 0) {
+    // each thread's keys (rows t, t + kAllocThreads, ...) computed once, not
+    // once per bit (a 64-bit division each); rows past T hold 0, below every
+    // candidate. The search starts at the highest bit any key has: above it
+    // every count is 0 < left and the prefix would not change.
+    constexpr int kRows = PARO_MAX_BLOCKS / kAllocThreads;
+    unsigned long long kc[kRows];
+    unsigned long long any = 0;
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int i = t + u * kAllocThreads;
+      kc[u] = i < T ? key_of(i) : 0ull;
+      any |= kc[u];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) any |= __shfl_xor(any, o);
+    __syncthreads();
+    if (l == 0) red[w] = static_cast<long long>(any);
+    __syncthreads();
+    any = 0;
+#pragma unroll
+    for (int i = 0; i < kAllocThreads / 64; ++i) any |= static_cast<unsigned long long>(red[i]);
     unsigned long long prefix = 0;
-    for (int b = 63; b >= 0; --b) {
+    for (int b = any ? 63 - __builtin_clzll(any) : -1; b >= 0; --b) {
       const unsigned long long cand = prefix | (1ull << b);
       long long c = 0;
-      for (int i = t; i < T; i += kAllocThreads) c += key_of(i) >= cand ? 1 : 0;
+#pragma unroll
+      for (int u = 0; u < kRows; ++u) c += kc[u] >= cand ? 1 : 0;
       if (block_sum(c) >= left) prefix = cand;
     }
     thr = prefix;
